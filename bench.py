@@ -1,0 +1,229 @@
+"""Benchmark: GPTQ of one Llama-7B-shaped q_proj layer on one MI355X.
+
+Workload (default): W [4096 x 4096] fp16 ~ N(0, 0.02); calibration X = 128
+sequences x 2048 tokens x 4096 channels, bf16, Student-t(4) with 0.5 % of the
+channels x30; 4-bit asymmetric, group 128, block 128, damp 0.01, natural order.
+One step is the whole path on inputs already resident in HBM:
+H = 0; H += 2 X^T X; damp + order + U; column loop with lazy updates; pack.
+
+Prints one JSON line.  The roofline object is for the dominant stage (the
+Hessian: the SYRK kernel plus its fixed-order split reduction), timed with HIP
+events on the stream the library launches on.  The cpu_baseline object times
+the float64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="c2_llama7b_q_proj")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
+                    help="tokens in the oracle's Hessian sample (result scaled to all tokens)")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="rows in the oracle's column-loop sample (result scaled to all rows)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hessian_c2_traffic.json"))
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(W, X, wl, args):
+    """The oracle as it stands, on a bounded sample: its Hessian over the first
+    cpu_tokens tokens (time scaled by n_tokens/cpu_tokens), its factor for the
+    whole layer, its column loop over cpu_rows rows (time scaled by
+    d_out/cpu_rows; rows are independent), and its packing."""
+    import numpy as np
+    import gptq_inputs as gi
+    from oracle import gptq_ref as o
+
+    layer, calib, q = wl.layers[0], wl.calib[0], wl.quant[0]
+    cores = len(os.sched_getaffinity(0))
+    nt = min(args.cpu_tokens, calib.n_tokens)
+    xs = gi.to_float64(X[:nt], calib.dtype)
+    t0 = time.perf_counter()
+    Hs = o.hessian([xs], calib.d_in)
+    t_h = (time.perf_counter() - t0) * (calib.n_tokens / nt)
+    rows = min(args.cpu_rows, layer.d_out)
+    W64 = gi.to_float64(W[:rows], layer.dtype)
+    t0 = time.perf_counter()
+    r = o.gptq(W64, Hs, bits=q.bits, group_size=q.group_size, block_size=q.block_size,
+               damp_percent=q.damp_percent, desc_act=bool(q.desc_act))
+    t_q = time.perf_counter() - t0
+    # split the loop time from the factor time: time the factor alone
+    t0 = time.perf_counter()
+    Hd, _ = o.damp(Hs, q.damp_percent)
+    o.hinv_factor(Hd)
+    t_f = time.perf_counter() - t0
+    t_loop = max(t_q - t_f, 0.0) * (layer.d_out / rows)
+    t0 = time.perf_counter()
+    o.pack_int4(r.codes)
+    t_p = (time.perf_counter() - t0) * (layer.d_out / rows)
+    total = t_h + t_f + t_loop + t_p
+    weights = layer.d_out * layer.d_in
+    return {
+        "value": weights / total, "unit": "weights/s", "cores": cores, "kind": "oracle",
+        "sample": (f"float64 numpy oracle: Hessian over {nt} of {calib.n_tokens} tokens "
+                   f"(x{calib.n_tokens / nt:g}), factor of the full {calib.d_in}^2 H, column loop "
+                   f"over {rows} of {layer.d_out} rows (x{layer.d_out / rows:g}); "
+                   f"est. total {total:.1f} s per layer"),
+        "stages_s": {"hessian": round(t_h, 3), "factor": round(t_f, 3), "loop": round(t_loop, 3),
+                     "pack": round(t_p, 4)},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gptq_inputs as gi
+    import post_weight_quantization_29_amd as P
+
+    wl = gi.workload(args.workload)
+    layer, calib, q = wl.layers[0], wl.calib[0], wl.quant[0]
+    d_out, d = layer.d_out, layer.d_in
+    N = calib.n_tokens
+    log(f"[bench] generating {args.workload}: W {d_out}x{d} {layer.dtype}, X {N}x{d} {calib.dtype}")
+    t0 = time.time()
+    W = gi.weight(layer, wl.config)
+    X = gi.x_full(calib, wl.config)
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    if calib.dtype == "bf16":
+        Xg = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        Xg = torch.from_numpy(X).to(dev)
+    Wg = torch.from_numpy(W).to(dev)
+    assert Wg.dtype == tdt[layer.dtype]
+
+    cfg = P.make_config(bits=q.bits, group_size=q.group_size, block_size=q.block_size,
+                        damp_percent=q.damp_percent, desc_act=q.desc_act)
+    G = d if q.group_size == -1 else q.group_size
+    ng = (d + G - 1) // G
+    H = torch.zeros((d, d), dtype=torch.float32, device=dev)
+    hdiag = torch.zeros((d,), dtype=torch.float64, device=dev)
+    U = torch.empty((d, d), dtype=torch.float32, device=dev)
+    perm = torch.empty((d,), dtype=torch.int32, device=dev)
+    codes = torch.empty((d_out, d), dtype=torch.uint8, device=dev)
+    scales = torch.empty((d_out, ng), dtype=torch.float32, device=dev)
+    zeros = torch.empty((d_out, ng), dtype=torch.int32, device=dev)
+    g_idx = torch.empty((d,), dtype=torch.int32, device=dev)
+    packed = torch.empty((d_out, d // 8), dtype=torch.int32, device=dev)
+    ws_h = torch.empty(P.gptq_hessian_workspace_size(N, d), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(P.gptq_prepare_hinv_workspace_size(d), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(P.gptq_quantize_workspace_size(d_out, d, cfg), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        H.zero_()
+        hdiag.zero_()
+        P.gptq_hessian_accumulate(H, Xg, hdiag, ws_h)
+        if ev is not None:
+            ev[1].record(stream)
+        P.gptq_prepare_hinv(H, q.damp_percent, q.desc_act, U, perm, hdiag, ws_f)
+        if ev is not None:
+            ev[2].record(stream)
+        P.gptq_quantize_layer(Wg, U, perm, cfg, codes, scales, zeros, g_idx, None, ws_q)
+        if ev is not None:
+            ev[3].record(stream)
+        P.gptq_pack_int4(codes, packed)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"[bench] {args.steps} timed steps done in {wall:.3f}s")
+
+    names = ["hessian", "prepare_hinv", "quantize", "pack"]
+    st = {n: [] for n in names}
+    for e in evs:
+        for k, n in enumerate(names):
+            st[n].append(e[k].elapsed_time(e[k + 1]))
+    mean = {n: float(np.mean(v)) for n, v in st.items()}
+    ms_step = wall * 1e3 / args.steps
+    weights = d_out * d
+    value = weights / (ms_step / 1e3)
+
+    h_flops = float(N) * d * (d + 1)                  # lower triangle incl. diagonal
+    achieved_tf = h_flops / (mean["hessian"] / 1e3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("workload") == args.workload:
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": "GPTQ weights quantized/s per layer (+ Hessian TFLOP/s, % MFMA/HBM peak)",
+        "value": value,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 (bf16 x bf16 -> fp32 Hessian)",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "d_out": d_out, "d_in": d, "n_tokens": N,
+                   "x_dtype": calib.dtype, "w_dtype": layer.dtype, "bits": q.bits,
+                   "group_size": q.group_size, "block_size": q.block_size,
+                   "damp_percent": q.damp_percent, "desc_act": q.desc_act,
+                   "parallelism": "single GPU"},
+        "stages_ms": {k: round(v, 4) for k, v in mean.items()},
+        "hessian_tflops": achieved_tf,
+        "weights_per_s_excl_hessian": weights / ((ms_step - mean["hessian"]) / 1e3),
+        "roofline": {"bound": "mfma", "achieved": achieved_tf, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "kernel": "Hessian stage: syrk16_kernel<bf16> + syrk_reduce_kernel<4>",
+                     "work_per_launch": f"N*d*(d+1) = {h_flops:.4g} flop"},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(W, X, wl, args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ layer quantizer, libgptq.so.
+ *
+ * The library quantizes the weights of one linear layer W [d_out x d_in] with
+ * GPTQ: a Hessian from calibration activations, damping of its diagonal, an
+ * optional column order by descending diag(H), the upper Cholesky factor of
+ * H^-1, and a column-by-column min-max group quantization whose rounding
+ * error is pushed onto the columns not yet quantized, 128 columns at a time
+ * with one lazy update of the rest.
+ *
+ * Sources: the GPTQ practice page at m.lqnn.cn/news/117696, section 2.1 (the
+ * OBQ step and the Hessian from calibration activations), section 2.2 (fixed
+ * order, lazy batch updates, Cholesky of H^-1), section 3.3 (bits,
+ * group_size, desc_act, damp_percent); the tutorial page "大模型压缩量化技术：
+ * GPTQ 与 AWQ 原理详解 + Python 实战教程", section 二 (the min-max grid).
+ *
+ * Conventions shared by every call:
+ *  - Pointers are device pointers owned by the caller, except out_host in
+ *    gptq_layer_error, which is host memory.  The library keeps no state and
+ *    allocates no device memory; scratch memory comes in through ws/ws_bytes,
+ *    sized by the matching *_workspace_size query.  Workspaces need 256-byte
+ *    alignment (any hipMalloc / torch allocation satisfies this).
+ *  - All work is enqueued on stream s, in stream order.  Only
+ *    gptq_prepare_hinv and gptq_layer_error synchronize s (to read one
+ *    device flag or scalar).
+ *  - Argument errors return GPTQ_ERR_INVALID_ARG (or GPTQ_ERR_WORKSPACE)
+ *    before anything is enqueued.  HIP failures return GPTQ_ERR_HIP.
+ *  - Layouts are row-major.  Columns of W are input channels.  X is
+ *    token-major [n_tokens x d_in].
+ *  - Calls on distinct buffers and streams are independent (reentrant).
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GPTQ_F32 = 0, GPTQ_F16 = 1, GPTQ_BF16 = 2 } gptq_dtype;
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = -1,
+  GPTQ_ERR_NOT_PD = -2,      /* damped Hessian not positive definite: raise damp_percent */
+  GPTQ_ERR_HIP = -3,
+  GPTQ_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query returns */
+  GPTQ_ERR_UNSUPPORTED = -5  /* a valid option this build does not implement */
+} gptq_status;
+
+/* The quantizer's options, as the pages' config objects name them
+ * (practice page section 3.3; the ms-swift review page's GptqConfig).
+ *  bits          2..8 (the code range is [0, 2^bits - 1])
+ *  group_size    columns sharing one scale/zero (consecutive in processing
+ *                order); -1 = one group per row.  Must divide block_size, or
+ *                be a multiple of it, or be -1; in-block groups must be a
+ *                multiple of 4.
+ *  block_size    lazy-batch width; this build supports 128 only.
+ *  damp_percent  lambda = damp_percent * mean(diag H) is added to diag(H).
+ *  desc_act      0/1: process columns by descending diag(H).
+ *  sym           0 = asymmetric min-max grid (the only mode implemented). */
+typedef struct {
+  int32_t bits;
+  int32_t group_size;
+  int32_t block_size;
+  float damp_percent;
+  int32_t desc_act;
+  int32_t sym;
+} gptq_config;
+
+/* ---------------------------------------------------------------- Hessian
+ * H += 2 * X^T X over n_tokens calibration tokens (practice page 2.1: the
+ * Hessian is built from the layer's input activations).
+ *  H        [d_in x d_in] fp32, full symmetric, accumulated into (the caller
+ *           zero-fills it once; further calls add more tokens).
+ *  hdiag    [d_in] fp64, nullable, accumulated like H: diag(H) summed in fp64
+ *           (the squares of bf16/fp16 values are exact).  gptq_prepare_hinv
+ *           orders columns by these keys when given, so the desc_act order is
+ *           the exact one and does not depend on fp32 accumulation rounding.
+ *  X        [n_tokens x d_in], token-major, of x_dtype (bf16/fp16 multiply
+ *           exactly in fp32 on MFMA; fp32 inputs use the fp32 MFMA).
+ *  d_in     1..65536, multiple of 8.  n_tokens >= 0 (0 leaves H unchanged).
+ *  ws       scratch of gptq_hessian_workspace_size(n_tokens, d_in) bytes
+ *           (partial sums of the split token range; the result does not
+ *           depend on timing: every partial is reduced in a fixed order). */
+size_t gptq_hessian_workspace_size(int64_t n_tokens, int32_t d_in);
+int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, gptq_dtype x_dtype,
+                            int64_t n_tokens, int32_t d_in, void* ws, size_t ws_bytes,
+                            hipStream_t s);
+
+/* ---------------------------------------------------------------- H^-1 factor
+ * From H (undamped, as accumulated): lambda = damp_percent * mean(diag H);
+ * perm = processing order -> original column (identity, or stable descending
+ * diag(H) when desc_act); U [d_in x d_in] fp32 upper triangular (zeros below)
+ * with U^T U = (H[perm][:,perm] + lambda I)^-1 -- the triangular factor of the
+ * inverse Hessian of practice page section 2.2 ("third").  The page calls it
+ * lower-triangular; that factor is U^T.
+ *  H        [d_in x d_in] fp32 input, unchanged.
+ *  hdiag    [d_in] fp64 diagonal keys from gptq_hessian_accumulate, or NULL
+ *           to take diag(H): used for lambda and for the desc_act order.
+ *  U        [d_in x d_in] fp32 output.  perm [d_in] int32 output.
+ *  ws       scratch of gptq_prepare_hinv_workspace_size(d_in) bytes.
+ * Synchronizes s.  Returns GPTQ_ERR_NOT_PD when a pivot of the factorization
+ * is <= 0 or NaN (the pages' remedy: a larger damp_percent); U is then
+ * undefined. */
+size_t gptq_prepare_hinv_workspace_size(int32_t d_in);
+int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_in, float damp_percent,
+                      int32_t desc_act, float* U, int32_t* perm, void* ws, size_t ws_bytes,
+                      hipStream_t s);
+
+/* ---------------------------------------------------------------- quantize
+ * GPTQ column loop (practice page 2.1 / 2.2; min-max grid of the tutorial
+ * page section 二).  In processing order k (column perm[k]) and per row r:
+ * at each group start, scale = (max - min)/maxq and zero = rint(-min/scale)
+ * over the group's current (already compensated) weights; code =
+ * clamp(rint(w/scale) + zero, 0, maxq); q = scale*(code - zero);
+ * e = (w - q)/U[k][k]; the later columns of the 128-column block take
+ * w -= e * U[k][.] at once, the columns after the block take one lazy update
+ * W -= Err * U[block rows][after] at the block's end.
+ *  W       [d_out x d_in] of w_dtype, original column order, unchanged.
+ *  U, perm as produced by gptq_prepare_hinv (processing order).
+ *  codes   [d_out x d_in] uint8 output, original column order.
+ *  scales  [d_out x n_groups] fp32, zeros [d_out x n_groups] int32 outputs,
+ *          indexed by processing-order group; n_groups = ceil(d_in / G).
+ *  g_idx   [d_in] int32 output: original column -> group.
+ *  Q       [d_out x d_in] fp32 dequantized weights, original order; may be NULL.
+ *  ws      scratch of gptq_quantize_workspace_size(d_out, d_in, cfg) bytes.
+ *  d_out >= 1, d_in >= 1 (any width; packing needs d_in % 8 == 0). */
+size_t gptq_quantize_workspace_size(int32_t d_out, int32_t d_in, const gptq_config* cfg);
+int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in,
+                        const float* U, const int32_t* perm, const gptq_config* cfg,
+                        uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx,
+                        float* Q, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------- pack
+ * Eight 4-bit codes per uint32 (practice page section 1.1: half a byte per
+ * weight at 4 bits): packed[r][m] = sum_k (codes[r][8m+k] & 15) << 4k.
+ *  codes [rows x cols] uint8, packed [rows x cols/8] uint32; cols % 8 == 0.
+ *  3-bit codes are stored as nibbles too. */
+int gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_t cols, uint32_t* packed,
+                   hipStream_t s);
+
+/* ---------------------------------------------------------------- layer error
+ * out_host[0] = ||(W - Q) X^T||_F^2 = 1/2 tr((W - Q) H (W - Q)^T) with the
+ * undamped H (practice page section 5.5: measure the loss, do not eyeball it).
+ * fp32 products, fp64 final sum.  Synchronizes s.
+ *  H [d_in x d_in] fp32, W [d_out x d_in] of w_dtype, Q [d_out x d_in] fp32.
+ *  ws: gptq_layer_error_workspace_size(d_out, d_in) bytes. */
+size_t gptq_layer_error_workspace_size(int32_t d_out, int32_t d_in);
+int gptq_layer_error(const float* H, const void* W, gptq_dtype w_dtype, const float* Q,
+                     int32_t d_out, int32_t d_in, double* out_host, void* ws, size_t ws_bytes,
+                     hipStream_t s);
+
+/* ---------------------------------------------------------------- misc */
+const char* gptq_status_string(int status);
+int gptq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPTQ_MI355X_H */

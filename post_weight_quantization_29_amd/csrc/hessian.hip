@@ -1,0 +1,467 @@
+// Calibration Hessian H += 2 X^T X (GPTQ practice page m.lqnn.cn/news/117696,
+// section 2.1: the Hessian comes from the layer's input activations).
+//
+// X is token-major [n_tokens x d], so both MFMA operands have the token index
+// as their contraction index and channels contiguous in memory.  Tiles of X
+// are copied to LDS exactly as laid out in HBM (channel-contiguous rows) and
+// the K-contiguous MFMA operands are produced by the gfx950 transposing LDS
+// read ds_read_b64_tr_b16.  Only lower-triangle tiles are computed; the token
+// range is split so that enough workgroups exist, each split writes its
+// partial tile in the MFMA register order, and a second kernel adds the
+// partials in a fixed order into H and mirrors off-diagonal tiles.
+#include "common.h"
+
+namespace gptq {
+
+// ---------------------------------------------------------------------------
+// tile bookkeeping
+// ---------------------------------------------------------------------------
+GPTQ_DEV void tri_tile(int q, int& I, int& J) {
+  // q enumerates (I, J), I >= J, row by row: q = I(I+1)/2 + J
+  int i = (int)((sqrtf(8.0f * (float)q + 1.0f) - 1.0f) * 0.5f);
+  while ((i + 1) * (i + 2) / 2 <= q) ++i;
+  while (i * (i + 1) / 2 > q) --i;
+  I = i;
+  J = q - i * (i + 1) / 2;
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit inputs: bf16 / fp16, v_mfma_f32_32x32x16_{bf16,f16}
+// Workgroup tile 256x256, 4 waves (2x2) of 128x128, 32 tokens per LDS stage.
+// ---------------------------------------------------------------------------
+constexpr int kT16 = 256;          // tile edge (channels)
+constexpr int kK16 = 32;           // tokens per stage
+constexpr int kP16 = kT16 + 32;    // LDS row pitch in elements: consecutive token
+                                   // rows land 16 banks apart, so the four rows a
+                                   // 32-lane transposing read touches never collide
+
+template <typename T> struct Op16;
+template <> struct Op16<__bf16> {
+  typedef bf16x8_t v8;
+  typedef bf16x4_t v4;
+  static GPTQ_DEV v4 tr(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4*)(LDS_AS void*)p);
+  }
+  static GPTQ_DEV f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Op16<_Float16> {
+  typedef f16x8_t v8;
+  typedef f16x4_t v4;
+  typedef __fp16 raw4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  static GPTQ_DEV v4 tr(const _Float16* p) {
+    raw4 r = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS raw4*)(LDS_AS void*)p);
+    return __builtin_bit_cast(v4, r);
+  }
+  static GPTQ_DEV f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// K-contiguous operand for a 32-channel block starting at channel cbase of an
+// LDS stage [kK16][kP16], k-slice ks (16 tokens).  The transposing read gives
+// lane j of each 16-lane group g the element (4e + (j%16)/4, j%4) of the
+// group's 16x4 block of 64-bit loads; pointing lane 16g+4a+b at token
+// (8*(g/2) + 4r + a) and channels (16*(g%2) + 4b .. +3) hands lane l channel
+// cbase + l%32 at tokens 8*(l/32) + 4r + 0..3, i.e. MFMA k-slot order.
+template <typename T>
+GPTQ_DEV typename Op16<T>::v8 operand16(const T* stage, int ks, int cbase, int lane) {
+  const int g = lane >> 4, a = (lane >> 2) & 3, b = lane & 3;
+  const int tok = ks * 16 + 8 * (g >> 1) + a;
+  const int ch = cbase + 16 * (g & 1) + 4 * b;
+  typename Op16<T>::v4 lo = Op16<T>::tr(stage + tok * kP16 + ch);
+  typename Op16<T>::v4 hi = Op16<T>::tr(stage + (tok + 4) * kP16 + ch);
+  typename Op16<T>::v8 v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
+// Partial layout (floats): [work item][wave 4][block 16 = mb*4+nb][reg 16][lane 64]
+template <typename T>
+GPTQ_DEV float elem16(uint32_t word, int half) {
+  const uint16_t h = (uint16_t)(word >> (16 * half));
+  if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, h);
+  }
+}
+
+// Diagonal tiles also sum x^2 per channel in fp64 (the squares of 16-bit
+// values are exact), one partial row per (split, tile row): these sums are the
+// keys of the descending-diagonal column order, so the order does not hinge on
+// fp32 accumulation rounding.
+template <typename T>
+__global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X, int64_t n_tokens,
+                                                         int d, int nt, int ntiles, int splits,
+                                                         int64_t nk, float* __restrict__ partial,
+                                                         double* __restrict__ pdiag) {
+  __shared__ __attribute__((aligned(16))) T sA[2][kK16 * kP16];
+  __shared__ __attribute__((aligned(16))) T sB[2][kK16 * kP16];
+  __shared__ double sD[8][kT16 + 1];
+
+  const int w = blockIdx.x;
+  const int s = w / ntiles;
+  const int q = w - s * ntiles;
+  int I, J;
+  tri_tile(q, I, J);
+  const bool diag = (I == J);
+  const int64_t ks0 = nk * s / splits, ks1 = nk * (s + 1) / splits;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // global -> LDS copy assignment: 4 chunks of 8 channels per thread per panel
+  const int crow = tid >> 5;          // token row 0..7 (+8*i)
+  const int ccol = (tid & 31) * 8;    // channel offset in the panel
+  const int chA = I * kT16 + ccol, chB = J * kT16 + ccol;
+  const bool okA = chA < d, okB = chB < d;
+
+  uint4 ra[4], rb[4];
+  auto gload = [&](int64_t kstep) {
+    const int64_t t0 = kstep * kK16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + crow + 8 * i;
+      const bool tv = t < n_tokens;
+      ra[i] = (tv && okA) ? *reinterpret_cast<const uint4*>(X + t * d + chA) : make_uint4(0, 0, 0, 0);
+      if (!diag)
+        rb[i] = (tv && okB) ? *reinterpret_cast<const uint4*>(X + t * d + chB) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  double dsum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dsum[e] = 0.0;
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4*>(&sA[buf][(crow + 8 * i) * kP16 + ccol]) = ra[i];
+      if (!diag) *reinterpret_cast<uint4*>(&sB[buf][(crow + 8 * i) * kP16 + ccol]) = rb[i];
+    }
+    if (diag) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wd[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double v = (double)elem16<T>(wd[e >> 1], e & 1);
+          dsum[e] = fma(v, v, dsum[e]);
+        }
+      }
+    }
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  if (ks0 < ks1) {
+    gload(ks0);
+    lstore(0);
+    __syncthreads();
+    for (int64_t kk = ks0; kk < ks1; ++kk) {
+      const int buf = (int)((kk - ks0) & 1);
+      if (kk + 1 < ks1) gload(kk + 1);
+      const T* stA = sA[buf];
+      const T* stB = diag ? sA[buf] : sB[buf];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        typename Op16<T>::v8 a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = operand16<T>(stA, ks, wm * 128 + i * 32, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = operand16<T>(stB, ks, wn * 128 + j * 32, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = Op16<T>::mfma(a[i], b[j], acc[i][j]);
+      }
+      if (kk + 1 < ks1) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  float* out = partial + ((size_t)w * 4 + wave) * (16 * 16 * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[((i * 4 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+
+  if (diag) {
+    // threads with equal (tid & 31) hold the same 8 channels: add their
+    // partial sums in a fixed order
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sD[crow][ccol + e] = dsum[e];
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) t += sD[r][tid];
+    pdiag[((size_t)s * nt + I) * kT16 + tid] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: v_mfma_f32_32x32x2f32 (lane l supplies A[l%32][k=l/32]).
+// Workgroup tile 128x128, 4 waves (2x2) of 64x64, 16 tokens per stage.
+// ---------------------------------------------------------------------------
+constexpr int kT32 = 128;
+constexpr int kK32 = 16;
+constexpr int kP32 = kT32 + 32;   // rows 32 banks apart: the two half-waves never collide
+
+__global__ __launch_bounds__(256, 2) void syrk32_kernel(const float* __restrict__ X, int64_t n_tokens,
+                                                         int d, int nt, int ntiles, int splits,
+                                                         int64_t nk, float* __restrict__ partial,
+                                                         double* __restrict__ pdiag) {
+  __shared__ __attribute__((aligned(16))) float sA[2][kK32 * kP32];
+  __shared__ __attribute__((aligned(16))) float sB[2][kK32 * kP32];
+  __shared__ double sD[8][kT32 + 1];
+  const int w = blockIdx.x;
+  const int s = w / ntiles;
+  const int q = w - s * ntiles;
+  int I, J;
+  tri_tile(q, I, J);
+  const bool diag = (I == J);
+  const int64_t ks0 = nk * s / splits, ks1 = nk * (s + 1) / splits;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // 16 rows x 128 channels = 512 float4 per panel: 2 per thread
+  const int crow = tid >> 5;          // 0..7 (+8)
+  const int ccol = (tid & 31) * 4;
+  const int chA = I * kT32 + ccol, chB = J * kT32 + ccol;
+  const bool okA = chA < d, okB = chB < d;   // d % 8 == 0 => whole float4 in or out
+  float4 ra[2], rb[2];
+  auto gload = [&](int64_t kstep) {
+    const int64_t t0 = kstep * kK32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t t = t0 + crow + 8 * i;
+      const bool tv = t < n_tokens;
+      ra[i] = (tv && okA) ? *reinterpret_cast<const float4*>(X + t * d + chA) : make_float4(0, 0, 0, 0);
+      if (!diag)
+        rb[i] = (tv && okB) ? *reinterpret_cast<const float4*>(X + t * d + chB) : make_float4(0, 0, 0, 0);
+    }
+  };
+  double dsum[4] = {0.0, 0.0, 0.0, 0.0};
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<float4*>(&sA[buf][(crow + 8 * i) * kP32 + ccol]) = ra[i];
+      if (!diag) *reinterpret_cast<float4*>(&sB[buf][(crow + 8 * i) * kP32 + ccol]) = rb[i];
+    }
+    if (diag) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float vv[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsum[e] = fma((double)vv[e], (double)vv[e], dsum[e]);
+      }
+    }
+  };
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  if (ks0 < ks1) {
+    gload(ks0);
+    lstore(0);
+    __syncthreads();
+    for (int64_t kk = ks0; kk < ks1; ++kk) {
+      const int buf = (int)((kk - ks0) & 1);
+      if (kk + 1 < ks1) gload(kk + 1);
+      const float* stA = sA[buf];
+      const float* stB = diag ? sA[buf] : sB[buf];
+#pragma unroll
+      for (int k2 = 0; k2 < kK32; k2 += 2) {
+        const int row = (k2 + (lane >> 5)) * kP32;
+        float a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = stA[row + wm * 64 + i * 32 + (lane & 31)];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = stB[row + wn * 64 + j * 32 + (lane & 31)];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+      if (kk + 1 < ks1) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  float* out = partial + ((size_t)w * 4 + wave) * (4 * 16 * 64);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+
+  if (diag) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sD[crow][ccol + e] = dsum[e];
+    __syncthreads();
+    if (tid < kT32) {
+      double t = 0.0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) t += sD[r][tid];
+      pdiag[((size_t)s * nt + I) * kT32 + tid] = t;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// H += 2 * sum_s partial[s]  (fixed order), mirrored for off-diagonal tiles.
+// One workgroup per (tile, wave sub-tile); WB = 32-blocks per sub-tile edge.
+// ---------------------------------------------------------------------------
+template <int WB>
+__global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ partial,
+                                                          float* __restrict__ H, int d, int ntiles,
+                                                          int splits) {
+  constexpr int E = 32 * WB;            // sub-tile edge
+  constexpr int NEL = WB * WB * 1024;   // elements per wave sub-tile
+  constexpr int TILE = 2 * E;
+  __shared__ float sub[E][E + 1];
+  const int q = blockIdx.x >> 2, wave = blockIdx.x & 3;
+  int I, J;
+  tri_tile(q, I, J);
+  const int row0 = I * TILE + (wave >> 1) * E;
+  const int col0 = J * TILE + (wave & 1) * E;
+  const size_t item_stride = (size_t)ntiles * 4 * NEL;
+  const float* src = partial + ((size_t)q * 4 + wave) * NEL;
+  for (int e = threadIdx.x; e < NEL; e += 256) {
+    float acc = 0.0f;
+    for (int s = 0; s < splits; ++s) acc += src[s * item_stride + e];
+    acc *= 2.0f;
+    const int blk = e >> 10, r = (e >> 6) & 15, lane = e & 63;
+    const int m = (blk / WB) * 32 + mfma32_row(r, lane);
+    const int n = (blk % WB) * 32 + mfma32_col(lane);
+    sub[m][n] = acc;
+    if (row0 + m < d && col0 + n < d) {
+      float* h = H + (size_t)(row0 + m) * d + (col0 + n);
+      *h += acc;
+    }
+  }
+  if (I == J) return;                  // diagonal tiles were computed in full
+  __syncthreads();
+  // mirror: H[col0 + n][row0 + m] += sub[m][n]
+  for (int e = threadIdx.x; e < E * E; e += 256) {
+    const int n = e / E, m = e % E;
+    if (row0 + m < d && col0 + n < d) {
+      float* h = H + (size_t)(col0 + n) * d + (row0 + m);
+      *h += sub[m][n];
+    }
+  }
+}
+
+// hdiag[c] += 2 * sum_s pdiag[s][c]   (fixed order, fp64)
+__global__ __launch_bounds__(256) void diag_reduce_kernel(const double* __restrict__ pdiag, int d,
+                                                          int np, int splits,
+                                                          double* __restrict__ hdiag) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d) return;
+  double t = 0.0;
+  for (int s = 0; s < splits; ++s) t += pdiag[(size_t)s * np + c];
+  hdiag[c] += 2.0 * t;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct SyrkPlan {
+  int tile;       // 256 (16-bit inputs) or 128 (fp32)
+  int ntiles;
+  int splits;
+  int64_t nk;     // number of token stages
+  int nt;         // tile rows
+  size_t off_diag;
+  size_t ws;      // partial buffers, bytes
+};
+
+static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32) {
+  SyrkPlan p;
+  p.tile = f32 ? kT32 : kT16;
+  const int kst = f32 ? kK32 : kK16;
+  const int nt = (d + p.tile - 1) / p.tile;
+  p.nt = nt;
+  p.ntiles = nt * (nt + 1) / 2;
+  p.nk = (n_tokens + kst - 1) / kst;
+  // Pick the split count that minimizes (rounds of 256 resident workgroups per
+  // unit of work) plus the partial-sum traffic, with >= 16 stages per split.
+  const double tile_flops = 2.0 * p.tile * p.tile * (double)kst;   // per stage
+  const double t_stage = tile_flops / (2.5e15 / 256.0 * 0.6);      // s per stage per WG
+  const double bytes_tile = (double)p.tile * p.tile * 4.0 * 2.0;    // partial write + read
+  double best = 1e300;
+  int best_s = 1;
+  const int smax = (int)std::max<int64_t>(1, std::min<int64_t>(64, p.nk / 16));
+  for (int s = 1; s <= smax; ++s) {
+    const double items = (double)p.ntiles * s;
+    const double rounds = std::ceil(items / 256.0);
+    const double t = rounds * ((double)p.nk / s) * t_stage + items * bytes_tile / 6.0e12;
+    if (t < best * 0.999) { best = t; best_s = s; }
+  }
+  p.splits = (p.nk == 0) ? 1 : best_s;
+  const size_t per_item = (size_t)p.tile * p.tile * sizeof(float);
+  p.off_diag = align_up((size_t)p.splits * p.ntiles * per_item);
+  p.ws = align_up(p.off_diag + (size_t)p.splits * nt * p.tile * sizeof(double));
+  return p;
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_hessian_workspace_size(int64_t n_tokens, int32_t d_in) {
+  if (n_tokens < 0 || d_in <= 0) return 0;
+  SyrkPlan a = syrk_plan(n_tokens, d_in, false), b = syrk_plan(n_tokens, d_in, true);
+  return std::max(a.ws, b.ws);
+}
+
+extern "C" int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, gptq_dtype x_dtype,
+                                       int64_t n_tokens, int32_t d_in, void* ws, size_t ws_bytes,
+                                       hipStream_t s) {
+  if (!H || d_in <= 0 || d_in > 65536 || (d_in % 8) != 0 || n_tokens < 0) return GPTQ_ERR_INVALID_ARG;
+  if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_F16 && x_dtype != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return GPTQ_OK;
+  if (!X) return GPTQ_ERR_INVALID_ARG;
+  const bool f32 = (x_dtype == GPTQ_F32);
+  SyrkPlan p = syrk_plan(n_tokens, d_in, f32);
+  if (!ws || ws_bytes < p.ws || ws_bytes < gptq_hessian_workspace_size(n_tokens, d_in))
+    return GPTQ_ERR_WORKSPACE;
+  float* partial = static_cast<float*>(ws);
+  double* pdiag = reinterpret_cast<double*>(static_cast<char*>(ws) + p.off_diag);
+  const unsigned items = (unsigned)(p.ntiles * p.splits);
+  if (x_dtype == GPTQ_BF16) {
+    syrk16_kernel<__bf16><<<items, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in,
+                                                 p.nt, p.ntiles, p.splits, p.nk, partial, pdiag);
+  } else if (x_dtype == GPTQ_F16) {
+    syrk16_kernel<_Float16><<<items, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in,
+                                                   p.nt, p.ntiles, p.splits, p.nk, partial, pdiag);
+  } else {
+    syrk32_kernel<<<items, 256, 0, s>>>(static_cast<const float*>(X), n_tokens, d_in, p.nt, p.ntiles,
+                                        p.splits, p.nk, partial, pdiag);
+  }
+  GPTQ_LAUNCH_CHECK();
+  if (f32)
+    syrk_reduce_kernel<2><<<p.ntiles * 4, 256, 0, s>>>(partial, H, d_in, p.ntiles, p.splits);
+  else
+    syrk_reduce_kernel<4><<<p.ntiles * 4, 256, 0, s>>>(partial, H, d_in, p.ntiles, p.splits);
+  GPTQ_LAUNCH_CHECK();
+  if (hdiag) {
+    diag_reduce_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(pdiag, d_in, p.nt * p.tile, p.splits, hdiag);
+    GPTQ_LAUNCH_CHECK();
+  }
+  return GPTQ_OK;
+}

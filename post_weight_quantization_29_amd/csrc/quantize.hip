@@ -1,0 +1,340 @@
+// GPTQ column loop and INT4 packing.
+//
+// Sources: GPTQ practice page m.lqnn.cn/news/117696, section 2.1 (quantize one
+// weight, move the not-yet-quantized ones along the inverse-Hessian column),
+// section 2.2 "second" (quantize a 128-column block, then update everything
+// after it with one matrix product), section 3.3 (group_size consecutive
+// columns share a scale and zero point); tutorial page "大模型压缩量化技术：GPTQ
+// 与 AWQ 原理详解 + Python 实战教程", section 二 (min-max uniform grid).
+//
+// Per 128-column block b (processing order):
+//   panel_kernel:   rows in parallel, 4 lanes per row, the block's 128
+//                   weights of a row spread over the quad's registers (lane q
+//                   holds columns 4i+q); U's diagonal block in LDS; column j's
+//                   weight is broadcast inside the quad with DPP, quantized,
+//                   its scaled error e = (w - q)/U[j][j] pushed onto the later
+//                   columns of the block (w -= e*U[j][.]) and kept in ErrT.
+//   trailing GEMM:  W[:, b1:] -= Err * U[b0:b1, b1:] (fp32 MFMA).
+#include "gemm_f32.h"
+
+namespace gptq {
+
+constexpr int kQB = 128;          // block width (lazy batch)
+constexpr int kQRows = 64;        // rows per workgroup (256 threads, 4 per row)
+constexpr int kUP = 36;           // LDS pitch of one (column j, lane q) slot row
+
+// ---------------------------------------------------------------- W gather
+__global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ W, gptq_dtype wt,
+                                                       int d_out, int d, const int* __restrict__ perm,
+                                                       int G, float* __restrict__ Wp,
+                                                       int* __restrict__ g_idx) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= d) return;
+  const int src = perm[j];
+  if (blockIdx.y == 0) g_idx[src] = j / G;
+  for (int r = blockIdx.y; r < d_out; r += gridDim.y)
+    Wp[(size_t)r * d + j] = load_as_float(W, wt, (size_t)r * d + src);
+}
+
+// ---------------------------------------------------------------- helpers
+template <int P>
+GPTQ_DEV float quad_bcast_c(float v) {
+  // DPP quad_perm [P,P,P,P]: every lane of a quad reads lane P of that quad
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), P | (P << 2) | (P << 4) | (P << 6),
+                                      0xF, 0xF, false));
+}
+// p is a constant after unrolling; the switch folds away
+GPTQ_DEV float quad_bcast(float v, int p) {
+  switch (p) {
+    case 0: return quad_bcast_c<0>(v);
+    case 1: return quad_bcast_c<1>(v);
+    case 2: return quad_bcast_c<2>(v);
+    default: return quad_bcast_c<3>(v);
+  }
+}
+GPTQ_DEV float quad_min(float v) {
+  v = fminf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = fminf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  return v;
+}
+GPTQ_DEV float quad_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  return v;
+}
+
+// min-max grid of one group: scale = (max - min)/maxq, zero = rint(-min/scale);
+// a constant group a uses the range [min(a,0), max(a,0)]; all-zero -> (1, 0).
+GPTQ_DEV void grid_params(float xmin, float xmax, float maxq, float& scale, float& zero) {
+  if (xmax == xmin) {
+    xmin = fminf(xmin, 0.0f);
+    xmax = fmaxf(xmax, 0.0f);
+  }
+  if (xmax == xmin) {
+    scale = 1.0f;
+    zero = 0.0f;
+    return;
+  }
+  scale = (xmax - xmin) / maxq;
+  zero = rintf(-xmin / scale);
+}
+
+// ---------------------------------------------------------------- panel
+struct PanelArgs {
+  float* Wp;            // [d_out x d] fp32 work copy, processing order
+  const float* U;       // [d x d]
+  const int* perm;
+  uint8_t* codes;       // [d_out x d], original order
+  float* Q;             // nullable
+  float* scales;        // [d_out x ng]
+  int* zeros;
+  float* ErrT;          // [128 x d_out]
+  int d_out, d, b0, bw, G, ng;
+  float maxq;
+};
+
+__global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
+  __shared__ __attribute__((aligned(16))) float sU[kQB][4][kUP];   // sU[j][q][i] = U[b0+j][b0+4i+q]
+  __shared__ float sInv[kQB];
+  __shared__ int sPerm[kQB];
+
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kQB * kQB; e += 256) {
+    const int j = e >> 7, c = e & 127;
+    float v = 0.0f;
+    if (j < a.bw && c < a.bw) v = a.U[(size_t)(a.b0 + j) * a.d + a.b0 + c];
+    sU[j][c & 3][c >> 2] = v;
+  }
+  for (int j = tid; j < kQB; j += 256) {
+    sInv[j] = (j < a.bw) ? 1.0f / a.U[(size_t)(a.b0 + j) * a.d + a.b0 + j] : 0.0f;
+    sPerm[j] = (j < a.bw) ? a.perm[a.b0 + j] : 0;
+  }
+  __syncthreads();
+
+  const int q = tid & 3;
+  const int row = blockIdx.x * kQRows + (tid >> 2);
+  const bool rv = row < a.d_out;
+  const int rowc = rv ? row : 0;     // clamped row for loads; stores are masked
+  const float* wrow = a.Wp + (size_t)rowc * a.d + a.b0;
+
+  float w[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i] = (4 * i + q < a.bw) ? wrow[4 * i + q] : 0.0f;
+
+  float scale = 1.0f, zero = 0.0f, rscale = 1.0f;
+  const int G = a.G;
+  if (a.b0 % G != 0) {
+    // a group wider than the block started in an earlier block: continue with
+    // the parameters that launch stored
+    scale = a.scales[(size_t)rowc * a.ng + a.b0 / G];
+    zero = (float)a.zeros[(size_t)rowc * a.ng + a.b0 / G];
+    rscale = 1.0f / scale;
+  }
+
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int j = 4 * i + p;                 // column inside the block
+      if (j >= a.bw) break;
+      const int jg = a.b0 + j;                 // processing-order column
+      if (p == 0 && jg % G == 0) {
+        // group [jg, min(jg + G, d)): in-block part from registers (slots t >= i
+        // hold the columns >= j), the rest (G larger than the block) from the
+        // work copy, which already holds every earlier block's lazy update
+        const int gend = min(jg + G, a.d);
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int t = i; t < 32; ++t) {
+          const int cg = a.b0 + 4 * t + q;
+          if (4 * t + q < a.bw && cg < gend) {
+            mn = fminf(mn, w[t]);
+            mx = fmaxf(mx, w[t]);
+          }
+        }
+        for (int cg = a.b0 + a.bw + q; cg < gend; cg += 4) {
+          const float v = a.Wp[(size_t)rowc * a.d + cg];
+          mn = fminf(mn, v);
+          mx = fmaxf(mx, v);
+        }
+        mn = quad_min(mn);
+        mx = quad_max(mx);
+        grid_params(mn, mx, a.maxq, scale, zero);
+        rscale = 1.0f / scale;
+        if (rv && q == 0) {
+          a.scales[(size_t)row * a.ng + jg / G] = scale;
+          a.zeros[(size_t)row * a.ng + jg / G] = (int)zero;
+        }
+      }
+      const float wj = quad_bcast(w[i], p);
+      // correctly rounded wj/scale from the reciprocal (one Newton correction)
+      const float t0 = wj * rscale;
+      const float res = fmaf(-t0, scale, wj);
+      const float tq = fmaf(res, rscale, t0);
+      const float c = fminf(fmaxf(rintf(tq) + zero, 0.0f), a.maxq);
+      const float qv = scale * (c - zero);
+      const float e = (wj - qv) * sInv[j];
+      if (q == p && rv) {
+        const int oc = sPerm[j];
+        a.codes[(size_t)row * a.d + oc] = (uint8_t)(int)c;
+        if (a.Q) a.Q[(size_t)row * a.d + oc] = qv;
+        a.ErrT[(size_t)j * a.d_out + row] = e;
+      }
+      // w[t] -= e * U[j][4t+q] for the later columns of the block (slots t >= i;
+      // the lanes' entries at columns <= j are retired and ignored)
+      const float* urow = &sU[j][q][0];
+#pragma unroll
+      for (int t = (i & ~3); t < 32; t += 4) {
+        const float4 u4 = *reinterpret_cast<const float4*>(urow + t);
+        if (t + 0 >= i) w[t + 0] = fmaf(-e, u4.x, w[t + 0]);
+        if (t + 1 >= i) w[t + 1] = fmaf(-e, u4.y, w[t + 1]);
+        if (t + 2 >= i) w[t + 2] = fmaf(-e, u4.z, w[t + 2]);
+        if (t + 3 >= i) w[t + 3] = fmaf(-e, u4.w, w[t + 3]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pack
+// packed word m = sum_k (codes[8m+k] & 15) << 4k over the flat code array
+// (cols % 8 == 0, so no word straddles two rows).
+__global__ __launch_bounds__(256) void pack_int4_kernel(const uint8_t* __restrict__ codes,
+                                                        int64_t nwords, uint32_t* __restrict__ out) {
+  const int64_t nq = nwords / 4;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nq; i += stride) {
+    const uint4 a = reinterpret_cast<const uint4*>(codes)[2 * i];
+    const uint4 b = reinterpret_cast<const uint4*>(codes)[2 * i + 1];
+    auto pk = [](uint32_t lo, uint32_t hi) -> uint32_t {
+      uint32_t r = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r |= ((lo >> (8 * k)) & 0xFu) << (4 * k);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r |= ((hi >> (8 * k)) & 0xFu) << (16 + 4 * k);
+      return r;
+    };
+    uint4 o;
+    o.x = pk(a.x, a.y);
+    o.y = pk(a.z, a.w);
+    o.z = pk(b.x, b.y);
+    o.w = pk(b.z, b.w);
+    reinterpret_cast<uint4*>(out)[i] = o;
+  }
+  // tail words (nwords % 4), one thread each
+  const int64_t tail0 = nq * 4;
+  const int64_t ti = tail0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && ti < nwords) {
+    uint32_t r = 0;
+    for (int k = 0; k < 8; ++k) r |= ((uint32_t)codes[8 * ti + k] & 0xFu) << (4 * k);
+    out[ti] = r;
+  }
+}
+
+// ---------------------------------------------------------------- planning
+struct QuantLayout {
+  size_t off_wp, off_err, total;
+};
+
+static QuantLayout quant_layout(int d_out, int d) {
+  QuantLayout L;
+  size_t off = 0;
+  L.off_wp = off;
+  off = align_up(off + (size_t)d_out * d * sizeof(float));
+  L.off_err = off;
+  off = align_up(off + (size_t)kQB * d_out * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+static int check_config(const gptq_config* c, int d) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  if (c->bits < 2 || c->bits > 8) return GPTQ_ERR_INVALID_ARG;
+  if (c->desc_act != 0 && c->desc_act != 1) return GPTQ_ERR_INVALID_ARG;
+  if (c->block_size <= 0 || c->sym < 0 || c->sym > 1) return GPTQ_ERR_INVALID_ARG;
+  const int G = c->group_size;
+  if (G != -1 && G <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (c->block_size != kQB) return GPTQ_ERR_UNSUPPORTED;
+  if (c->sym != 0) return GPTQ_ERR_UNSUPPORTED;
+  if (G != -1) {
+    const bool inside = (kQB % G == 0) && (G % 4 == 0);
+    const bool spans = (G % kQB == 0);
+    if (!inside && !spans) {
+      // G and the block size neither divide one another: lazy batching would
+      // no longer equal the column-by-column method
+      if ((kQB % G != 0) && (G % kQB != 0)) return GPTQ_ERR_INVALID_ARG;
+      return GPTQ_ERR_UNSUPPORTED;
+    }
+  }
+  (void)d;
+  return GPTQ_OK;
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_quantize_workspace_size(int32_t d_out, int32_t d_in, const gptq_config* cfg) {
+  (void)cfg;
+  if (d_out <= 0 || d_in <= 0) return 0;
+  return quant_layout(d_out, d_in).total;
+}
+
+extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in,
+                                   const float* U, const int32_t* perm, const gptq_config* cfg,
+                                   uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx,
+                                   float* Q, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!W || !U || !perm || !codes || !scales || !zeros || !g_idx) return GPTQ_ERR_INVALID_ARG;
+  if (d_out <= 0 || d_in <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (w_dtype != GPTQ_F32 && w_dtype != GPTQ_F16 && w_dtype != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
+  const int st = check_config(cfg, d_in);
+  if (st != GPTQ_OK) return st;
+  const QuantLayout L = quant_layout(d_out, d_in);
+  if (!ws || ws_bytes < L.total) return GPTQ_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  float* Wp = reinterpret_cast<float*>(base + L.off_wp);
+  float* ErrT = reinterpret_cast<float*>(base + L.off_err);
+  const int d = d_in;
+  const int G = (cfg->group_size == -1) ? d : cfg->group_size;
+  const int ng = (d + G - 1) / G;
+
+  gather_w_kernel<<<dim3((d + 255) / 256, std::min(d_out, 1024)), 256, 0, s>>>(W, w_dtype, d_out, d,
+                                                                              perm, G, Wp, g_idx);
+  GPTQ_LAUNCH_CHECK();
+
+  PanelArgs pa;
+  pa.Wp = Wp; pa.U = U; pa.perm = perm; pa.codes = codes; pa.Q = Q;
+  pa.scales = scales; pa.zeros = zeros; pa.ErrT = ErrT;
+  pa.d_out = d_out; pa.d = d; pa.G = G; pa.ng = ng;
+  pa.maxq = (float)((1 << cfg->bits) - 1);
+  const int nrow_blocks = (d_out + kQRows - 1) / kQRows;
+  for (int b0 = 0; b0 < d; b0 += kQB) {
+    const int bw = std::min(kQB, d - b0);
+    pa.b0 = b0;
+    pa.bw = bw;
+    panel_kernel<<<nrow_blocks, 256, 0, s>>>(pa);
+    GPTQ_LAUNCH_CHECK();
+    const int b1 = b0 + bw;
+    if (b1 < d) {
+      // W[:, b1:] -= Err * U[b0:b1, b1:]  with Aop(m, k) = ErrT[k][m]
+      gemm_f32<true>(ErrT, d_out, U + (size_t)b0 * d + b1, d, Wp + b1, d, d_out, d - b1, bw, -1.0f,
+                     1.0f, 0, 0, 0, s);
+      GPTQ_LAUNCH_CHECK();
+    }
+  }
+  return GPTQ_OK;
+}
+
+extern "C" int gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_t cols, uint32_t* packed,
+                              hipStream_t s) {
+  if (!codes || !packed || rows < 0 || cols < 0 || (cols % 8) != 0) return GPTQ_ERR_INVALID_ARG;
+  const int64_t nwords = rows * cols / 8;
+  if (nwords == 0) return GPTQ_OK;
+  if ((reinterpret_cast<uintptr_t>(codes) & 15) || (reinterpret_cast<uintptr_t>(packed) & 15))
+    return GPTQ_ERR_INVALID_ARG;
+  const int64_t nq = std::max<int64_t>(1, nwords / 4);
+  const int blocks = (int)std::min<int64_t>((nq + 255) / 256, 8192);
+  pack_int4_kernel<<<blocks, 256, 0, s>>>(codes, nwords, packed);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
