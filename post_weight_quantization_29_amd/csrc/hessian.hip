@@ -332,6 +332,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
                                                           int splits) {
   constexpr int E = 32 * WB;            // sub-tile edge
   constexpr int NEL = WB * WB * 1024;   // elements per wave sub-tile
+  constexpr int NV = NEL / 1024;        // float4 per thread
   constexpr int TILE = 2 * E;
   __shared__ float sub[E][E + 1];
   const int q = blockIdx.x >> 2, wave = blockIdx.x & 3;
@@ -339,30 +340,45 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   tri_tile(q, I, J);
   const int row0 = I * TILE + (wave >> 1) * E;
   const int col0 = J * TILE + (wave & 1) * E;
-  const size_t item_stride = (size_t)ntiles * 4 * NEL;
-  const float* src = partial + ((size_t)q * 4 + wave) * NEL;
-  for (int e = threadIdx.x; e < NEL; e += 256) {
-    float acc = 0.0f;
-    for (int s = 0; s < splits; ++s) acc += src[s * item_stride + e];
-    acc *= 2.0f;
-    const int blk = e >> 10, r = (e >> 6) & 15, lane = e & 63;
-    const int m = (blk / WB) * 32 + mfma32_row(r, lane);
-    const int n = (blk % WB) * 32 + mfma32_col(lane);
-    sub[m][n] = acc;
-    if (row0 + m < d && col0 + n < d) {
-      float* h = H + (size_t)(row0 + m) * d + (col0 + n);
-      *h += acc;
+  const size_t item_stride4 = (size_t)ntiles * 4 * NEL / 4;
+  const float4* src = reinterpret_cast<const float4*>(partial + ((size_t)q * 4 + wave) * NEL);
+  const int tid = threadIdx.x;
+  float4 acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < splits; ++s) {
+    const float4* ps = src + s * item_stride4;
+    float4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = ps[tid + 256 * i];     // all loads in flight
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      acc[i].x += v[i].x; acc[i].y += v[i].y; acc[i].z += v[i].z; acc[i].w += v[i].w;
     }
   }
-  if (I == J) return;                  // diagonal tiles were computed in full
-  __syncthreads();
-  // mirror: H[col0 + n][row0 + m] += sub[m][n]
-  for (int e = threadIdx.x; e < E * E; e += 256) {
-    const int n = e / E, m = e % E;
-    if (row0 + m < d && col0 + n < d) {
-      float* h = H + (size_t)(col0 + n) * d + (row0 + m);
-      *h += sub[m][n];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float a4[4] = {acc[i].x, acc[i].y, acc[i].z, acc[i].w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * (tid + 256 * i) + u;
+      const int blk = e >> 10, r = (e >> 6) & 15, lane = e & 63;
+      const int m = (blk / WB) * 32 + mfma32_row(r, lane);
+      const int n = (blk % WB) * 32 + mfma32_col(lane);
+      sub[m][n] = 2.0f * a4[u];
     }
+  }
+  __syncthreads();
+  // H[row0 + m][col0 + n] += sub[m][n], rows coalesced
+  for (int e = tid; e < E * E; e += 256) {
+    const int m = e / E, n = e % E;
+    if (row0 + m < d && col0 + n < d) H[(size_t)(row0 + m) * d + (col0 + n)] += sub[m][n];
+  }
+  if (I == J) return;                  // diagonal tiles were computed in full
+  // mirror: H[col0 + n][row0 + m] += sub[m][n]
+  for (int e = tid; e < E * E; e += 256) {
+    const int n = e / E, m = e % E;
+    if (row0 + m < d && col0 + n < d) H[(size_t)(col0 + n) * d + (row0 + m)] += sub[m][n];
   }
 }
 

@@ -113,10 +113,12 @@ __global__ __launch_bounds__(256) void gather_flip_kernel(const float* __restric
 // halves.  Column j of the left half is retired at that step, so it stores the
 // new column j of the right half.  The finished block holds R^-T (lower incl.
 // diagonal) and R (strict upper).  Thread t owns column t%128 and rows
-// 16*(t/128) .. +15 in registers; pivot rows travel through LDS.
+// 16*(t/128) .. +15 in registers (a wave's rows are uniform); pivot rows go
+// through LDS.  The step loop is unrolled by 16 so that register indices and
+// the "row below the pivot" tests are compile-time.
 __global__ __launch_bounds__(1024) void chol_diag_kernel(float* __restrict__ A, int np, int k,
                                                          int* __restrict__ flag) {
-  __shared__ float rowbuf[2][kNB];
+  __shared__ __attribute__((aligned(16))) float rowbuf[2][kNB];
   const int t = threadIdx.x;
   const int x = t & (kNB - 1), g = t >> 7;
   float* blk = A + (size_t)k * kNB * np + (size_t)k * kNB;
@@ -124,27 +126,39 @@ __global__ __launch_bounds__(1024) void chol_diag_kernel(float* __restrict__ A, 
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = blk[(size_t)(16 * g + i) * np + x];
 
-  for (int j = 0; j < kNB; ++j) {
-    float* rb = rowbuf[j & 1];
-    if (g == (j >> 4)) {
+#pragma unroll 1
+  for (int jb = 0; jb < kNB / 16; ++jb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (i == (j & 15)) rb[x] = v[i];
-    }
-    __syncthreads();
-    const float p = rb[j];
-    if (t == 0 && !(p > 0.0f)) flag[0] = 1;
-    const float sc = 1.0f / sqrtf(p);
-    const float rjx = (x == j) ? sc : rb[x] * sc;
-    if (16 * g + 15 >= j) {
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = 16 * jb + jj;
+      float* rb = rowbuf[jj & 1];
+      if (g == jb) rb[x] = v[jj];
+      __syncthreads();
+      if (g < jb) continue;                 // rows already final
+      const float p = rb[j];
+      if (g == jb && x == j && !(p > 0.0f)) flag[0] = 1;   // an active lane reports the pivot
+      // 1/sqrt(p): hardware estimate refined by one Newton step
+      float sc = __builtin_amdgcn_rsqf(p);
+      sc = sc * fmaf(-0.5f * p * sc, sc, 1.5f);
+      const bool isj = (x == j);
+      const float rjx = isj ? sc : rb[x] * sc;
+      const float keep = isj ? 0.0f : 1.0f;
+      const float cmul = sc * rjx;          // row i: v -= rb[i] * sc * rjx
+      const float4* r4 = reinterpret_cast<const float4*>(rb + 16 * g);
+      float m[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 16 * g + i;
-        if (row == j) {
-          v[i] = rjx;
-        } else if (row > j) {
-          const float mi = rb[row] * sc;
-          v[i] = ((x == j) ? 0.0f : v[i]) - mi * rjx;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 u = r4[i4];
+        m[4 * i4 + 0] = u.x; m[4 * i4 + 1] = u.y; m[4 * i4 + 2] = u.z; m[4 * i4 + 3] = u.w;
+      }
+      if (g > jb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = fmaf(-m[i], cmul, v[i] * keep);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (i == jj) v[i] = rjx;
+          else if (i > jj) v[i] = fmaf(-m[i], cmul, v[i] * keep);
         }
       }
     }

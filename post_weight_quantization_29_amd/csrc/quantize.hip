@@ -17,10 +17,12 @@
 //   trailing GEMM:  W[:, b1:] -= Err * U[b0:b1, b1:] (fp32 MFMA).
 #include "gemm_f32.h"
 
+#include <utility>
+
 namespace gptq {
 
 constexpr int kQB = 128;          // block width (lazy batch)
-constexpr int kQRows = 64;        // rows per workgroup (256 threads, 4 per row)
+constexpr int kQRows = 16;        // rows per workgroup (one wave, 4 lanes per row)
 constexpr int kUP = 36;           // LDS pitch of one (column j, lane q) slot row
 
 // ---------------------------------------------------------------- W gather
@@ -43,15 +45,6 @@ GPTQ_DEV float quad_bcast_c(float v) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), P | (P << 2) | (P << 4) | (P << 6),
                                       0xF, 0xF, false));
-}
-// p is a constant after unrolling; the switch folds away
-GPTQ_DEV float quad_bcast(float v, int p) {
-  switch (p) {
-    case 0: return quad_bcast_c<0>(v);
-    case 1: return quad_bcast_c<1>(v);
-    case 2: return quad_bcast_c<2>(v);
-    default: return quad_bcast_c<3>(v);
-  }
 }
 GPTQ_DEV float quad_min(float v) {
   v = fminf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
@@ -94,19 +87,27 @@ struct PanelArgs {
   float maxq;
 };
 
-__global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
-  __shared__ __attribute__((aligned(16))) float sU[kQB][4][kUP];   // sU[j][q][i] = U[b0+j][b0+4i+q]
+// One wave per workgroup: 16 rows, 4 lanes per row (lane q holds the block's
+// columns 4t+q, t = 0..31).  Every column step is instantiated separately
+// (template fold over the 128 columns), so the row slice stays in registers
+// with compile-time indices.  GT > 0: groups of GT columns inside the block
+// (group starts known at compile time); GT == 0: groups of G >= 128 columns,
+// which can only start at the block's first column.
+template <int GT>
+__global__ __launch_bounds__(64) void panel_kernel(PanelArgs a) {
+  __shared__ float4 sU4[kQB][4][kUP / 4];   // sU4[j][q][t/4] = U[b0+j][b0+4t+q .. +12 step 4]
   __shared__ float sInv[kQB];
   __shared__ int sPerm[kQB];
 
   const int tid = threadIdx.x;
-  for (int e = tid; e < kQB * kQB; e += 256) {
+  float* sU = reinterpret_cast<float*>(&sU4[0][0][0]);
+  for (int e = tid; e < kQB * kQB; e += 64) {
     const int j = e >> 7, c = e & 127;
     float v = 0.0f;
-    if (j < a.bw && c < a.bw) v = a.U[(size_t)(a.b0 + j) * a.d + a.b0 + c];
-    sU[j][c & 3][c >> 2] = v;
+    if (j < a.bw && c < a.bw && c > j) v = a.U[(size_t)(a.b0 + j) * a.d + a.b0 + c];
+    sU[(j * 4 + (c & 3)) * kUP + (c >> 2)] = v;
   }
-  for (int j = tid; j < kQB; j += 256) {
+  for (int j = tid; j < kQB; j += 64) {
     sInv[j] = (j < a.bw) ? 1.0f / a.U[(size_t)(a.b0 + j) * a.d + a.b0 + j] : 0.0f;
     sPerm[j] = (j < a.bw) ? a.perm[a.b0 + j] : 0;
   }
@@ -117,81 +118,116 @@ __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
   const bool rv = row < a.d_out;
   const int rowc = rv ? row : 0;     // clamped row for loads; stores are masked
   const float* wrow = a.Wp + (size_t)rowc * a.d + a.b0;
+  const int bw = a.bw;
 
   float w[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) w[i] = (4 * i + q < a.bw) ? wrow[4 * i + q] : 0.0f;
+  for (int t = 0; t < 32; ++t) w[t] = (4 * t + q < bw) ? wrow[4 * t + q] : 0.0f;
 
   float scale = 1.0f, zero = 0.0f, rscale = 1.0f;
-  const int G = a.G;
-  if (a.b0 % G != 0) {
+  if (GT == 0 && a.b0 % a.G != 0) {
     // a group wider than the block started in an earlier block: continue with
     // the parameters that launch stored
-    scale = a.scales[(size_t)rowc * a.ng + a.b0 / G];
-    zero = (float)a.zeros[(size_t)rowc * a.ng + a.b0 / G];
+    scale = a.scales[(size_t)rowc * a.ng + a.b0 / a.G];
+    zero = (float)a.zeros[(size_t)rowc * a.ng + a.b0 / a.G];
     rscale = 1.0f / scale;
   }
+  // results of the lane's own columns, stored once at the end
+  float eown[32], qown[32];
+  uint32_t cown[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) cown[t] = 0u;
 
+  auto group_start = [&]<int J>() {
+    constexpr int I = J / 4;
+    float mn = INFINITY, mx = -INFINITY;
+    if constexpr (GT > 0) {
+      // slots I .. I + GT/4 - 1 hold the group's columns J .. J + GT - 1
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int j = 4 * i + p;                 // column inside the block
-      if (j >= a.bw) break;
-      const int jg = a.b0 + j;                 // processing-order column
-      if (p == 0 && jg % G == 0) {
-        // group [jg, min(jg + G, d)): in-block part from registers (slots t >= i
-        // hold the columns >= j), the rest (G larger than the block) from the
-        // work copy, which already holds every earlier block's lazy update
-        const int gend = min(jg + G, a.d);
-        float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-        for (int t = i; t < 32; ++t) {
-          const int cg = a.b0 + 4 * t + q;
-          if (4 * t + q < a.bw && cg < gend) {
-            mn = fminf(mn, w[t]);
-            mx = fmaxf(mx, w[t]);
-          }
-        }
-        for (int cg = a.b0 + a.bw + q; cg < gend; cg += 4) {
-          const float v = a.Wp[(size_t)rowc * a.d + cg];
-          mn = fminf(mn, v);
-          mx = fmaxf(mx, v);
-        }
-        mn = quad_min(mn);
-        mx = quad_max(mx);
-        grid_params(mn, mx, a.maxq, scale, zero);
-        rscale = 1.0f / scale;
-        if (rv && q == 0) {
-          a.scales[(size_t)row * a.ng + jg / G] = scale;
-          a.zeros[(size_t)row * a.ng + jg / G] = (int)zero;
+      for (int t = I; t < I + GT / 4; ++t) {
+        if (4 * t + q < bw) {
+          mn = fminf(mn, w[t]);
+          mx = fmaxf(mx, w[t]);
         }
       }
-      const float wj = quad_bcast(w[i], p);
-      // correctly rounded wj/scale from the reciprocal (one Newton correction)
-      const float t0 = wj * rscale;
-      const float res = fmaf(-t0, scale, wj);
-      const float tq = fmaf(res, rscale, t0);
-      const float c = fminf(fmaxf(rintf(tq) + zero, 0.0f), a.maxq);
-      const float qv = scale * (c - zero);
-      const float e = (wj - qv) * sInv[j];
-      if (q == p && rv) {
-        const int oc = sPerm[j];
-        a.codes[(size_t)row * a.d + oc] = (uint8_t)(int)c;
-        if (a.Q) a.Q[(size_t)row * a.d + oc] = qv;
-        a.ErrT[(size_t)j * a.d_out + row] = e;
-      }
-      // w[t] -= e * U[j][4t+q] for the later columns of the block (slots t >= i;
-      // the lanes' entries at columns <= j are retired and ignored)
-      const float* urow = &sU[j][q][0];
+    } else {
+      // J == 0: the whole block (columns < bw), then the rest of the group
+      // from the work copy, which holds every earlier block's lazy update
 #pragma unroll
-      for (int t = (i & ~3); t < 32; t += 4) {
-        const float4 u4 = *reinterpret_cast<const float4*>(urow + t);
-        if (t + 0 >= i) w[t + 0] = fmaf(-e, u4.x, w[t + 0]);
-        if (t + 1 >= i) w[t + 1] = fmaf(-e, u4.y, w[t + 1]);
-        if (t + 2 >= i) w[t + 2] = fmaf(-e, u4.z, w[t + 2]);
-        if (t + 3 >= i) w[t + 3] = fmaf(-e, u4.w, w[t + 3]);
+      for (int t = 0; t < 32; ++t) {
+        if (4 * t + q < bw) {
+          mn = fminf(mn, w[t]);
+          mx = fmaxf(mx, w[t]);
+        }
       }
+      const int gend = min(a.b0 + a.G, a.d);
+      const float* wr = a.Wp + (size_t)rowc * a.d;
+      for (int cg = a.b0 + bw + q; cg < gend; cg += 4) {
+        const float v = wr[cg];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+    }
+    mn = quad_min(mn);
+    mx = quad_max(mx);
+    grid_params(mn, mx, a.maxq, scale, zero);
+    rscale = 1.0f / scale;
+    const int gi = (GT > 0) ? (a.b0 + J) / GT : a.b0 / a.G;
+    if (rv && q == 0) {
+      a.scales[(size_t)row * a.ng + gi] = scale;
+      a.zeros[(size_t)row * a.ng + gi] = (int)zero;
+    }
+  };
+
+  auto step = [&]<int J>() {
+    constexpr int I = J / 4, P = J % 4;
+    if (J >= bw) return;
+    if constexpr (GT > 0) {
+      if constexpr (J % GT == 0) group_start.template operator()<J>();
+    } else {
+      if constexpr (J == 0) {
+        if (a.b0 % a.G == 0) group_start.template operator()<0>();
+      }
+    }
+    const float wj = quad_bcast_c<P>(w[I]);
+    // correctly rounded wj/scale from the reciprocal (one residual correction)
+    const float t0 = wj * rscale;
+    const float res = fmaf(-t0, scale, wj);
+    const float tq = fmaf(res, rscale, t0);
+    const float c = fminf(fmaxf(rintf(tq) + zero, 0.0f), a.maxq);
+    const float qv = scale * (c - zero);
+    const float e = (wj - qv) * sInv[J];
+    if (q == P) {
+      eown[I] = e;
+      qown[I] = qv;
+      cown[I >> 2] |= (uint32_t)c << (8 * (I & 3));
+    }
+    // w[t] -= e * U[J][4t+q] for the later columns of the block (slots t >= I;
+    // entries at columns <= J are retired, and U is zero there)
+#pragma unroll
+    for (int t = (I & ~3); t < 32; t += 4) {
+      const float4 u4 = sU4[J][q][t >> 2];
+      if (t + 0 >= I) w[t + 0] = fmaf(-e, u4.x, w[t + 0]);
+      if (t + 1 >= I) w[t + 1] = fmaf(-e, u4.y, w[t + 1]);
+      if (t + 2 >= I) w[t + 2] = fmaf(-e, u4.z, w[t + 2]);
+      if (t + 3 >= I) w[t + 3] = fmaf(-e, u4.w, w[t + 3]);
+    }
+  };
+  [&]<int... Js>(std::integer_sequence<int, Js...>) {
+    (step.template operator()<Js>(), ...);
+  }(std::make_integer_sequence<int, kQB>{});
+
+  if (!rv) return;
+  uint8_t* crow = a.codes + (size_t)row * a.d;
+  float* qrow = a.Q ? a.Q + (size_t)row * a.d : nullptr;
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int j = 4 * t + q;
+    if (j < bw) {
+      const int oc = sPerm[j];
+      crow[oc] = (uint8_t)(cown[t >> 2] >> (8 * (t & 3)));
+      if (qrow) qrow[oc] = qown[t];
+      a.ErrT[(size_t)j * a.d_out + row] = eown[t];
     }
   }
 }
@@ -308,11 +344,21 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   pa.d_out = d_out; pa.d = d; pa.G = G; pa.ng = ng;
   pa.maxq = (float)((1 << cfg->bits) - 1);
   const int nrow_blocks = (d_out + kQRows - 1) / kQRows;
+  // in-block group sizes are compile-time; wider groups (or one per row) use 0
+  const int gt = (G <= kQB && kQB % G == 0 && G % 4 == 0) ? G : 0;
   for (int b0 = 0; b0 < d; b0 += kQB) {
     const int bw = std::min(kQB, d - b0);
     pa.b0 = b0;
     pa.bw = bw;
-    panel_kernel<<<nrow_blocks, 256, 0, s>>>(pa);
+    switch (gt) {
+      case 4: panel_kernel<4><<<nrow_blocks, 64, 0, s>>>(pa); break;
+      case 8: panel_kernel<8><<<nrow_blocks, 64, 0, s>>>(pa); break;
+      case 16: panel_kernel<16><<<nrow_blocks, 64, 0, s>>>(pa); break;
+      case 32: panel_kernel<32><<<nrow_blocks, 64, 0, s>>>(pa); break;
+      case 64: panel_kernel<64><<<nrow_blocks, 64, 0, s>>>(pa); break;
+      case 128: panel_kernel<128><<<nrow_blocks, 64, 0, s>>>(pa); break;
+      default: panel_kernel<0><<<nrow_blocks, 64, 0, s>>>(pa); break;
+    }
     GPTQ_LAUNCH_CHECK();
     const int b1 = b0 + bw;
     if (b1 < d) {
