@@ -6,7 +6,9 @@
 //
 // Aop(m, k) = A[k*lda + m] ("k-major", A_KMAJOR) or A[m*lda + k];
 // Bop(k, n) = B[k*ldb + n] always.  Tiles are 128x128, four waves (2x2) of
-// 64x64, 16 values of k per LDS stage, double-buffered.  Several independent
+// 64x64; k runs in chunks of 64, each loaded into registers (float4 when the
+// leading dimensions allow) while the previous chunk is multiplied out of
+// LDS, so global latency hides behind a chunk of MFMA work.  Several independent
 // problems of one shape class (a "group") run in one launch; each workgroup
 // finds its problem from the tile prefix sums passed by value.
 //
@@ -20,9 +22,8 @@
 namespace gptq {
 
 constexpr int kGT = 128;          // tile edge
-constexpr int kGK = 16;           // k per stage
-constexpr int kGP = kGT + 32;     // LDS pitch (floats): the two half-waves of an
-                                  // operand read sit 32 banks apart
+constexpr int kGK = 64;           // k per chunk: loaded into registers one chunk ahead
+constexpr int kGP = kGT + 4;      // LDS pitch (floats)
 constexpr int kGemmMaxGroup = 32;
 
 struct GemmProblem {
@@ -42,18 +43,82 @@ struct GemmGroup {
 
 enum GemmEpilogue { kStore = 0, kDot = 1 };
 
-template <bool A_KMAJOR, int EPI>
+// 4 consecutive floats p[0..3], the ones at index >= lim read as 0.  VEC: the
+// address is 16-byte aligned whenever lim >= 4.
+template <bool VEC>
+GPTQ_DEV float4 load4(const float* p, int lim) {
+  if (VEC && lim >= 4) return *reinterpret_cast<const float4*>(p);
+  float4 r;
+  r.x = lim > 0 ? p[0] : 0.0f;
+  r.y = lim > 1 ? p[1] : 0.0f;
+  r.z = lim > 2 ? p[2] : 0.0f;
+  r.w = lim > 3 ? p[3] : 0.0f;
+  return r;
+}
+
+// One chunk of 64 k: A chunk 128 (m) x 64 (k), B chunk 64 (k) x 128 (n); each
+// thread holds 8 float4 of each.
+template <bool A_KMAJOR, bool VEC>
+GPTQ_DEV void gemm_gload(const GemmProblem& P, int m0, int n0, int k0, int khi, int tid,
+                         float4 (&ra)[8], float4 (&rb)[8]) {
+  // B (and k-major A): row k = k0 + tid/32 + 8i, columns c = 4*(tid%32) .. +3
+  const int c4 = 4 * (tid & 31);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = k0 + (tid >> 5) + 8 * i;
+    const bool kv = k < khi;
+    rb[i] = kv ? load4<VEC>(P.B + (size_t)k * P.ldb + n0 + c4, P.N - n0 - c4)
+               : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (A_KMAJOR)
+      ra[i] = kv ? load4<VEC>(P.A + (size_t)k * P.lda + m0 + c4, P.M - m0 - c4)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (!A_KMAJOR) {
+    // m-major A: row m = m0 + tid/16 + 16i, k = k0 + 4*(tid%16) .. +3
+    const int kq = k0 + 4 * (tid & 15);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + (tid >> 4) + 16 * i;
+      ra[i] = (m < P.M) ? load4<VEC>(P.A + (size_t)m * P.lda + kq, khi - kq)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+template <bool A_KMAJOR>
+GPTQ_DEV void gemm_lstore(float* sA, float* sB, int tid, const float4 (&ra)[8], const float4 (&rb)[8]) {
+  const int c4 = 4 * (tid & 31);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int kr = (tid >> 5) + 8 * i;
+    *reinterpret_cast<float4*>(sB + kr * kGP + c4) = rb[i];
+    if (A_KMAJOR) *reinterpret_cast<float4*>(sA + kr * kGP + c4) = ra[i];
+  }
+  if (!A_KMAJOR) {
+    const int kq = 4 * (tid & 15);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int mr = (tid >> 4) + 16 * i;
+      sA[(kq + 0) * kGP + mr] = ra[i].x;
+      sA[(kq + 1) * kGP + mr] = ra[i].y;
+      sA[(kq + 2) * kGP + mr] = ra[i].z;
+      sA[(kq + 3) * kGP + mr] = ra[i].w;
+    }
+  }
+}
+
+template <bool A_KMAJOR, int EPI, bool VEC>
 __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float alpha, float beta,
                                                           int kloFromM, int khiFromN, int upperOnly,
                                                           double* __restrict__ dot_out) {
-  __shared__ __attribute__((aligned(16))) float sA[2][kGK * kGP];
-  __shared__ __attribute__((aligned(16))) float sB[2][kGK * kGP];
+  __shared__ __attribute__((aligned(16))) float sA[kGK * kGP];
+  __shared__ __attribute__((aligned(16))) float sB[kGK * kGP];
   __shared__ double sRed[4];
 
   const int wg = blockIdx.x;
   int pi = 0;
   while (pi + 1 < grp.count && grp.tile_start[pi + 1] <= wg) ++pi;
-  const GemmProblem& P = grp.p[pi];
+  const GemmProblem P = grp.p[pi];          // fields held in registers from here on
   const int local = wg - grp.tile_start[pi];
   const int tn = (P.N + kGT - 1) / kGT;
   const int m0 = (local / tn) * kGT, n0 = (local % tn) * kGT;
@@ -74,64 +139,54 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   if (!skip && klo < khi) {
-    float ra[8], rb[8];
-    // B (and k-major A): 16 rows of 128 -> thread owns column c = tid%128, rows r0+2i
-    // m-major A: 128 rows of 16 -> thread owns k = tid%16, rows tid/16 + 16i
-    auto gload = [&](int k0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kr = (tid >> 7) + 2 * i, c = tid & 127;
-        const int k = k0 + kr, n = n0 + c;
-        rb[i] = (k < khi && n < P.N) ? P.B[(size_t)k * P.ldb + n] : 0.0f;
-        if (A_KMAJOR) {
-          const int m = m0 + c;
-          ra[i] = (k < khi && m < P.M) ? P.A[(size_t)k * P.lda + m] : 0.0f;
-        } else {
-          const int kk = k0 + (tid & 15), mr = (tid >> 4) + 16 * i, m = m0 + mr;
-          ra[i] = (kk < khi && m < P.M) ? P.A[(size_t)m * P.lda + kk] : 0.0f;
-        }
-      }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kr = (tid >> 7) + 2 * i, c = tid & 127;
-        sB[buf][kr * kGP + c] = rb[i];
-        if (A_KMAJOR) {
-          sA[buf][kr * kGP + c] = ra[i];
-        } else {
-          sA[buf][(tid & 15) * kGP + (tid >> 4) + 16 * i] = ra[i];
-        }
-      }
-    };
-    const int kbeg = klo - (klo % kGK);
-    gload(kbeg);
-    lstore(0);
-    __syncthreads();
-    int buf = 0;
-    for (int k0 = kbeg; k0 < khi; k0 += kGK) {
-      const bool more = k0 + kGK < khi;
-      if (more) gload(k0 + kGK);
-      const float* a_s = sA[buf];
-      const float* b_s = sB[buf];
-#pragma unroll
-      for (int k2 = 0; k2 < kGK; k2 += 2) {
+    float4 ra[8], rb[8];
+    gemm_gload<A_KMAJOR, VEC>(P, m0, n0, klo, khi, tid, ra, rb);
+    for (int k0 = klo; k0 < khi; k0 += kGK) {
+      __syncthreads();                         // the previous chunk is consumed
+      gemm_lstore<A_KMAJOR>(sA, sB, tid, ra, rb);
+      __syncthreads();
+      if (k0 + kGK < khi) gemm_gload<A_KMAJOR, VEC>(P, m0, n0, k0 + kGK, khi, tid, ra, rb);
+      const int kn = min(kGK, khi - k0);       // zero-filled beyond khi: keep even steps
+#pragma unroll 4
+      for (int k2 = 0; k2 < kn; k2 += 2) {
         const int row = (k2 + (lane >> 5)) * kGP + (lane & 31);
-        const float a0 = a_s[row + wm * 64], a1 = a_s[row + wm * 64 + 32];
-        const float b0 = b_s[row + wn * 64], b1 = b_s[row + wn * 64 + 32];
+        const float a0 = sA[row + wm * 64], a1 = sA[row + wm * 64 + 32];
+        const float b0 = sB[row + wn * 64], b1 = sB[row + wn * 64 + 32];
         acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
         acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
         acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
         acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
       }
-      if (more) lstore(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
     }
   }
 
   if (EPI == kStore) {
     if (skip) return;
+    // all reads of C first, then all writes: a read placed after a write that
+    // might alias it would wait for that write's round trip
+    if (beta != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float cold[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+            const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
+            cold[r] = (m < P.M && n < P.N) ? P.C[(size_t)m * P.ldc + n] : 0.0f;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = alpha * acc[i][j][r] + beta * cold[r];
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= alpha;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -140,12 +195,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
           const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
-          if (m < P.M && n < P.N) {
-            float* c = P.C + (size_t)m * P.ldc + n;
-            float v = alpha * acc[i][j][r];
-            if (beta != 0.0f) v += beta * *c;
-            *c = v;
-          }
+          if (m < P.M && n < P.N) P.C[(size_t)m * P.ldc + n] = acc[i][j][r];
         }
   } else {
     double s = 0.0;
@@ -169,18 +219,29 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
 inline int gemm_tiles(int M, int N) { return ((M + kGT - 1) / kGT) * ((N + kGT - 1) / kGT); }
 
 // Launch one group (count <= kGemmMaxGroup).  Returns the total tile count.
+// float4 global loads are used when every leading dimension is a multiple of 4
+// and every base pointer is 16-byte aligned (tile origins are multiples of 128).
 template <bool A_KMAJOR, int EPI>
 inline int launch_gemm_group(GemmGroup& g, float alpha, float beta, int kloFromM, int khiFromN,
                              int upperOnly, double* dot_out, hipStream_t s) {
   int t = 0;
+  bool vec = true;
   for (int i = 0; i < g.count; ++i) {
     g.tile_start[i] = t;
     t += gemm_tiles(g.p[i].M, g.p[i].N);
+    const GemmProblem& p = g.p[i];
+    vec = vec && (p.lda % 4 == 0) && (p.ldb % 4 == 0) &&
+          ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 15) == 0;
   }
   g.tile_start[g.count] = t;
-  if (t > 0)
-    gemm_f32_kernel<A_KMAJOR, EPI><<<t, 256, 0, s>>>(g, alpha, beta, kloFromM, khiFromN, upperOnly,
-                                                    dot_out);
+  if (t > 0) {
+    if (vec)
+      gemm_f32_kernel<A_KMAJOR, EPI, true><<<t, 256, 0, s>>>(g, alpha, beta, kloFromM, khiFromN,
+                                                           upperOnly, dot_out);
+    else
+      gemm_f32_kernel<A_KMAJOR, EPI, false><<<t, 256, 0, s>>>(g, alpha, beta, kloFromM, khiFromN,
+                                                            upperOnly, dot_out);
+  }
   return t;
 }
 

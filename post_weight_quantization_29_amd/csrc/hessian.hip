@@ -369,16 +369,30 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
     }
   }
   __syncthreads();
-  // H[row0 + m][col0 + n] += sub[m][n], rows coalesced
-  for (int e = tid; e < E * E; e += 256) {
-    const int m = e / E, n = e % E;
-    if (row0 + m < d && col0 + n < d) H[(size_t)(row0 + m) * d + (col0 + n)] += sub[m][n];
-  }
-  if (I == J) return;                  // diagonal tiles were computed in full
-  // mirror: H[col0 + n][row0 + m] += sub[m][n]
-  for (int e = tid; e < E * E; e += 256) {
-    const int n = e / E, m = e % E;
-    if (row0 + m < d && col0 + n < d) H[(size_t)(col0 + n) * d + (row0 + m)] += sub[m][n];
+  // H[row0 + m][col0 + n] += sub[m][n] (rows coalesced), then the mirror
+  // H[col0 + n][row0 + m] += sub[m][n]; each batch of 16 reads is issued before
+  // its 16 writes so the read-modify-writes do not serialize
+  constexpr int NB = 16;
+  for (int pass = 0; pass < ((I == J) ? 1 : 2); ++pass) {
+    for (int e0 = 0; e0 < E * E; e0 += 256 * NB) {
+      float old[NB];
+      size_t off[NB];
+      bool ok[NB];
+      float add[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int e = e0 + u * 256 + tid;
+        const int a = e / E, b = e % E;           // pass 0: (m, n) = (a, b); pass 1: (n, m)
+        const int m = pass ? b : a, n = pass ? a : b;
+        ok[u] = (e < E * E) && row0 + m < d && col0 + n < d;
+        off[u] = pass ? (size_t)(col0 + n) * d + (row0 + m) : (size_t)(row0 + m) * d + (col0 + n);
+        add[u] = ok[u] ? sub[m][n] : 0.0f;
+        old[u] = ok[u] ? H[off[u]] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (ok[u]) H[off[u]] = old[u] + add[u];
+    }
   }
 }
 

@@ -101,11 +101,21 @@ __global__ __launch_bounds__(64) void panel_kernel(PanelArgs a) {
 
   const int tid = threadIdx.x;
   float* sU = reinterpret_cast<float*>(&sU4[0][0][0]);
-  for (int e = tid; e < kQB * kQB; e += 64) {
-    const int j = e >> 7, c = e & 127;
-    float v = 0.0f;
-    if (j < a.bw && c < a.bw && c > j) v = a.U[(size_t)(a.b0 + j) * a.d + a.b0 + c];
-    sU[(j * 4 + (c & 3)) * kUP + (c >> 2)] = v;
+  // U's diagonal block (strict upper part), 16 independent loads in flight per lane
+  for (int e0 = 0; e0 < kQB * kQB; e0 += 64 * 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + u * 64 + tid;
+      const int j = e >> 7, c = e & 127;
+      v[u] = (j < a.bw && c < a.bw && c > j) ? a.U[(size_t)(a.b0 + j) * a.d + a.b0 + c] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + u * 64 + tid;
+      const int j = e >> 7, c = e & 127;
+      sU[(j * 4 + (c & 3)) * kUP + (c >> 2)] = v[u];
+    }
   }
   for (int j = tid; j < kQB; j += 64) {
     sInv[j] = (j < a.bw) ? 1.0f / a.U[(size_t)(a.b0 + j) * a.d + a.b0 + j] : 0.0f;
