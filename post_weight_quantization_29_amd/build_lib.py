@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["hessian.hip", "hinv.hip", "quantize.hip", "error.hip"]
 ARCH = "gfx950"
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-result",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-result", "-Wno-inline-asm",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

@@ -25,15 +25,90 @@ GPTQ_DEV void tri_tile(int q, int& I, int& J) {
   J = q - i * (i + 1) / 2;
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (XCD = w % 8), each
+// with its own L2.  Tiles are ordered by 4x4 super-blocks of the lower
+// triangle and cut into 8 contiguous chunks, one per XCD, so the tiles an XCD
+// runs share few channel panels; inside an XCD the items run split-major, so
+// the co-resident workgroups read the same token range.  Returns false for the
+// padding workgroups past the last tile of a chunk.
+constexpr int kXCD = 8;
+constexpr int kSB = 4;
+
+GPTQ_DEV bool xcd_item(int w, int nt, int ntiles, int splits, int& s, int& I, int& J) {
+  const int chunk = (ntiles + kXCD - 1) / kXCD;
+  const int x = w % kXCD, k = w / kXCD;
+  s = k / chunk;
+  const int L = x * chunk + (k - s * chunk);
+  if (s >= splits || L >= ntiles) return false;
+  // walk the super-blocks (row-major over the lower triangle) to tile number L
+  const int nsb = (nt + kSB - 1) / kSB;
+  int rem = L;
+  for (int ib = 0; ib < nsb; ++ib) {
+    const int h = min(kSB, nt - ib * kSB);
+    for (int jb = 0; jb <= ib; ++jb) {
+      const int wdt = min(kSB, nt - jb * kSB);
+      const int cnt = (ib == jb) ? h * (h + 1) / 2 : h * wdt;
+      if (rem < cnt) {
+        if (ib == jb) {
+          int r = 0;
+          while (rem >= r + 1) { rem -= r + 1; ++r; }
+          I = ib * kSB + r;
+          J = jb * kSB + rem;
+        } else {
+          I = ib * kSB + rem / wdt;
+          J = jb * kSB + rem % wdt;
+        }
+        return true;
+      }
+      rem -= cnt;
+    }
+  }
+  return false;
+}
+
+GPTQ_DEV int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
+
 // ---------------------------------------------------------------------------
 // 16-bit inputs: bf16 / fp16, v_mfma_f32_32x32x16_{bf16,f16}
-// Workgroup tile 256x256, 4 waves (2x2) of 128x128, 32 tokens per LDS stage.
+// Workgroup tile 256x256, 4 waves (2x2) of 128x128, 32 tokens per stage.
+//
+// Stages are copied HBM -> LDS by buffer_load ... lds (16 bytes per lane, the
+// 64 lanes of one instruction fill 1 KB of LDS in lane order) into two slots:
+// stage kk+1 streams in while stage kk is multiplied, with no staging
+// registers.  A stage row (one token, 256 channels) is 512 bytes, unpadded;
+// its 16-byte chunk c sits at slot c ^ 4*(row % 4), which keeps the
+// transposing operand reads free of bank conflicts (the DMA side applies the
+// swizzle by permuting the lanes' source addresses).  Tokens past the end and
+// channels past d read as zero through the buffer descriptor's range.
 // ---------------------------------------------------------------------------
 constexpr int kT16 = 256;          // tile edge (channels)
-constexpr int kK16 = 32;           // tokens per stage
-constexpr int kP16 = kT16 + 32;    // LDS row pitch in elements: consecutive token
-                                   // rows land 16 banks apart, so the four rows a
-                                   // 32-lane transposing read touches never collide
+constexpr int kK16 = 64;           // tokens per stage (4 k-slices of 16)
+constexpr int kRow16 = kT16;       // LDS row pitch in elements (512 bytes)
+constexpr int kStage16 = kK16 * kRow16;
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// buffer_load_dwordx4 ... lds: each lane's 16 bytes go to LDS at M0 + 16*lane.
+// Issued from asm so that the compiler does not model an outstanding LDS write
+// (it would otherwise drain every copy in flight before each LDS read); the
+// kernel waits for the copies itself with counted s_waitcnt vmcnt.  All
+// operands are wave-uniform except the per-lane offset.
+GPTQ_DEV void dma16(i32x4_t rsrc, const void* lds_dst, int voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS const void*)lds_dst);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(rsrc[0]);
+  r[1] = __builtin_amdgcn_readfirstlane(rsrc[1]);
+  r[2] = __builtin_amdgcn_readfirstlane(rsrc[2]);
+  r[3] = __builtin_amdgcn_readfirstlane(rsrc[3]);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+// workgroup barrier that also stops the compiler from moving memory accesses
+// across it, without the fence's drain of outstanding global loads
+GPTQ_DEV void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <typename T> struct Op16;
 template <> struct Op16<__bf16> {
@@ -45,6 +120,7 @@ template <> struct Op16<__bf16> {
   static GPTQ_DEV f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  static GPTQ_DEV float to_f32(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
 };
 template <> struct Op16<_Float16> {
   typedef f16x8_t v8;
@@ -57,99 +133,98 @@ template <> struct Op16<_Float16> {
   static GPTQ_DEV f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
+  static GPTQ_DEV float to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 };
 
-// K-contiguous operand for a 32-channel block starting at channel cbase of an
-// LDS stage [kK16][kP16], k-slice ks (16 tokens).  The transposing read gives
-// lane j of each 16-lane group g the element (4e + (j%16)/4, j%4) of the
-// group's 16x4 block of 64-bit loads; pointing lane 16g+4a+b at token
-// (8*(g/2) + 4r + a) and channels (16*(g%2) + 4b .. +3) hands lane l channel
-// cbase + l%32 at tokens 8*(l/32) + 4r + 0..3, i.e. MFMA k-slot order.
+// element offset of (token row, channel) inside a stage
+GPTQ_DEV int swz16(int row, int ch) { return row * kRow16 + ((((ch >> 3) ^ (4 * (row & 3)))) << 3) + (ch & 7); }
+
+// K-contiguous operand for a 32-channel block starting at channel cbase, k-slice
+// ks (16 tokens).  The transposing read gives lane j of each 16-lane group g the
+// element (4e + (j%16)/4, j%4) of the group's 16x4 block of 64-bit loads;
+// pointing lane 16g+4a+b at token (8*(g/2) + 4r + a) and channels
+// (16*(g%2) + 4b .. +3) hands lane l channel cbase + l%32 at tokens
+// 8*(l/32) + 4r + 0..3, i.e. MFMA k-slot order.
 template <typename T>
 GPTQ_DEV typename Op16<T>::v8 operand16(const T* stage, int ks, int cbase, int lane) {
   const int g = lane >> 4, a = (lane >> 2) & 3, b = lane & 3;
   const int tok = ks * 16 + 8 * (g >> 1) + a;
   const int ch = cbase + 16 * (g & 1) + 4 * b;
-  typename Op16<T>::v4 lo = Op16<T>::tr(stage + tok * kP16 + ch);
-  typename Op16<T>::v4 hi = Op16<T>::tr(stage + (tok + 4) * kP16 + ch);
+  typename Op16<T>::v4 lo = Op16<T>::tr(stage + swz16(tok, ch));
+  typename Op16<T>::v4 hi = Op16<T>::tr(stage + swz16(tok + 4, ch));
   typename Op16<T>::v8 v;
   v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
   v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
   return v;
 }
 
-// Partial layout (floats): [work item][wave 4][block 16 = mb*4+nb][reg 16][lane 64]
-template <typename T>
-GPTQ_DEV float elem16(uint32_t word, int half) {
-  const uint16_t h = (uint16_t)(word >> (16 * half));
-  if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
-    return __builtin_bit_cast(float, (uint32_t)h << 16);
-  } else {
-    return (float)__builtin_bit_cast(_Float16, h);
-  }
+GPTQ_DEV void wait_vm(int n) {
+  // s_waitcnt with vmcnt = n (0, 4 or 8 here), expcnt and lgkmcnt left open
+  if (n >= 8) __builtin_amdgcn_s_waitcnt((8 & 0xF) | (0x7 << 4) | (0xF << 8));
+  else if (n >= 4) __builtin_amdgcn_s_waitcnt((4 & 0xF) | (0x7 << 4) | (0xF << 8));
+  else __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
 }
 
 // Diagonal tiles also sum x^2 per channel in fp64 (the squares of 16-bit
 // values are exact), one partial row per (split, tile row): these sums are the
 // keys of the descending-diagonal column order, so the order does not hinge on
 // fp32 accumulation rounding.
+//
+// Partial layout (floats): [work item][wave 4][block 16 = mb*4+nb][reg 16][lane 64]
 template <typename T>
 __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X, int64_t n_tokens,
                                                          int d, int nt, int ntiles, int splits,
                                                          int64_t nk, float* __restrict__ partial,
                                                          double* __restrict__ pdiag) {
-  __shared__ __attribute__((aligned(16))) T sA[2][kK16 * kP16];
-  __shared__ __attribute__((aligned(16))) T sB[2][kK16 * kP16];
-  __shared__ double sD[8][kT16 + 1];
-
-  const int w = blockIdx.x;
-  const int s = w / ntiles;
-  const int q = w - s * ntiles;
-  int I, J;
-  tri_tile(q, I, J);
-  const bool diag = (I == J);
-  const int64_t ks0 = nk * s / splits, ks1 = nk * (s + 1) / splits;
+  __shared__ __attribute__((aligned(16))) T sA[2][kStage16];
+  __shared__ __attribute__((aligned(16))) T sB[2][kStage16];
+  __shared__ double sD[2][kT16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // global -> LDS copy assignment: 4 chunks of 8 channels per thread per panel
-  const int crow = tid >> 5;          // token row 0..7 (+8*i)
-  const int ccol = (tid & 31) * 8;    // channel offset in the panel
-  const int chA = I * kT16 + ccol, chB = J * kT16 + ccol;
-  const bool okA = chA < d, okB = chB < d;
+  // Persistent: workgroup (x = XCD, c) runs items c, c + nper, c + 2*nper, ... of
+  // XCD x's list, so the workgroups of an XCD move through the list in rounds
+  // and those sharing channel panels read the same tokens at the same time.
+  const int x = blockIdx.x % kXCD, c = blockIdx.x / kXCD, nper = gridDim.x / kXCD;
+  const int per_xcd = ((ntiles + kXCD - 1) / kXCD) * splits;
+  for (int kidx = c; kidx < per_xcd; kidx += nper) {
+  int s, I, J;
+  if (!xcd_item(kidx * kXCD + x, nt, ntiles, splits, s, I, J)) continue;
+  const int w = s * ntiles + tri_index(I, J);     // partial slot
+  const bool diag = (I == J);
+  const int64_t ks0 = nk * s / splits, ks1 = nk * (s + 1) / splits;
+  lds_barrier();                                   // the previous item is done with LDS
 
-  uint4 ra[4], rb[4];
-  auto gload = [&](int64_t kstep) {
-    const int64_t t0 = kstep * kK16;
+  // DMA assignment: instruction i of wave v fills stage rows 8i+2v (lanes 0-31)
+  // and 8i+2v+1 (lanes 32-63); lane slot L%32 of row R takes chunk
+  // (L%32) ^ 4(R%4), i.e. channels 8*that .. +7 of the panel.
+  constexpr int NI = kK16 / 8;                     // copies per panel per lane
+  int voffA[NI], voffB[NI];
+  const uint32_t row_bytes = (uint32_t)d * 2u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = t0 + crow + 8 * i;
-      const bool tv = t < n_tokens;
-      ra[i] = (tv && okA) ? *reinterpret_cast<const uint4*>(X + t * d + chA) : make_uint4(0, 0, 0, 0);
-      if (!diag)
-        rb[i] = (tv && okB) ? *reinterpret_cast<const uint4*>(X + t * d + chB) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  double dsum[8];
+  for (int i = 0; i < NI; ++i) {
+    const int R = 8 * i + 2 * wave + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (R & 3));
+    const int chA = I * kT16 + 8 * c, chB = J * kT16 + 8 * c;
+    voffA[i] = (chA < d) ? (int)(R * row_bytes + chA * 2) : 0x7ffffff0;
+    voffB[i] = (chB < d) ? (int)(R * row_bytes + chB * 2) : 0x7ffffff0;
+  }
+  auto issue = [&](int64_t kk) {
+    const int slot = (int)((kk - ks0) & 1);
+    const int64_t t0 = kk * kK16;
+    const uint64_t base = reinterpret_cast<uint64_t>(X) + (uint64_t)t0 * row_bytes;
+    const int64_t rows = min<int64_t>(kK16, n_tokens - t0);
+    i32x4_t rsrc;
+    rsrc[0] = (int)(uint32_t)(base & 0xffffffffu);
+    rsrc[1] = (int)(uint32_t)(base >> 32);        // stride 0
+    rsrc[2] = (int)(rows * row_bytes);            // bytes in range; beyond reads as 0
+    rsrc[3] = 0x00020000;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) dsum[e] = 0.0;
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(&sA[buf][(crow + 8 * i) * kP16 + ccol]) = ra[i];
-      if (!diag) *reinterpret_cast<uint4*>(&sB[buf][(crow + 8 * i) * kP16 + ccol]) = rb[i];
-    }
-    if (diag) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t wd[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double v = (double)elem16<T>(wd[e >> 1], e & 1);
-          dsum[e] = fma(v, v, dsum[e]);
-        }
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int R0 = 8 * i + 2 * wave;
+      dma16(rsrc, &sA[slot][R0 * kRow16], voffA[i]);
+      if (!diag) dma16(rsrc, &sB[slot][R0 * kRow16], voffB[i]);
     }
   };
 
@@ -160,30 +235,58 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  double dsum0 = 0.0, dsum1 = 0.0;     // diagonal tiles: channels 2*(tid%128) + {0,1}
 
   if (ks0 < ks1) {
-    gload(ks0);
-    lstore(0);
-    __syncthreads();
+    issue(ks0);
     for (int64_t kk = ks0; kk < ks1; ++kk) {
-      const int buf = (int)((kk - ks0) & 1);
-      if (kk + 1 < ks1) gload(kk + 1);
-      const T* stA = sA[buf];
-      const T* stB = diag ? sA[buf] : sB[buf];
+      // stage kk's copies have landed, for every wave; every wave is done with
+      // the other slot (stage kk-1), which now receives stage kk+1
+      wait_vm(0);
+      lds_barrier();
+      if (kk + 1 < ks1) issue(kk + 1);
+      const int slot = (int)((kk - ks0) & 1);
+      const T* stA = sA[slot];
+      const T* stB = diag ? sA[slot] : sB[slot];
+      // operands double-buffered across the 16-token k-slices: the next
+      // slice's 16 transposing reads are issued one per MFMA of this slice
+      typename Op16<T>::v8 a[2][4], b[2][4];
+      auto load_ops = [&](int ks, int bufi) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        typename Op16<T>::v8 a[4], b[4];
+        for (int i = 0; i < 4; ++i) a[bufi][i] = operand16<T>(stA, ks, wm * 128 + i * 32, lane);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = operand16<T>(stA, ks, wm * 128 + i * 32, lane);
+        for (int j = 0; j < 4; ++j) b[bufi][j] = operand16<T>(stB, ks, wn * 128 + j * 32, lane);
+      };
+      constexpr int NKS = kK16 / 16;
+      load_ops(0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = operand16<T>(stB, ks, wn * 128 + j * 32, lane);
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) load_ops(ks + 1, (ks + 1) & 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = Op16<T>::mfma(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < 4; ++j) acc[i][j] = Op16<T>::mfma(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
       }
-      if (kk + 1 < ks1) lstore(buf ^ 1);
-      __syncthreads();
+      // scheduling groups (0x100 LDS read, 0x008 MFMA): slice 0's reads first,
+      // then each later slice's reads interleaved with the previous slice's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+      for (int n = 0; n < 16 * (NKS - 1); ++n) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      if (diag) {
+        const int cp = 2 * (tid & 127), r0 = (kK16 / 2) * (tid >> 7);
+#pragma unroll
+        for (int r = 0; r < kK16 / 2; ++r) {
+          const uint32_t pr = *reinterpret_cast<const uint32_t*>(stA + swz16(r0 + r, cp));
+          const double v0 = (double)Op16<T>::to_f32((uint16_t)(pr & 0xffffu));
+          const double v1 = (double)Op16<T>::to_f32((uint16_t)(pr >> 16));
+          dsum0 = fma(v0, v0, dsum0);
+          dsum1 = fma(v1, v1, dsum1);
+        }
+      }
     }
   }
 
@@ -196,15 +299,12 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
       for (int r = 0; r < 16; ++r) out[((i * 4 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
 
   if (diag) {
-    // threads with equal (tid & 31) hold the same 8 channels: add their
-    // partial sums in a fixed order
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sD[crow][ccol + e] = dsum[e];
+    const int cp = 2 * (tid & 127), h = tid >> 7;
+    sD[h][cp] = dsum0;
+    sD[h][cp + 1] = dsum1;
     __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) t += sD[r][tid];
-    pdiag[((size_t)s * nt + I) * kT16 + tid] = t;
+    pdiag[((size_t)s * nt + I) * kT16 + tid] = sD[0][tid] + sD[1][tid];
+  }
   }
 }
 
@@ -223,11 +323,9 @@ __global__ __launch_bounds__(256, 2) void syrk32_kernel(const float* __restrict_
   __shared__ __attribute__((aligned(16))) float sA[2][kK32 * kP32];
   __shared__ __attribute__((aligned(16))) float sB[2][kK32 * kP32];
   __shared__ double sD[8][kT32 + 1];
-  const int w = blockIdx.x;
-  const int s = w / ntiles;
-  const int q = w - s * ntiles;
-  int I, J;
-  tri_tile(q, I, J);
+  int s, I, J;
+  if (!xcd_item(blockIdx.x, nt, ntiles, splits, s, I, J)) return;
+  const int w = s * ntiles + tri_index(I, J);     // partial slot
   const bool diag = (I == J);
   const int64_t ks0 = nk * s / splits, ks1 = nk * (s + 1) / splits;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -437,7 +535,7 @@ static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32) {
   int best_s = 1;
   const int smax = (int)std::max<int64_t>(1, std::min<int64_t>(64, p.nk / 16));
   for (int s = 1; s <= smax; ++s) {
-    const double items = (double)p.ntiles * s;
+    const double items = (double)kXCD * ((p.ntiles + kXCD - 1) / kXCD) * s;
     const double rounds = std::ceil(items / 256.0);
     const double t = rounds * ((double)p.nk / s) * t_stage + items * bytes_tile / 6.0e12;
     if (t < best * 0.999) { best = t; best_s = s; }
@@ -472,12 +570,15 @@ extern "C" int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, g
     return GPTQ_ERR_WORKSPACE;
   float* partial = static_cast<float*>(ws);
   double* pdiag = reinterpret_cast<double*>(static_cast<char*>(ws) + p.off_diag);
-  const unsigned items = (unsigned)(p.ntiles * p.splits);
+  const unsigned items = (unsigned)(kXCD * ((p.ntiles + kXCD - 1) / kXCD) * p.splits);
+  // 16-bit path: one resident workgroup per CU (256 CUs), persistent over items
+  const unsigned pgrid = std::min<unsigned>(256u, items);
+  const unsigned pg = (pgrid + kXCD - 1) / kXCD * kXCD;
   if (x_dtype == GPTQ_BF16) {
-    syrk16_kernel<__bf16><<<items, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in,
+    syrk16_kernel<__bf16><<<pg, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in,
                                                  p.nt, p.ntiles, p.splits, p.nk, partial, pdiag);
   } else if (x_dtype == GPTQ_F16) {
-    syrk16_kernel<_Float16><<<items, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in,
+    syrk16_kernel<_Float16><<<pg, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in,
                                                    p.nt, p.ntiles, p.splits, p.nk, partial, pdiag);
   } else {
     syrk32_kernel<<<items, 256, 0, s>>>(static_cast<const float*>(X), n_tokens, d_in, p.nt, p.ntiles,
