@@ -38,7 +38,32 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows in the oracle's column-loop sample (result scaled to all rows)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hessian_c2_traffic.json"))
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+HESSIAN_SOURCE = os.path.join(ROOT, "post_weight_quantization_29_amd", "csrc", "hessian.hip")
+
+
+def source_digest(path=HESSIAN_SOURCE):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def calibrate_copy(mib):
+    """One copy kernel of a known size: it reads and writes mib MiB once each."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4}),
+          flush=True)
 
 
 def log(*a):
@@ -95,6 +120,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import numpy as np
     import torch
@@ -187,7 +216,8 @@ def main():
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
-            if tj.get("workload") == args.workload:
+            # counters taken on another kernel build do not describe this one
+            if tj.get("workload") == args.workload and tj.get("source_sha256") == source_digest():
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None

@@ -70,12 +70,14 @@ GPTQ_DEV int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
 
 // ---------------------------------------------------------------------------
 // 16-bit inputs: bf16 / fp16, v_mfma_f32_32x32x16_{bf16,f16}
-// Workgroup tile 256x256, 4 waves (2x2) of 128x128, 32 tokens per stage.
+// Workgroup tile 256x256, 4 waves (2x2) of 128x128, 64 tokens per stage.
 //
 // Stages are copied HBM -> LDS by buffer_load ... lds (16 bytes per lane, the
 // 64 lanes of one instruction fill 1 KB of LDS in lane order) into two slots:
 // stage kk+1 streams in while stage kk is multiplied, with no staging
-// registers.  A stage row (one token, 256 channels) is 512 bytes, unpadded;
+// registers.  The 16 copies a wave issues per stage are interleaved one per
+// MFMA with the first k-slice, so the MFMA pipe keeps running while the
+// address unit takes them.  A stage row (one token, 256 channels) is 512 bytes, unpadded;
 // its 16-byte chunk c sits at slot c ^ 4*(row % 4), which keeps the
 // transposing operand reads free of bank conflicts (the DMA side applies the
 // swizzle by permuting the lanes' source addresses).  Tokens past the end and
@@ -85,6 +87,7 @@ constexpr int kT16 = 256;          // tile edge (channels)
 constexpr int kK16 = 64;           // tokens per stage (4 k-slices of 16)
 constexpr int kRow16 = kT16;       // LDS row pitch in elements (512 bytes)
 constexpr int kStage16 = kK16 * kRow16;
+constexpr int kDiagRows = 8;       // x^2 rows per thread per stage issued up front
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -114,8 +117,8 @@ template <typename T> struct Op16;
 template <> struct Op16<__bf16> {
   typedef bf16x8_t v8;
   typedef bf16x4_t v4;
-  static GPTQ_DEV v4 tr(const __bf16* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4*)(LDS_AS void*)p);
+  static GPTQ_DEV v4 tr(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4*)(uintptr_t)addr);
   }
   static GPTQ_DEV f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -126,8 +129,8 @@ template <> struct Op16<_Float16> {
   typedef f16x8_t v8;
   typedef f16x4_t v4;
   typedef __fp16 raw4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
-  static GPTQ_DEV v4 tr(const _Float16* p) {
-    raw4 r = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS raw4*)(LDS_AS void*)p);
+  static GPTQ_DEV v4 tr(uint32_t addr) {
+    raw4 r = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS raw4*)(uintptr_t)addr);
     return __builtin_bit_cast(v4, r);
   }
   static GPTQ_DEV f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
@@ -139,49 +142,68 @@ template <> struct Op16<_Float16> {
 // element offset of (token row, channel) inside a stage
 GPTQ_DEV int swz16(int row, int ch) { return row * kRow16 + ((((ch >> 3) ^ (4 * (row & 3)))) << 3) + (ch & 7); }
 
-// K-contiguous operand for a 32-channel block starting at channel cbase, k-slice
-// ks (16 tokens).  The transposing read gives lane j of each 16-lane group g the
-// element (4e + (j%16)/4, j%4) of the group's 16x4 block of 64-bit loads;
-// pointing lane 16g+4a+b at token (8*(g/2) + 4r + a) and channels
-// (16*(g%2) + 4b .. +3) hands lane l channel cbase + l%32 at tokens
-// 8*(l/32) + 4r + 0..3, i.e. MFMA k-slot order.
+// Transposing read at an LDS byte address (the constant part of the address
+// folds into the instruction's offset field).
 template <typename T>
-GPTQ_DEV typename Op16<T>::v8 operand16(const T* stage, int ks, int cbase, int lane) {
+GPTQ_DEV typename Op16<T>::v4 tr_at(uint32_t addr) {
+  return Op16<T>::tr(addr);
+}
+
+// Per-lane byte offset, inside a stage, of the first of a lane's two
+// transposing reads for the 32-channel block starting at cbase, k-slice 0.
+// The read gives lane j of each 16-lane group g the element (4e + (j%16)/4,
+// j%4) of the group's 16x4 block of 64-bit loads; pointing lane 16g+4a+b at
+// token 8*(g/2) + a (+4 for the second read) and channels cbase + 16*(g%2) +
+// 4b .. +3 hands lane l channel cbase + l%32 at tokens 8*(l/32) + 0..7, i.e.
+// MFMA k-slot order.  Token rows of one read differ by multiples of 4, so the
+// swizzle term 4*(row%4) = 4a is fixed per lane and k-slice s / second read
+// only add 16*s*512 and 4*512 bytes.
+GPTQ_DEV uint32_t lane_op_offset(int cbase, int lane) {
   const int g = lane >> 4, a = (lane >> 2) & 3, b = lane & 3;
-  const int tok = ks * 16 + 8 * (g >> 1) + a;
+  const int tok = 8 * (g >> 1) + a;
   const int ch = cbase + 16 * (g & 1) + 4 * b;
-  typename Op16<T>::v4 lo = Op16<T>::tr(stage + swz16(tok, ch));
-  typename Op16<T>::v4 hi = Op16<T>::tr(stage + swz16(tok + 4, ch));
-  typename Op16<T>::v8 v;
-  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
-  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-  return v;
+  return 2u * (uint32_t)swz16(tok, ch);
 }
 
-GPTQ_DEV void wait_vm(int n) {
-  // s_waitcnt with vmcnt = n (0, 4 or 8 here), expcnt and lgkmcnt left open
-  if (n >= 8) __builtin_amdgcn_s_waitcnt((8 & 0xF) | (0x7 << 4) | (0xF << 8));
-  else if (n >= 4) __builtin_amdgcn_s_waitcnt((4 & 0xF) | (0x7 << 4) | (0xF << 8));
-  else __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-}
+// s_waitcnt with vmcnt = 0 (expcnt and lgkmcnt left open)
+GPTQ_DEV void wait_vm0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); }
 
-// Diagonal tiles also sum x^2 per channel in fp64 (the squares of 16-bit
-// values are exact), one partial row per (split, tile row): these sums are the
-// keys of the descending-diagonal column order, so the order does not hinge on
-// fp32 accumulation rounding.
+// Every tile also sums x^2 in fp64 for a slice of the channels of its two
+// panels (the squares of 16-bit values are exact): tile (I, J) takes slice J
+// of panel I and, off the diagonal, slice I of panel J, where slice q of a
+// panel is channels [256q/nt, 256(q+1)/nt).  Each (panel, slice) pair occurs
+// in exactly one tile, so every channel is summed once per split, and every
+// tile carries the same small share of this work.  These sums are the keys of
+// the descending-diagonal column order, so that order does not hinge on fp32
+// accumulation rounding.
 //
 // Partial layout (floats): [work item][wave 4][block 16 = mb*4+nb][reg 16][lane 64]
 template <typename T>
 __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X, int64_t n_tokens,
                                                          int d, int nt, int ntiles, int splits,
-                                                         int64_t nk, float* __restrict__ partial,
+                                                         int nk, float* __restrict__ partial,
                                                          double* __restrict__ pdiag) {
   __shared__ __attribute__((aligned(16))) T sA[2][kStage16];
   __shared__ __attribute__((aligned(16))) T sB[2][kStage16];
-  __shared__ double sD[2][kT16];
+  __shared__ double sD[kT16];
+  constexpr uint32_t kSlotBytes = kStage16 * 2;    // 32 KB
+  constexpr uint32_t kSliceBytes = 16 * kRow16 * 2; // 16 token rows
+  constexpr int NI = kK16 / 8;                     // copies per panel per lane per stage
+  constexpr int NKS = kK16 / 16;                   // k-slices per stage
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t row_bytes = (uint32_t)d * 2u;
+  const uint32_t ldsA = (uint32_t)(uintptr_t)(LDS_AS const void*)&sA[0][0];
+  const uint32_t ldsB = (uint32_t)(uintptr_t)(LDS_AS const void*)&sB[0][0];
+
+  uint32_t offA[4], offB[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    offA[i] = lane_op_offset(wm * 128 + i * 32, lane);
+    offB[i] = lane_op_offset(wn * 128 + i * 32, lane);
+  }
 
   // Persistent: workgroup (x = XCD, c) runs items c, c + nper, c + 2*nper, ... of
   // XCD x's list, so the workgroups of an XCD move through the list in rounds
@@ -191,42 +213,68 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   for (int kidx = c; kidx < per_xcd; kidx += nper) {
   int s, I, J;
   if (!xcd_item(kidx * kXCD + x, nt, ntiles, splits, s, I, J)) continue;
+  s = __builtin_amdgcn_readfirstlane(s);
+  I = __builtin_amdgcn_readfirstlane(I);
+  J = __builtin_amdgcn_readfirstlane(J);
   const int w = s * ntiles + tri_index(I, J);     // partial slot
-  const bool diag = (I == J);
-  const int64_t ks0 = nk * s / splits, ks1 = nk * (s + 1) / splits;
-  lds_barrier();                                   // the previous item is done with LDS
+  const int ks0 = __builtin_amdgcn_readfirstlane((int)((int64_t)nk * s / splits));
+  const int ks1 = __builtin_amdgcn_readfirstlane((int)((int64_t)nk * (s + 1) / splits));
 
-  // DMA assignment: instruction i of wave v fills stage rows 8i+2v (lanes 0-31)
+  // copies of the previous item (and its stores) are complete and every wave
+  // is done with its LDS
+  wait_vm0();
+  lds_barrier();
+
+  // DMA assignment: copy i of wave v fills stage rows R = 8i+2v (lanes 0-31)
   // and 8i+2v+1 (lanes 32-63); lane slot L%32 of row R takes chunk
-  // (L%32) ^ 4(R%4), i.e. channels 8*that .. +7 of the panel.
-  constexpr int NI = kK16 / 8;                     // copies per panel per lane
+  // (L%32) ^ 4(R%4), i.e. channels 8*that .. +7 of the panel.  R%4 does not
+  // depend on i.
   int voffA[NI], voffB[NI];
-  const uint32_t row_bytes = (uint32_t)d * 2u;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int R = 8 * i + 2 * wave + (lane >> 5);
-    const int c = (lane & 31) ^ (4 * (R & 3));
-    const int chA = I * kT16 + 8 * c, chB = J * kT16 + 8 * c;
-    voffA[i] = (chA < d) ? (int)(R * row_bytes + chA * 2) : 0x7ffffff0;
-    voffB[i] = (chB < d) ? (int)(R * row_bytes + chB * 2) : 0x7ffffff0;
-  }
-  auto issue = [&](int64_t kk) {
-    const int slot = (int)((kk - ks0) & 1);
-    const int64_t t0 = kk * kK16;
-    const uint64_t base = reinterpret_cast<uint64_t>(X) + (uint64_t)t0 * row_bytes;
-    const int64_t rows = min<int64_t>(kK16, n_tokens - t0);
-    i32x4_t rsrc;
-    rsrc[0] = (int)(uint32_t)(base & 0xffffffffu);
-    rsrc[1] = (int)(uint32_t)(base >> 32);        // stride 0
-    rsrc[2] = (int)(rows * row_bytes);            // bytes in range; beyond reads as 0
-    rsrc[3] = 0x00020000;
+  {
+    const int R = 2 * wave + (lane >> 5);
+    const int cc = (lane & 31) ^ (4 * (R & 3));
+    const int chA = I * kT16 + 8 * cc, chB = J * kT16 + 8 * cc;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int R0 = 8 * i + 2 * wave;
-      dma16(rsrc, &sA[slot][R0 * kRow16], voffA[i]);
-      if (!diag) dma16(rsrc, &sB[slot][R0 * kRow16], voffB[i]);
+      voffA[i] = (chA < d) ? (int)((uint32_t)(R + 8 * i) * row_bytes + chA * 2) : 0x7ffffff0;
+      voffB[i] = (chB < d) ? (int)((uint32_t)(R + 8 * i) * row_bytes + chB * 2) : 0x7ffffff0;
     }
+  }
+  // buffer descriptor of stage kk (rows past the end, or kk outside this
+  // split, read as zero)
+  auto stage_rsrc = [&](int kk) {
+    const int64_t t0 = (int64_t)kk * kK16;
+    const int64_t rows = (kk < ks1) ? min<int64_t>(kK16, n_tokens - t0) : 0;
+    const uint64_t base = reinterpret_cast<uint64_t>(X) + (uint64_t)t0 * row_bytes;
+    i32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));   // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)(rows * row_bytes));
+    r[3] = 0x00020000;
+    return r;
   };
+  // copy n (0..2*NI-1) of stage kk's DMA into slot `slot`
+  auto dma = [&](const i32x4_t& r, int slot, int n) {
+    const int i = n % NI;
+    const uint32_t dst = ((n < NI) ? ldsA : ldsB) + (uint32_t)slot * kSlotBytes + 4096u * i + 1024u * wave;
+    const int voff = (n < NI) ? voffA[i] : voffB[i];
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(r)
+                 : "memory", "m0");
+  };
+
+  // fp64 x^2 slices: C channels over P row phases
+  const int lo0 = (J * kT16) / nt, hi0 = ((J + 1) * kT16) / nt;
+  const int lo1 = (I * kT16) / nt, hi1 = ((I + 1) * kT16) / nt;
+  const int n0 = hi0 - lo0, n1 = (I != J) ? hi1 - lo1 : 0;
+  const int C = n0 + n1, P = kT16 / C;
+  const int dq = tid % C, dph = tid / C;
+  const bool dact = dph < P;
+  const bool dB = dq >= n0;                        // slice of panel J (in sB)
+  const int dch = dB ? lo1 + (dq - n0) : lo0 + dq;
+  const int dM = dact ? (kK16 - dph + P - 1) / P : 0;   // rows dph, dph+P, ... < kK16
+  double dsum = 0.0;
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -235,57 +283,71 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  double dsum0 = 0.0, dsum1 = 0.0;     // diagonal tiles: channels 2*(tid%128) + {0,1}
 
   if (ks0 < ks1) {
-    issue(ks0);
-    for (int64_t kk = ks0; kk < ks1; ++kk) {
-      // stage kk's copies have landed, for every wave; every wave is done with
-      // the other slot (stage kk-1), which now receives stage kk+1
-      wait_vm(0);
+    {
+      const i32x4_t r0 = stage_rsrc(ks0);
+#pragma unroll
+      for (int n = 0; n < 2 * NI; ++n) dma(r0, 0, n);
+    }
+    for (int kk = ks0; kk < ks1; ++kk) {
+      // this wave's copies of stage kk have landed; after the barrier so have
+      // every wave's, and every wave is done with the other slot (stage kk-1),
+      // which now receives stage kk+1
+      wait_vm0();
       lds_barrier();
-      if (kk + 1 < ks1) issue(kk + 1);
-      const int slot = (int)((kk - ks0) & 1);
-      const T* stA = sA[slot];
-      const T* stB = diag ? sA[slot] : sB[slot];
-      // operands double-buffered across the 16-token k-slices: the next
-      // slice's 16 transposing reads are issued one per MFMA of this slice
-      typename Op16<T>::v8 a[2][4], b[2][4];
-      auto load_ops = [&](int ks, int bufi) {
+      const int slot = (kk - ks0) & 1;
+      const uint32_t bA = ldsA + (uint32_t)slot * kSlotBytes, bB = ldsB + (uint32_t)slot * kSlotBytes;
+      const i32x4_t rn = stage_rsrc(kk + 1);
+      typename Op16<T>::v4 op[2][8][2];           // [buffer][a0..a3, b0..b3][lo, hi]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[bufi][i] = operand16<T>(stA, ks, wm * 128 + i * 32, lane);
+      for (int f = 0; f < 8; ++f)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[bufi][j] = operand16<T>(stB, ks, wn * 128 + j * 32, lane);
-      };
-      constexpr int NKS = kK16 / 16;
-      load_ops(0, 0);
+        for (int h = 0; h < 2; ++h)
+          op[0][f][h] = tr_at<T>((f < 4 ? bA + offA[f] : bB + offB[f - 4]) + h * 2048u);
+      // this thread's x^2 rows of the stage (up to kDiagRows; the rest loop below)
+      const T* dst_ = dB ? sB[slot] : sA[slot];
+      uint16_t dv[kDiagRows];
+#pragma unroll
+      for (int u = 0; u < kDiagRows; ++u) {
+        const int r = (u < dM) ? dph + P * u : 0;
+        dv[u] = *reinterpret_cast<const uint16_t*>(dst_ + swz16(r, dch));
+      }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        if (ks + 1 < NKS) load_ops(ks + 1, (ks + 1) & 1);
+        const int cur = ks & 1, nxt = cur ^ 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int n = 0; n < 16; ++n) {
+          const int i = n >> 2, j = n & 3;
+          typename Op16<T>::v8 av, bv;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = Op16<T>::mfma(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
-      }
-      // scheduling groups (0x100 LDS read, 0x008 MFMA): slice 0's reads first,
-      // then each later slice's reads interleaved with the previous slice's MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-      for (int n = 0; n < 16 * (NKS - 1); ++n) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-      if (diag) {
-        const int cp = 2 * (tid & 127), r0 = (kK16 / 2) * (tid >> 7);
-#pragma unroll
-        for (int r = 0; r < kK16 / 2; ++r) {
-          const uint32_t pr = *reinterpret_cast<const uint32_t*>(stA + swz16(r0 + r, cp));
-          const double v0 = (double)Op16<T>::to_f32((uint16_t)(pr & 0xffffu));
-          const double v1 = (double)Op16<T>::to_f32((uint16_t)(pr >> 16));
-          dsum0 = fma(v0, v0, dsum0);
-          dsum1 = fma(v1, v1, dsum1);
+          for (int e = 0; e < 4; ++e) {
+            av[e] = op[cur][i][0][e]; av[e + 4] = op[cur][i][1][e];
+            bv[e] = op[cur][4 + j][0][e]; bv[e + 4] = op[cur][4 + j][1][e];
+          }
+          acc[i][j] = Op16<T>::mfma(av, bv, acc[i][j]);
+          if (ks + 1 < NKS) {
+            const int f = n >> 1, h = n & 1;
+            op[nxt][f][h] = tr_at<T>((f < 4 ? bA + offA[f] : bB + offB[f - 4]) +
+                                     (uint32_t)(ks + 1) * kSliceBytes + h * 2048u);
+          }
+          if (ks == 0) dma(rn, slot ^ 1, n);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        if (ks == 0) {
+#pragma unroll
+          for (int u = 0; u < kDiagRows; ++u) {
+            const double v = (u < dM) ? (double)Op16<T>::to_f32(dv[u]) : 0.0;
+            dsum = fma(v, v, dsum);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // slices wider than kDiagRows * P rows per stage (only when nt < 8)
+      for (int u = kDiagRows; u < dM; ++u) {
+        const uint16_t hv = *reinterpret_cast<const uint16_t*>(dst_ + swz16(dph + P * u, dch));
+        const double v = (double)Op16<T>::to_f32(hv);
+        dsum = fma(v, v, dsum);
       }
     }
   }
@@ -298,12 +360,13 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
 #pragma unroll
       for (int r = 0; r < 16; ++r) out[((i * 4 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
 
-  if (diag) {
-    const int cp = 2 * (tid & 127), h = tid >> 7;
-    sD[h][cp] = dsum0;
-    sD[h][cp + 1] = dsum1;
-    __syncthreads();
-    pdiag[((size_t)s * nt + I) * kT16 + tid] = sD[0][tid] + sD[1][tid];
+  sD[tid] = dsum;
+  __syncthreads();
+  if (tid < C) {
+    double t = 0.0;
+    for (int ph = 0; ph < P; ++ph) t += sD[ph * C + tid];
+    const int pan = dB ? J : I;
+    pdiag[((size_t)s * nt + pan) * kT16 + dch] = t;
   }
   }
 }
@@ -576,10 +639,10 @@ extern "C" int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, g
   const unsigned pg = (pgrid + kXCD - 1) / kXCD * kXCD;
   if (x_dtype == GPTQ_BF16) {
     syrk16_kernel<__bf16><<<pg, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in,
-                                                 p.nt, p.ntiles, p.splits, p.nk, partial, pdiag);
+                                                 p.nt, p.ntiles, p.splits, (int)p.nk, partial, pdiag);
   } else if (x_dtype == GPTQ_F16) {
     syrk16_kernel<_Float16><<<pg, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in,
-                                                   p.nt, p.ntiles, p.splits, p.nk, partial, pdiag);
+                                                   p.nt, p.ntiles, p.splits, (int)p.nk, partial, pdiag);
   } else {
     syrk32_kernel<<<items, 256, 0, s>>>(static_cast<const float*>(X), n_tokens, d_in, p.nt, p.ntiles,
                                         p.splits, p.nk, partial, pdiag);

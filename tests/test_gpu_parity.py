@@ -26,7 +26,7 @@ def _gpu():
 
 @pytest.mark.parametrize("x_dtype,d,n", [
     ("f32", 256, 2048), ("f32", 200, 777), ("bf16", 512, 4096), ("bf16", 264, 1000),
-    ("f16", 520, 3000), ("bf16", 1024, 20000),
+    ("f16", 520, 3000), ("bf16", 1024, 20000), ("bf16", 1240, 5000), ("f16", 1704, 3333),
 ])
 def test_hessian_parity(x_dtype, d, n):
     say(f"[hessian] dtype={x_dtype} d={d} n={n}")
@@ -36,7 +36,12 @@ def test_hessian_parity(x_dtype, d, n):
     Hr = o.hessian([X64], d)
     # two calls on a split of the tokens: H is accumulated
     k = n // 3
-    H = gpu_hessian([c.X[:k], c.X[k:]], x_dtype, d).cpu().numpy().astype(np.float64)
+    Hg, hd = gpu_hessian([c.X[:k], c.X[k:]], x_dtype, d, with_diag=True)
+    H = Hg.cpu().numpy().astype(np.float64)
+    # the fp64 diagonal sums squares of exactly representable inputs: it matches
+    # the float64 oracle up to summation order
+    hd = hd.cpu().numpy()
+    assert np.max(np.abs(hd - np.diag(Hr)) / np.diag(Hr)) <= 1e-12
     assert np.array_equal(H, H.T), "H must be exactly symmetric"
     dg = np.diag(Hr)
     assert np.max(np.abs(np.diag(H) - dg) / dg) <= 1e-4
