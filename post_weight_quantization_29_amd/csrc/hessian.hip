@@ -70,12 +70,12 @@ GPTQ_DEV int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
 
 // ---------------------------------------------------------------------------
 // 16-bit inputs: bf16 / fp16, v_mfma_f32_32x32x16_{bf16,f16}
-// Workgroup tile 256x256, 4 waves (2x2) of 128x128, 64 tokens per stage.
+// Workgroup tile 256x256, 4 waves (2x2) of 128x128, 48 tokens per stage.
 //
 // Stages are copied HBM -> LDS by buffer_load ... lds (16 bytes per lane, the
-// 64 lanes of one instruction fill 1 KB of LDS in lane order) into two slots:
-// stage kk+1 streams in while stage kk is multiplied, with no staging
-// registers.  The 16 copies a wave issues per stage are interleaved one per
+// 64 lanes of one instruction fill 1 KB of LDS in lane order) into a ring of
+// three slots: stage kk+2 streams in while stage kk is multiplied, so a copy
+// has about two stages to land, with no staging registers.  The 16 copies a wave issues per stage are interleaved one per
 // MFMA with the first k-slice, so the MFMA pipe keeps running while the
 // address unit takes them.  A stage row (one token, 256 channels) is 512 bytes, unpadded;
 // its 16-byte chunk c sits at slot c ^ 4*(row % 4), which keeps the
@@ -84,7 +84,8 @@ GPTQ_DEV int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
 // channels past d read as zero through the buffer descriptor's range.
 // ---------------------------------------------------------------------------
 constexpr int kT16 = 256;          // tile edge (channels)
-constexpr int kK16 = 64;           // tokens per stage (4 k-slices of 16)
+constexpr int kK16 = 32;           // tokens per stage (2 k-slices of 16)
+constexpr int kSlots16 = 4;        // LDS ring slots
 constexpr int kRow16 = kT16;       // LDS row pitch in elements (512 bytes)
 constexpr int kStage16 = kK16 * kRow16;
 constexpr int kDiagRows = 8;       // x^2 rows per thread per stage issued up front
@@ -165,8 +166,13 @@ GPTQ_DEV uint32_t lane_op_offset(int cbase, int lane) {
   return 2u * (uint32_t)swz16(tok, ch);
 }
 
-// s_waitcnt with vmcnt = 0 (expcnt and lgkmcnt left open)
-GPTQ_DEV void wait_vm0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); }
+// s_waitcnt with vmcnt = N (expcnt and lgkmcnt left open)
+template <int N>
+GPTQ_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+GPTQ_DEV void wait_vm0() { wait_vm<0>(); }
 
 // Every tile also sums x^2 in fp64 for a slice of the channels of its two
 // panels (the squares of 16-bit values are exact): tile (I, J) takes slice J
@@ -183,10 +189,10 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
                                                          int d, int nt, int ntiles, int splits,
                                                          int nk, float* __restrict__ partial,
                                                          double* __restrict__ pdiag) {
-  __shared__ __attribute__((aligned(16))) T sA[2][kStage16];
-  __shared__ __attribute__((aligned(16))) T sB[2][kStage16];
+  __shared__ __attribute__((aligned(16))) T sA[kSlots16][kStage16];
+  __shared__ __attribute__((aligned(16))) T sB[kSlots16][kStage16];
   __shared__ double sD[kT16];
-  constexpr uint32_t kSlotBytes = kStage16 * 2;    // 32 KB
+  constexpr uint32_t kSlotBytes = kStage16 * 2;    // 24 KB
   constexpr uint32_t kSliceBytes = 16 * kRow16 * 2; // 16 token rows
   constexpr int NI = kK16 / 8;                     // copies per panel per lane per stage
   constexpr int NKS = kK16 / 16;                   // k-slices per stage
@@ -285,26 +291,40 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   if (ks0 < ks1) {
-    {
-      const i32x4_t r0 = stage_rsrc(ks0);
+    // Ring of kSlots16 stage slots.  The sync point of stage k sits before
+    // the last k-slice of stage k-1: there every wave has waited for its own
+    // copies of stage k (so after the barrier stage k is complete for all) and
+    // has finished the earlier slices of stage k-1 (so stage k-2's slot is
+    // free and receives stage k + kSlots16 - 2).  The last slice of a stage
+    // then overlaps its MFMAs with the reads of the next stage's first slice
+    // and with the next copies.
+    constexpr int kInFlight = kSlots16 - 3;        // later stages still in flight at a sync point
+    static_assert(kSlots16 >= 3 && NKS % 2 == 0, "ring layout");
 #pragma unroll
-      for (int n = 0; n < 2 * NI; ++n) dma(r0, 0, n);
+    for (int a = 0; a <= kSlots16 - 3; ++a) {
+      const i32x4_t r0 = stage_rsrc(ks0 + a);
+#pragma unroll
+      for (int n = 0; n < 2 * NI; ++n) dma(r0, a, n);
     }
+    wait_vm<kInFlight * 2 * NI>();
+    lds_barrier();
+    {
+      const i32x4_t r0 = stage_rsrc(ks0 + kSlots16 - 2);
+#pragma unroll
+      for (int n = 0; n < 2 * NI; ++n) dma(r0, kSlots16 - 2, n);
+    }
+    typename Op16<T>::v4 op[2][8][2];             // [buffer][a0..a3, b0..b3][lo, hi]
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        op[0][f][h] = tr_at<T>((f < 4 ? ldsA + offA[f] : ldsB + offB[f - 4]) + h * 2048u);
+    int slot = 0;                                  // (kk - ks0) % kSlots16
     for (int kk = ks0; kk < ks1; ++kk) {
-      // this wave's copies of stage kk have landed; after the barrier so have
-      // every wave's, and every wave is done with the other slot (stage kk-1),
-      // which now receives stage kk+1
-      wait_vm0();
-      lds_barrier();
-      const int slot = (kk - ks0) & 1;
+      const int nslot = (slot + 1 == kSlots16) ? 0 : slot + 1;
+      const int dslot = (slot == 0) ? kSlots16 - 1 : slot - 1;
       const uint32_t bA = ldsA + (uint32_t)slot * kSlotBytes, bB = ldsB + (uint32_t)slot * kSlotBytes;
-      const i32x4_t rn = stage_rsrc(kk + 1);
-      typename Op16<T>::v4 op[2][8][2];           // [buffer][a0..a3, b0..b3][lo, hi]
-#pragma unroll
-      for (int f = 0; f < 8; ++f)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          op[0][f][h] = tr_at<T>((f < 4 ? bA + offA[f] : bB + offB[f - 4]) + h * 2048u);
+      const uint32_t nA = ldsA + (uint32_t)nslot * kSlotBytes, nB = ldsB + (uint32_t)nslot * kSlotBytes;
       // this thread's x^2 rows of the stage (up to kDiagRows; the rest loop below)
       const T* dst_ = dB ? sB[slot] : sA[slot];
       uint16_t dv[kDiagRows];
@@ -313,9 +333,16 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
         const int r = (u < dM) ? dph + P * u : 0;
         dv[u] = *reinterpret_cast<const uint16_t*>(dst_ + swz16(r, dch));
       }
+      i32x4_t rn;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int cur = ks & 1, nxt = cur ^ 1;
+        const bool last = (ks == NKS - 1);
+        if (last) {
+          wait_vm<kInFlight * 2 * NI>();
+          lds_barrier();
+          rn = stage_rsrc(kk + kSlots16 - 1);
+        }
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
           const int i = n >> 2, j = n & 3;
@@ -326,12 +353,13 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
             bv[e] = op[cur][4 + j][0][e]; bv[e + 4] = op[cur][4 + j][1][e];
           }
           acc[i][j] = Op16<T>::mfma(av, bv, acc[i][j]);
-          if (ks + 1 < NKS) {
-            const int f = n >> 1, h = n & 1;
+          const int f = n >> 1, h = n & 1;
+          if (!last)
             op[nxt][f][h] = tr_at<T>((f < 4 ? bA + offA[f] : bB + offB[f - 4]) +
                                      (uint32_t)(ks + 1) * kSliceBytes + h * 2048u);
-          }
-          if (ks == 0) dma(rn, slot ^ 1, n);
+          else
+            op[nxt][f][h] = tr_at<T>((f < 4 ? nA + offA[f] : nB + offB[f - 4]) + h * 2048u);
+          if (last && n < 2 * NI) dma(rn, dslot, n);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (ks == 0) {
@@ -343,12 +371,13 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // slices wider than kDiagRows * P rows per stage (only when nt < 8)
+      // slices wider than kDiagRows * P rows per stage (only when nt is small)
       for (int u = kDiagRows; u < dM; ++u) {
         const uint16_t hv = *reinterpret_cast<const uint16_t*>(dst_ + swz16(dph + P * u, dch));
         const double v = (double)Op16<T>::to_f32(hv);
         dsum = fma(v, v, dsum);
       }
+      slot = nslot;
     }
   }
 
