@@ -8,12 +8,13 @@
 // 与 AWQ 原理详解 + Python 实战教程", section 二 (min-max uniform grid).
 //
 // Per 128-column block b (processing order):
-//   panel_kernel:   rows in parallel, 4 lanes per row, the block's 128
-//                   weights of a row spread over the quad's registers (lane q
-//                   holds columns 4i+q); U's diagonal block in LDS; column j's
-//                   weight is broadcast inside the quad with DPP, quantized,
-//                   its scaled error e = (w - q)/U[j][j] pushed onto the later
-//                   columns of the block (w -= e*U[j][.]) and kept in ErrT.
+//   panel_kernel:   rows in parallel, 16 lanes per row (lane q holds the
+//                   block's columns 16t+q, t = 0..7), 4 rows per wave, 4 waves
+//                   per workgroup; U's diagonal block in LDS; column j's
+//                   weight is broadcast across the row's lanes with DPP,
+//                   quantized, its scaled error e = (w - q)/U[j][j] pushed onto
+//                   the later columns of the block (w -= e*U[j][.]) and kept in
+//                   ErrT.
 //   trailing GEMM:  W[:, b1:] -= Err * U[b0:b1, b1:] (fp32 MFMA).
 #include "gemm_f32.h"
 
@@ -22,8 +23,9 @@
 namespace gptq {
 
 constexpr int kQB = 128;          // block width (lazy batch)
-constexpr int kQRows = 16;        // rows per workgroup (one wave, 4 lanes per row)
-constexpr int kUP = 36;           // LDS pitch of one (column j, lane q) slot row
+constexpr int kQL = 16;           // lanes per row
+constexpr int kQS = kQB / kQL;    // columns (slots) per lane
+constexpr int kQRows = 16;        // rows per workgroup (4 waves x 4 rows)
 
 // ---------------------------------------------------------------- W gather
 __global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ W, gptq_dtype wt,
@@ -39,21 +41,43 @@ __global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ 
 }
 
 // ---------------------------------------------------------------- helpers
-template <int P>
-GPTQ_DEV float quad_bcast_c(float v) {
-  // DPP quad_perm [P,P,P,P]: every lane of a quad reads lane P of that quad
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), P | (P << 2) | (P << 4) | (P << 6),
-                                      0xF, 0xF, false));
+// DPP on 16-lane rows.  dpp control: quad_perm 0x00-0xFF, row_ror:r = 0x120+r;
+// bank k = lanes 4k..4k+3 of a row; lanes of banks left out of bank_mask keep
+// `old`.
+template <int CTRL, int BANKS>
+GPTQ_DEV int dpp_upd(int old, int src) {
+  return __builtin_amdgcn_update_dpp(old, src, CTRL, 0xF, BANKS, false);
 }
-GPTQ_DEV float quad_min(float v) {
-  v = fminf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-  v = fminf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+template <int CTRL>
+GPTQ_DEV float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// every lane of a 16-lane row reads lane P of that row: broadcast inside the
+// quads, then copy bank P/4 to the opposite bank (rotate by 8) and those two
+// to the remaining two (rotate by 4); either rotation direction maps the banks
+// the same way
+template <int P>
+GPTQ_DEV float row_bcast16(float v) {
+  constexpr int p = P & 3, B0 = P >> 2;
+  int x = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), p | (p << 2) | (p << 4) | (p << 6),
+                                   0xF, 0xF, false);
+  x = dpp_upd<0x128, (1 << (B0 ^ 2))>(x, x);
+  x = dpp_upd<0x124, (1 << (B0 ^ 1)) | (1 << (B0 ^ 3))>(x, x);
+  return __builtin_bit_cast(float, x);
+}
+GPTQ_DEV float row_min16(float v) {
+  v = fminf(v, dpp_f<0xB1>(v));
+  v = fminf(v, dpp_f<0x4E>(v));
+  v = fminf(v, dpp_f<0x124>(v));
+  v = fminf(v, dpp_f<0x128>(v));
   return v;
 }
-GPTQ_DEV float quad_max(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+GPTQ_DEV float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x128>(v));
   return v;
 }
 
@@ -87,52 +111,72 @@ struct PanelArgs {
   float maxq;
 };
 
-// One wave per workgroup: 16 rows, 4 lanes per row (lane q holds the block's
-// columns 4t+q, t = 0..31).  Every column step is instantiated separately
-// (template fold over the 128 columns), so the row slice stays in registers
-// with compile-time indices.  GT > 0: groups of GT columns inside the block
-// (group starts known at compile time); GT == 0: groups of G >= 128 columns,
-// which can only start at the block's first column.
+// 16 rows per workgroup, 16 lanes per row (lane q holds the block's columns
+// 16t+q, t = 0..7).  Every column step is instantiated separately (template
+// fold over the 128 columns), so the row slice stays in registers with
+// compile-time indices.  GT > 0: groups of GT columns inside the block (group
+// starts known at compile time); GT == 0: groups of G >= 128 columns, which
+// can only start at the block's first column.
 template <int GT>
-__global__ __launch_bounds__(64) void panel_kernel(PanelArgs a) {
-  __shared__ float4 sU4[kQB][4][kUP / 4];   // sU4[j][q][t/4] = U[b0+j][b0+4t+q .. +12 step 4]
+__global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
+  __shared__ float4 sU4[kQB][kQS / 4][kQL];   // sU4[j][t/4][q] = U[b0+j][b0+16t+q], t..t+3
   __shared__ float sInv[kQB];
   __shared__ int sPerm[kQB];
 
   const int tid = threadIdx.x;
   float* sU = reinterpret_cast<float*>(&sU4[0][0][0]);
-  // U's diagonal block (strict upper part), 16 independent loads in flight per lane
-  for (int e0 = 0; e0 < kQB * kQB; e0 += 64 * 16) {
-    float v[16];
+  // U's diagonal block, strict upper part (zero on and below the diagonal):
+  // 16 float4 loads in flight per thread
+  {
+    // 16-byte loads when every U row starts 16-byte aligned
+    const bool vec = (a.d % 4 == 0) && (reinterpret_cast<uintptr_t>(a.U) % 16 == 0);
+    float4 v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const int e = e0 + u * 64 + tid;
-      const int j = e >> 7, c = e & 127;
-      v[u] = (j < a.bw && c < a.bw && c > j) ? a.U[(size_t)(a.b0 + j) * a.d + a.b0 + c] : 0.0f;
+      const int e = u * 256 + tid;              // float4 index: row j, columns 4m .. 4m+3
+      const int j = e >> 5, c = 4 * (e & 31);
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < a.bw && c + 3 > j) {
+        const float* src = a.U + (size_t)(a.b0 + j) * a.d + a.b0 + c;
+        if (vec && c + 3 < a.bw) {
+          v[u] = *reinterpret_cast<const float4*>(src);
+        } else {
+          if (c + 3 < a.bw) v[u].w = src[3];
+          if (c + 0 < a.bw) v[u].x = src[0];
+          if (c + 1 < a.bw) v[u].y = src[1];
+          if (c + 2 < a.bw) v[u].z = src[2];
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const int e = e0 + u * 64 + tid;
-      const int j = e >> 7, c = e & 127;
-      sU[(j * 4 + (c & 3)) * kUP + (c >> 2)] = v[u];
+      const int e = u * 256 + tid;
+      const int j = e >> 5, c = 4 * (e & 31);
+      const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int cc = c + k;
+        const int t = cc >> 4;
+        sU[((j * (kQS / 4) + (t >> 2)) * kQL + (cc & 15)) * 4 + (t & 3)] = (cc > j) ? vv[k] : 0.0f;
+      }
     }
   }
-  for (int j = tid; j < kQB; j += 64) {
+  for (int j = tid; j < kQB; j += 256) {
     sInv[j] = (j < a.bw) ? 1.0f / a.U[(size_t)(a.b0 + j) * a.d + a.b0 + j] : 0.0f;
     sPerm[j] = (j < a.bw) ? a.perm[a.b0 + j] : 0;
   }
   __syncthreads();
 
-  const int q = tid & 3;
-  const int row = blockIdx.x * kQRows + (tid >> 2);
+  const int q = tid & 15;
+  const int row = blockIdx.x * kQRows + (tid >> 4);
   const bool rv = row < a.d_out;
   const int rowc = rv ? row : 0;     // clamped row for loads; stores are masked
   const float* wrow = a.Wp + (size_t)rowc * a.d + a.b0;
   const int bw = a.bw;
 
-  float w[32];
+  float w[kQS];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) w[t] = (4 * t + q < bw) ? wrow[4 * t + q] : 0.0f;
+  for (int t = 0; t < kQS; ++t) w[t] = (kQL * t + q < bw) ? wrow[kQL * t + q] : 0.0f;
 
   float scale = 1.0f, zero = 0.0f, rscale = 1.0f;
   if (GT == 0 && a.b0 % a.G != 0) {
@@ -143,43 +187,50 @@ __global__ __launch_bounds__(64) void panel_kernel(PanelArgs a) {
     rscale = 1.0f / scale;
   }
   // results of the lane's own columns, stored once at the end
-  float eown[32], qown[32];
-  uint32_t cown[8];
+  float eown[kQS], qown[kQS];
+  uint32_t cown[kQS / 4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) cown[t] = 0u;
+  for (int t = 0; t < kQS / 4; ++t) cown[t] = 0u;
 
   auto group_start = [&]<int J>() {
-    constexpr int I = J / 4;
+    constexpr int I = J / kQL;
     float mn = INFINITY, mx = -INFINITY;
-    if constexpr (GT > 0) {
-      // slots I .. I + GT/4 - 1 hold the group's columns J .. J + GT - 1
+    if constexpr (GT >= kQL) {
+      // slots I .. I + GT/16 - 1 hold the group's columns J .. J + GT - 1
 #pragma unroll
-      for (int t = I; t < I + GT / 4; ++t) {
-        if (4 * t + q < bw) {
+      for (int t = I; t < I + GT / kQL; ++t) {
+        if (kQL * t + q < bw) {
           mn = fminf(mn, w[t]);
           mx = fmaxf(mx, w[t]);
         }
+      }
+    } else if constexpr (GT > 0) {
+      // a group inside one slot: lanes J%16 .. J%16 + GT - 1
+      constexpr int L0 = J % kQL;
+      if (q >= L0 && q < L0 + GT && J + (q - L0) < bw) {
+        mn = w[I];
+        mx = w[I];
       }
     } else {
       // J == 0: the whole block (columns < bw), then the rest of the group
       // from the work copy, which holds every earlier block's lazy update
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        if (4 * t + q < bw) {
+      for (int t = 0; t < kQS; ++t) {
+        if (kQL * t + q < bw) {
           mn = fminf(mn, w[t]);
           mx = fmaxf(mx, w[t]);
         }
       }
       const int gend = min(a.b0 + a.G, a.d);
       const float* wr = a.Wp + (size_t)rowc * a.d;
-      for (int cg = a.b0 + bw + q; cg < gend; cg += 4) {
+      for (int cg = a.b0 + bw + q; cg < gend; cg += kQL) {
         const float v = wr[cg];
         mn = fminf(mn, v);
         mx = fmaxf(mx, v);
       }
     }
-    mn = quad_min(mn);
-    mx = quad_max(mx);
+    mn = row_min16(mn);
+    mx = row_max16(mx);
     grid_params(mn, mx, a.maxq, scale, zero);
     rscale = 1.0f / scale;
     const int gi = (GT > 0) ? (a.b0 + J) / GT : a.b0 / a.G;
@@ -190,7 +241,7 @@ __global__ __launch_bounds__(64) void panel_kernel(PanelArgs a) {
   };
 
   auto step = [&]<int J>() {
-    constexpr int I = J / 4, P = J % 4;
+    constexpr int I = J / kQL, P = J % kQL;
     if (J >= bw) return;
     if constexpr (GT > 0) {
       if constexpr (J % GT == 0) group_start.template operator()<J>();
@@ -199,7 +250,7 @@ __global__ __launch_bounds__(64) void panel_kernel(PanelArgs a) {
         if (a.b0 % a.G == 0) group_start.template operator()<0>();
       }
     }
-    const float wj = quad_bcast_c<P>(w[I]);
+    const float wj = row_bcast16<P>(w[I]);
     // correctly rounded wj/scale from the reciprocal (one residual correction)
     const float t0 = wj * rscale;
     const float res = fmaf(-t0, scale, wj);
@@ -212,11 +263,11 @@ __global__ __launch_bounds__(64) void panel_kernel(PanelArgs a) {
       qown[I] = qv;
       cown[I >> 2] |= (uint32_t)c << (8 * (I & 3));
     }
-    // w[t] -= e * U[J][4t+q] for the later columns of the block (slots t >= I;
+    // w[t] -= e * U[J][16t+q] for the later columns of the block (slots t >= I;
     // entries at columns <= J are retired, and U is zero there)
 #pragma unroll
-    for (int t = (I & ~3); t < 32; t += 4) {
-      const float4 u4 = sU4[J][q][t >> 2];
+    for (int t = (I & ~3); t < kQS; t += 4) {
+      const float4 u4 = sU4[J][t >> 2][q];
       if (t + 0 >= I) w[t + 0] = fmaf(-e, u4.x, w[t + 0]);
       if (t + 1 >= I) w[t + 1] = fmaf(-e, u4.y, w[t + 1]);
       if (t + 2 >= I) w[t + 2] = fmaf(-e, u4.z, w[t + 2]);
@@ -231,8 +282,8 @@ __global__ __launch_bounds__(64) void panel_kernel(PanelArgs a) {
   uint8_t* crow = a.codes + (size_t)row * a.d;
   float* qrow = a.Q ? a.Q + (size_t)row * a.d : nullptr;
 #pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    const int j = 4 * t + q;
+  for (int t = 0; t < kQS; ++t) {
+    const int j = kQL * t + q;
     if (j < bw) {
       const int oc = sPerm[j];
       crow[oc] = (uint8_t)(cown[t >> 2] >> (8 * (t & 3)));
@@ -361,13 +412,13 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
     pa.b0 = b0;
     pa.bw = bw;
     switch (gt) {
-      case 4: panel_kernel<4><<<nrow_blocks, 64, 0, s>>>(pa); break;
-      case 8: panel_kernel<8><<<nrow_blocks, 64, 0, s>>>(pa); break;
-      case 16: panel_kernel<16><<<nrow_blocks, 64, 0, s>>>(pa); break;
-      case 32: panel_kernel<32><<<nrow_blocks, 64, 0, s>>>(pa); break;
-      case 64: panel_kernel<64><<<nrow_blocks, 64, 0, s>>>(pa); break;
-      case 128: panel_kernel<128><<<nrow_blocks, 64, 0, s>>>(pa); break;
-      default: panel_kernel<0><<<nrow_blocks, 64, 0, s>>>(pa); break;
+      case 4: panel_kernel<4><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      case 8: panel_kernel<8><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      case 16: panel_kernel<16><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      case 32: panel_kernel<32><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      case 64: panel_kernel<64><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      case 128: panel_kernel<128><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      default: panel_kernel<0><<<nrow_blocks, 256, 0, s>>>(pa); break;
     }
     GPTQ_LAUNCH_CHECK();
     const int b1 = b0 + bw;
