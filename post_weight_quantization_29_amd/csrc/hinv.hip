@@ -16,10 +16,10 @@
 //   2. perm: identity or stable descending rank of diag(H)
 //   3. A[a][b] = H[perm[n-1-a]][perm[n-1-b]] + lambda*[a==b], padded with I
 //   4. blocked right-looking upper Cholesky, 128-row blocks:
-//        diag kernel: R_kk and R_kk^-1 from the block (one workgroup, LDS),
-//                     R_kk^-1 stored in place, PD flag on a bad pivot
-//        panel GEMM:  R_k,rest = R_kk^-T A_k,rest      (in place)
-//        update GEMM: A_rest -= R_k,rest^T R_k,rest    (upper tiles only)
+//        block kernel: every workgroup factors A_kk; workgroup 0 forms
+//                      R_kk^-1, the others the panel R_k,rest = R_kk^-T A_k,rest
+//                      (in place); PD flag on a bad pivot
+//        update GEMM:  A_rest -= R_k,rest^T R_k,rest    (upper tiles only)
 //   5. triangular inverse by a binary tree over the 128-blocks: for a node
 //      [a, mid) + [mid, b) with both halves already inverted,
 //      X12 = -X11 * R12 * X22 (two grouped GEMMs per tree level)
@@ -107,68 +107,257 @@ __global__ __launch_bounds__(256) void gather_flip_kernel(const float* __restric
   A[(size_t)a * np + b] = v;
 }
 
-// ---------------------------------------------------------------- 4a. diagonal block
-// In-place elimination on the augmented block [A_kk | I]: at step j the pivot
-// row is scaled by 1/sqrt(pivot) and subtracted from the rows below, on both
-// halves.  Column j of the left half is retired at that step, so it stores the
-// new column j of the right half.  The finished block holds R^-T (lower incl.
-// diagonal) and R (strict upper).  Thread t owns column t%128 and rows
-// 16*(t/128) .. +15 in registers (a wave's rows are uniform); pivot rows go
-// through LDS.  The step loop is unrolled by 16 so that register indices and
-// the "row below the pivot" tests are compile-time.
-__global__ __launch_bounds__(1024) void chol_diag_kernel(float* __restrict__ A, int np, int k,
-                                                         int* __restrict__ flag) {
-  __shared__ __attribute__((aligned(16))) float rowbuf[2][kNB];
-  const int t = threadIdx.x;
-  const int x = t & (kNB - 1), g = t >> 7;
-  float* blk = A + (size_t)k * kNB * np + (size_t)k * kNB;
-  float v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = blk[(size_t)(16 * g + i) * np + x];
+// ---------------------------------------------------------------- 4. block step
+// One launch per 128-block k: every workgroup factors the diagonal block
+// A_kk = L L^T itself (L = R_kk^T) and then applies L^-1 to a 128-column
+// tile T: workgroup 0 to the identity, which yields L^-1 = R_kk^-T (stored
+// transposed, as R_kk^-1, in Dinv), workgroup t >= 1 to the tile A_k,(k+t),
+// which yields the panel R_k,(k+t) = R_kk^-T A_k,(k+t) in place.  The
+// factorization is repeated per workgroup (the workgroups would otherwise
+// wait for one another), so the launch has no inter-workgroup dependency.
+//
+// Inside a workgroup (4 waves, all data in LDS):
+//   for each 32-column sub-block b: one wave factors and inverts the 32x32
+//   diagonal sub-block (two columns per step: the pivots through readlane,
+//   the scaled columns through LDS); then the sub-blocks below are scaled,
+//   M_ab <- M_ab L_bb^-T, and the trailing lower sub-blocks updated,
+//   M_ac -= M_ab M_cb^T, with v_mfma_f32_32x32x2f32;
+//   then each wave solves L X = T for 32 of the tile's columns, sub-block row
+//   by sub-block row: X_a = L_aa^-1 (T_a - sum_{m<a} L_am X_m).
+constexpr int kLP = kNB + 1;      // LDS pitch of the 128x128 tiles (odd: column walks hit distinct banks)
+constexpr int kVP = 33;           // LDS pitch of the 32x32 sub-block inverses
 
-#pragma unroll 1
-  for (int jb = 0; jb < kNB / 16; ++jb) {
+// acc(m, n) += sum_{k < 32} A(m, k) B(k, n), A(m, k) = sa * pa[m*lda + k];
+// B(k, n) = pb[n*ldb + k] (B_NMAJOR) or pb[k*ldb + n].  Lane l supplies
+// A(l%32, 2s + l/32) and B(2s + l/32, l%32) to step s.
+template <bool B_NMAJOR>
+GPTQ_DEV void mm32(f32x16_t& acc, const float* pa, int lda, float sa, const float* pb, int ldb, int lane) {
+  const int m = lane & 31, kh = lane >> 5;
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int j = 16 * jb + jj;
-      float* rb = rowbuf[jj & 1];
-      if (g == jb) rb[x] = v[jj];
-      __syncthreads();
-      if (g < jb) continue;                 // rows already final
-      const float p = rb[j];
-      if (g == jb && x == j && !(p > 0.0f)) flag[0] = 1;   // an active lane reports the pivot
-      // 1/sqrt(p): hardware estimate refined by one Newton step
-      float sc = __builtin_amdgcn_rsqf(p);
-      sc = sc * fmaf(-0.5f * p * sc, sc, 1.5f);
-      const bool isj = (x == j);
-      const float rjx = isj ? sc : rb[x] * sc;
-      const float keep = isj ? 0.0f : 1.0f;
-      const float cmul = sc * rjx;          // row i: v -= rb[i] * sc * rjx
-      const float4* r4 = reinterpret_cast<const float4*>(rb + 16 * g);
-      float m[16];
+  for (int st = 0; st < 16; ++st) {
+    const int k = 2 * st + kh;
+    const float av = sa * pa[m * lda + k];
+    const float bv = B_NMAJOR ? pb[m * ldb + k] : pb[k * ldb + m];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+  }
+}
+GPTQ_DEV void load32(f32x16_t& acc, const float* p, int ld, int lane) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 u = r4[i4];
-        m[4 * i4 + 0] = u.x; m[4 * i4 + 1] = u.y; m[4 * i4 + 2] = u.z; m[4 * i4 + 3] = u.w;
+  for (int r = 0; r < 16; ++r) acc[r] = p[mfma32_row(r, lane) * ld + mfma32_col(lane)];
+}
+GPTQ_DEV void store32(const f32x16_t& acc, float* p, int ld, int lane) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) p[mfma32_row(r, lane) * ld + mfma32_col(lane)] = acc[r];
+}
+
+// Cholesky and inverse of the 32x32 sub-block at Mb (pitch kLP), one wave.
+// Lane l holds row l%32 of the block, columns 16(l/32) .. +15 (v), and
+// column l%32 of the inverse, rows 16(l/32) .. +15 (y, starting from I).
+// Two columns J, J+1 per step: their pivots come through readlane, their L
+// values and the two finished inverse rows go through LDS (cb, 128 floats)
+// once, and every lane applies the rank-2 update to its part of the block
+// and of the inverse (the inverse takes the same row operations, so
+// y ends as L^-1).  Mb keeps L on and below the diagonal (the upper triangle
+// is left undefined); Vb (pitch kVP) receives L^-1 with zeros above.  bad is
+// set on a pivot that is not > 0.
+GPTQ_DEV void leaf_chol_inv(float* Mb, float* Vb, float* cb, int lane, int& bad) {
+  int i = lane & 31, h = lane >> 5;
+  // opaque per call: keeps the compiler from hoisting the per-step lane masks
+  // out of the caller's loop (they would spill)
+  asm volatile("" : "+v"(i), "+v"(h));
+  float v[16], y[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    v[r] = Mb[i * kLP + 16 * h + r];
+    y[r] = (16 * h + r == i) ? 1.0f : 0.0f;
+  }
+  auto rsq1 = [](float p) {
+    // 1/sqrt(p): hardware estimate refined by one Newton step
+    float dd = __builtin_amdgcn_rsqf(p);
+    return dd * fmaf(-0.5f * p * dd, dd, 1.5f);
+  };
+  auto rl = [](float x, int ln) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), ln));
+  };
+  auto step = [&]<int J2>() {
+    constexpr int J = 2 * J2, hj = J >> 4, r0 = J & 15, r1 = r0 + 1;
+    const float p0 = rl(v[r0], hj * 32 + J);          // A[J][J]
+    const float a10 = rl(v[r0], hj * 32 + J + 1);     // A[J+1][J]
+    const float p1r = rl(v[r1], hj * 32 + J + 1);     // A[J+1][J+1]
+    const float d0 = rsq1(p0);
+    const float l10 = a10 * d0;
+    const float p1 = fmaf(-l10, l10, p1r);
+    const float d1 = rsq1(p1);
+    if (!(p0 > 0.0f) || !(p1 > 0.0f)) bad = 1;
+    if (h == hj) {
+      const float c0 = (i == J) ? p0 * d0 : v[r0] * d0;                       // L[i][J]
+      const float c1 = (i == J + 1) ? p1 * d1 : fmaf(-c0, l10, v[r1]) * d1;   // L[i][J+1]
+      if (i >= J) v[r0] = c0;
+      if (i >= J + 1) v[r1] = c1;
+      // inverse rows J, J+1 of this lane's column i
+      const float yj = y[r0] * d0;
+      const float yj1 = fmaf(-l10, yj, y[r1]) * d1;
+      y[r0] = yj;
+      y[r1] = yj1;
+      cb[i] = c0;
+      cb[32 + i] = c1;
+      cb[64 + i] = yj;
+      cb[96 + i] = yj1;
+    }
+    asm volatile("" ::: "memory");
+    const float li0 = cb[i], li1 = cb[32 + i], yJ = cb[64 + i], yJ1 = cb[96 + i];
+    float lc0[16], lc1[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 q0 = reinterpret_cast<const float4*>(cb + 16 * h)[r4];
+      const float4 q1 = reinterpret_cast<const float4*>(cb + 32 + 16 * h)[r4];
+      lc0[4 * r4 + 0] = q0.x; lc0[4 * r4 + 1] = q0.y; lc0[4 * r4 + 2] = q0.z; lc0[4 * r4 + 3] = q0.w;
+      lc1[4 * r4 + 0] = q1.x; lc1[4 * r4 + 1] = q1.y; lc1[4 * r4 + 2] = q1.z; lc1[4 * r4 + 3] = q1.w;
+    }
+    // entries (row, c) with c, row = 16h + r > J + 1 take the rank-2 update:
+    // v(i, c) -= L[i][J] L[c][J] + L[i][J+1] L[c][J+1];
+    // y(row, i) -= L[row][J] Y[J][i] + L[row][J+1] Y[J+1][i]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float nv = fmaf(-li1, lc1[r], fmaf(-li0, lc0[r], v[r]));
+      const float ny = fmaf(-lc1[r], yJ1, fmaf(-lc0[r], yJ, y[r]));
+      if (J + 1 < 16) {
+        if (r > J + 1) { v[r] = nv; y[r] = ny; }
+        else { v[r] = h ? nv : v[r]; y[r] = h ? ny : y[r]; }
+      } else if (r > J + 1 - 16) {
+        v[r] = h ? nv : v[r];
+        y[r] = h ? ny : y[r];
       }
-      if (g > jb) {
+    }
+    asm volatile("" ::: "memory");
+  };
+  [&]<int... Js>(std::integer_sequence<int, Js...>) {
+    (step.template operator()<Js>(), ...);
+  }(std::make_integer_sequence<int, 16>{});
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = fmaf(-m[i], cmul, v[i] * keep);
-      } else {
+  for (int r = 0; r < 16; ++r) {
+    Mb[i * kLP + 16 * h + r] = v[r];
+    Vb[(16 * h + r) * kVP + i] = y[r];
+  }
+}
+
+__global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A, int np, int k,
+                                                         float* __restrict__ Dinv, int* __restrict__ flag) {
+  __shared__ __attribute__((aligned(16))) float M[kNB * kLP];
+  __shared__ __attribute__((aligned(16))) float T[kNB * kLP];
+  __shared__ __attribute__((aligned(16))) float V[4][32 * kVP];
+  __shared__ __attribute__((aligned(16))) float cb[128];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.x;                     // 0: identity, t >= 1: column block k + t
+  const float* Akk = A + (size_t)k * kNB * np + (size_t)k * kNB;
+  float* At = A + (size_t)k * kNB * np + (size_t)(k + tile) * kNB;
+
+  // load the diagonal block and the tile (16 float4 per thread each)
+  {
+    float4 va[16], vt[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (i == jj) v[i] = rjx;
-          else if (i > jj) v[i] = fmaf(-m[i], cmul, v[i] * keep);
+    for (int u = 0; u < 16; ++u) {
+      const int e = u * 256 + tid, r = e >> 5, c4 = 4 * (e & 31);
+      va[u] = *reinterpret_cast<const float4*>(Akk + (size_t)r * np + c4);
+      if (tile > 0) vt[u] = *reinterpret_cast<const float4*>(At + (size_t)r * np + c4);
+      else vt[u] = make_float4(r == c4 ? 1.f : 0.f, r == c4 + 1 ? 1.f : 0.f, r == c4 + 2 ? 1.f : 0.f,
+                               r == c4 + 3 ? 1.f : 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = u * 256 + tid, r = e >> 5, c4 = 4 * (e & 31);
+      float* pm = M + r * kLP + c4;
+      pm[0] = va[u].x; pm[1] = va[u].y; pm[2] = va[u].z; pm[3] = va[u].w;
+      float* pt = T + r * kLP + c4;
+      pt[0] = vt[u].x; pt[1] = vt[u].y; pt[2] = vt[u].z; pt[3] = vt[u].w;
+    }
+  }
+  __syncthreads();
+
+  int bad = 0;
+#pragma unroll 1
+  for (int b = 0; b < 4; ++b) {
+    const int o = 32 * b;
+    if (wave == 0) leaf_chol_inv(M + o * kLP + o, V[b], cb, lane, bad);
+    __syncthreads();
+    // sub-blocks below: M_ab <- M_ab L_bb^-T   (wave w: a = b + 1 + w)
+    if (wave < 3 - b) {
+      const int a = b + 1 + wave;
+      f32x16_t acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+      mm32<true>(acc, M + (32 * a) * kLP + o, kLP, 1.0f, V[b], kVP, lane);
+      asm volatile("" ::: "memory");
+      store32(acc, M + (32 * a) * kLP + o, kLP, lane);
+    }
+    __syncthreads();
+    // trailing lower sub-blocks: M_ac -= M_ab M_cb^T, a >= c > b
+    {
+      int q = 0;
+      for (int a = b + 1; a < 4; ++a) {
+        for (int c = b + 1; c <= a; ++c, ++q) {
+          if ((q & 3) != wave) continue;
+          f32x16_t acc;
+          load32(acc, M + (32 * a) * kLP + 32 * c, kLP, lane);
+          mm32<true>(acc, M + (32 * a) * kLP + o, kLP, -1.0f, M + (32 * c) * kLP + o, kLP, lane);
+          store32(acc, M + (32 * a) * kLP + 32 * c, kLP, lane);
         }
       }
     }
+    __syncthreads();
   }
-  // store R_kk^-1 = (R^-T)^T in place: blk[x][row] = v(row, x) for row >= x, 0 below
-  __syncthreads();
+  if (bad) flag[0] = 1;
+
+  // forward substitution on this wave's 32 columns of T
+  {
+    float* Tw = T + 32 * wave;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = 16 * g + i;
-    blk[(size_t)x * np + row] = (row >= x) ? v[i] : 0.0f;
+    for (int a = 0; a < 4; ++a) {
+      f32x16_t acc;
+      load32(acc, Tw + (32 * a) * kLP, kLP, lane);
+#pragma unroll
+      for (int m = 0; m < a; ++m)
+        mm32<false>(acc, M + (32 * a) * kLP + 32 * m, kLP, -1.0f, Tw + (32 * m) * kLP, kLP, lane);
+      store32(acc, Tw + (32 * a) * kLP, kLP, lane);
+      asm volatile("" ::: "memory");
+      f32x16_t x;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = 0.0f;
+      mm32<false>(x, V[a], kVP, 1.0f, Tw + (32 * a) * kLP, kLP, lane);
+      asm volatile("" ::: "memory");
+      store32(x, Tw + (32 * a) * kLP, kLP, lane);
+      asm volatile("" ::: "memory");
+    }
+  }
+  __syncthreads();
+
+  if (tile == 0) {
+    // R_kk^-1 = (L^-1)^T: Dinv[r][c] = T[c][r] for c >= r, 0 below the diagonal
+    float* D = Dinv + (size_t)k * kNB * kNB;
+    for (int e = tid; e < kNB * kNB; e += 256) {
+      const int r = e >> 7, c = e & 127;
+      D[e] = (c >= r) ? T[c * kLP + r] : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = u * 256 + tid, r = e >> 5, c4 = 4 * (e & 31);
+      const float* pt = T + r * kLP + c4;
+      *reinterpret_cast<float4*>(At + (size_t)r * np + c4) = make_float4(pt[0], pt[1], pt[2], pt[3]);
+    }
+  }
+}
+
+// diagonal blocks of R^-1 into A, where the triangular inverse starts from them
+__global__ __launch_bounds__(256) void dinv_scatter_kernel(const float* __restrict__ Dinv, float* __restrict__ A,
+                                                           int np) {
+  const int k = blockIdx.x;
+  const float* D = Dinv + (size_t)k * kNB * kNB;
+  float* blk = A + (size_t)k * kNB * np + (size_t)k * kNB;
+  for (int e = threadIdx.x; e < kNB * kNB / 4; e += 256) {
+    const int r = e >> 5, c4 = 4 * (e & 31);
+    *reinterpret_cast<float4*>(blk + (size_t)r * np + c4) = *reinterpret_cast<const float4*>(D + (size_t)r * kNB + c4);
   }
 }
 
@@ -259,22 +448,23 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
   gather_flip_kernel<<<dim3((np + 255) / 256, np), 256, 0, s>>>(H, n, np, perm, lam, A);
   GPTQ_LAUNCH_CHECK();
 
-  // 4. Cholesky A = R^T R, storing R_kk^-1 on the diagonal blocks
+  // 4. Cholesky A = R^T R: per block, diagonal factor + panel in one launch,
+  //    then the trailing update; R_kk^-1 goes to Dinv (in Z's space, which the
+  //    triangular inverse only uses later) and then onto A's diagonal blocks
+  float* Dinv = Z;
   for (int k = 0; k < nb; ++k) {
-    chol_diag_kernel<<<1, 1024, 0, s>>>(A, np, k, flag);
-    GPTQ_LAUNCH_CHECK();
     const int rest = np - (k + 1) * kNB;
-    if (rest <= 0) continue;
-    float* Akk = A + (size_t)k * kNB * np + (size_t)k * kNB;
-    float* Arow = Akk + kNB;                                  // A[k-block rows][after]
-    float* Atrail = A + (size_t)(k + 1) * kNB * np + (size_t)(k + 1) * kNB;
-    // R_k,rest = R_kk^-T A_k,rest : Aop(i,j) = Rinv[j][i] (k-major), in place
-    gemm_f32<true>(Akk, np, Arow, np, Arow, np, kNB, rest, kNB, 1.0f, 0.0f, 0, 0, 0, s);
+    chol_panel_kernel<<<1 + rest / kNB, 256, 0, s>>>(A, np, k, Dinv, flag);
     GPTQ_LAUNCH_CHECK();
+    if (rest <= 0) continue;
+    float* Arow = A + (size_t)k * kNB * np + (size_t)(k + 1) * kNB;   // R_k,rest
+    float* Atrail = A + (size_t)(k + 1) * kNB * np + (size_t)(k + 1) * kNB;
     // A_rest -= R_k,rest^T R_k,rest (upper tiles)
     gemm_f32<true>(Arow, np, Arow, np, Atrail, np, rest, rest, kNB, -1.0f, 1.0f, 0, 0, 1, s);
     GPTQ_LAUNCH_CHECK();
   }
+  dinv_scatter_kernel<<<nb, 256, 0, s>>>(Dinv, A, np);
+  GPTQ_LAUNCH_CHECK();
 
   // 5. triangular inverse, deepest tree level first
   std::vector<std::vector<TreeNode>> levels;

@@ -60,7 +60,7 @@ def test_hessian_zero_tokens_leaves_h():
 
 # ------------------------------------------------------------------ factor
 
-@pytest.mark.parametrize("d,desc", [(256, 0), (256, 1), (384, 1), (200, 0), (1000, 1)])
+@pytest.mark.parametrize("d,desc", [(256, 0), (256, 1), (384, 1), (200, 0), (1000, 1), (2048, 1)])
 def test_prepare_hinv_parity(d, desc):
     say(f"[hinv] d={d} desc_act={desc}")
     import post_weight_quantization_29_amd as P
