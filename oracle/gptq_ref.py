@@ -97,10 +97,15 @@ def damp(H: np.ndarray, damp_percent: float) -> Tuple[np.ndarray, float]:
 def act_order(H: np.ndarray, desc_act: bool) -> np.ndarray:
     """Processing order -> original column.  Identity unless desc_act, then
     descending diag(H) with ties broken by the lower original index."""
-    d = H.shape[0]
+    return order_from_keys(np.diag(H), desc_act)
+
+
+def order_from_keys(keys: np.ndarray, desc_act: bool) -> np.ndarray:
+    """The same order from the diagonal alone (keys = diag(H))."""
+    d = keys.shape[0]
     if not desc_act:
         return np.arange(d, dtype=np.int64)
-    return np.argsort(-np.diag(H), kind="stable").astype(np.int64)
+    return np.argsort(-np.asarray(keys, dtype=np.float64), kind="stable").astype(np.int64)
 
 
 # ----------------------------------------------------------------------------
@@ -183,9 +188,29 @@ def n_groups(d_in: int, group_size: int) -> int:
     return (d_in + G - 1) // G
 
 
+@dataclass
+class Prepared:
+    """The steps that depend on H only: processing order, damping, factor."""
+    perm: np.ndarray
+    lam: float
+    U: np.ndarray
+
+
+def prepare(H: np.ndarray, damp_percent: float = 0.01, desc_act: bool = False) -> Prepared:
+    """Order ([P5] 2.2 "first"), damp ([P5] 3.3), then the factor of the damped,
+    permuted H's inverse ([P5] 2.2 "third")."""
+    perm = act_order(H, desc_act)
+    Hp = H[np.ix_(perm, perm)]
+    Hd, lam = damp(Hp, damp_percent)
+    return Prepared(perm=perm, lam=lam, U=hinv_factor(Hd))
+
+
 def gptq(W: np.ndarray, H: np.ndarray, *, bits: int = 4, group_size: int = 128,
          block_size: int = 128, damp_percent: float = 0.01, desc_act: bool = False,
-         decision: str = "f32") -> GPTQResult:
+         decision: str = "f32", prepared: Optional[Prepared] = None) -> GPTQResult:
+    """The column loop.  ``prepared`` (from ``prepare(H, damp_percent,
+    desc_act)``) lets several quantizer settings share one H's order and
+    factor; without it they are computed here."""
     W64 = np.asarray(W, dtype=np.float64)
     d_out, d = W64.shape
     assert H.shape == (d, d)
@@ -193,10 +218,8 @@ def gptq(W: np.ndarray, H: np.ndarray, *, bits: int = 4, group_size: int = 128,
     G = d if group_size == -1 else int(group_size)
     B = int(block_size)
 
-    perm = act_order(H, desc_act)
-    Hp = H[np.ix_(perm, perm)]
-    Hd, lam = damp(Hp, damp_percent)
-    U = hinv_factor(Hd)
+    prep = prepared if prepared is not None else prepare(H, damp_percent, desc_act)
+    perm, lam, U = prep.perm, prep.lam, prep.U
 
     Wp = W64[:, perm].copy()
     codes_p = np.zeros((d_out, d), dtype=np.int64)

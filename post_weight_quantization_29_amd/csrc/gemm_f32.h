@@ -138,6 +138,22 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // C's old values are loaded before the contraction so that their latency and
+  // bandwidth overlap the MFMA work (C never aliases A or B when beta != 0)
+  float cold[2][2][16];
+  if (EPI == kStore && !skip && beta != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+          const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
+          cold[i][j][r] = (m < P.M && n < P.N) ? P.C[(size_t)m * P.ldc + n] : 0.0f;
+        }
+  }
+
   if (!skip && klo < khi) {
     float4 ra[8], rb[8];
     gemm_gload<A_KMAJOR, VEC>(P, m0, n0, klo, khi, tid, ra, rb);
@@ -162,23 +178,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
 
   if (EPI == kStore) {
     if (skip) return;
-    // all reads of C first, then all writes: a read placed after a write that
-    // might alias it would wait for that write's round trip
     if (beta != 0.0f) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float cold[16];
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-            const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
-            cold[r] = (m < P.M && n < P.N) ? P.C[(size_t)m * P.ldc + n] : 0.0f;
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = alpha * acc[i][j][r] + beta * cold[r];
-        }
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = alpha * acc[i][j][r] + beta * cold[i][j][r];
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
