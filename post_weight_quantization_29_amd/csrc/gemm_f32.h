@@ -41,7 +41,7 @@ struct GemmGroup {
   int count;
 };
 
-enum GemmEpilogue { kStore = 0, kDot = 1 };
+enum GemmEpilogue { kStore = 0, kDot = 1, kPartial = 2 };
 
 // 4 consecutive floats p[0..3], the ones at index >= lim read as 0.  VEC: the
 // address is 16-byte aligned whenever lim >= 4.
@@ -107,15 +107,21 @@ GPTQ_DEV void gemm_lstore(float* sA, float* sB, int tid, const float4 (&ra)[8], 
   }
 }
 
+// kPartial (split-K): workgroup w takes part w % parts of tile w / parts, i.e.
+// the part's share of the tile's contraction range (cut in multiples of 64),
+// and writes its raw 128x128 sum to partial (float*) in MFMA register order,
+// [tile*parts + part][wave 4][block 4][reg 16][lane 64]; gemm_splitk_reduce
+// adds the parts in order.
 template <bool A_KMAJOR, int EPI, bool VEC>
 __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float alpha, float beta,
                                                           int kloFromM, int khiFromN, int upperOnly,
-                                                          double* __restrict__ dot_out) {
+                                                          double* __restrict__ dot_out, int parts = 1) {
   __shared__ __attribute__((aligned(16))) float sA[kGK * kGP];
   __shared__ __attribute__((aligned(16))) float sB[kGK * kGP];
   __shared__ double sRed[4];
 
-  const int wg = blockIdx.x;
+  const int wg = (EPI == kPartial) ? (int)blockIdx.x / parts : (int)blockIdx.x;
+  const int part = (EPI == kPartial) ? (int)blockIdx.x % parts : 0;
   int pi = 0;
   while (pi + 1 < grp.count && grp.tile_start[pi + 1] <= wg) ++pi;
   const GemmProblem P = grp.p[pi];          // fields held in registers from here on
@@ -129,6 +135,12 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
   int klo = kloFromM ? m0 : 0;
   int khi = khiFromN ? min(P.K, n0 + kGT) : P.K;
   if (khi < klo) khi = klo;
+  if (EPI == kPartial) {
+    const int per = ((khi - klo + parts - 1) / parts + kGK - 1) / kGK * kGK;
+    const int b = min(khi, klo + part * per);
+    khi = min(khi, b + per);
+    klo = b;
+  }
 
   f32x16_t acc[2][2];
 #pragma unroll
@@ -176,6 +188,16 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
     }
   }
 
+  if (EPI == kPartial) {
+    float* out = reinterpret_cast<float*>(dot_out) + ((size_t)blockIdx.x * 4 + wave) * (4 * 16 * 64);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) out[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    return;
+  }
   if (EPI == kStore) {
     if (skip) return;
     if (beta != 0.0f) {
@@ -222,7 +244,57 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
   }
 }
 
+// C = alpha * sum_p partial[tile][p] + beta * C, parts added in order.  One
+// workgroup per tile; thread t handles elements t + 256i of the tile's 16384
+// in partial order (reads fully coalesced).
+static __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmGroup grp, const float* __restrict__ partial,
+                                                          int parts, float alpha, float beta) {
+  const int wg = blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < grp.count && grp.tile_start[pi + 1] <= wg) ++pi;
+  const GemmProblem P = grp.p[pi];
+  const int local = wg - grp.tile_start[pi];
+  const int tn = (P.N + kGT - 1) / kGT;
+  const int m0 = (local / tn) * kGT, n0 = (local % tn) * kGT;
+  const float* src = partial + (size_t)wg * parts * 16384;
+  for (int i = 0; i < 64; i += 16) {
+    float sum[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) sum[u] = 0.0f;
+    for (int p = 0; p < parts; ++p) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) sum[u] += src[(size_t)p * 16384 + threadIdx.x + 256 * (i + u)];
+    }
+    float cold[16];
+    size_t off[16];
+    bool ok[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = threadIdx.x + 256 * (i + u);
+      const int w = e >> 12, blk = (e >> 10) & 3, r = (e >> 6) & 15, lane = e & 63;
+      const int m = m0 + (w >> 1) * 64 + (blk >> 1) * 32 + mfma32_row(r, lane);
+      const int n = n0 + (w & 1) * 64 + (blk & 1) * 32 + mfma32_col(lane);
+      ok[u] = m < P.M && n < P.N;
+      off[u] = ok[u] ? (size_t)m * P.ldc + n : 0;
+      cold[u] = (ok[u] && beta != 0.0f) ? P.C[off[u]] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (ok[u]) P.C[off[u]] = alpha * sum[u] + beta * cold[u];
+  }
+}
+
 inline int gemm_tiles(int M, int N) { return ((M + kGT - 1) / kGT) * ((N + kGT - 1) / kGT); }
+
+// Parts per tile for a launch of `tiles` tiles whose longest contraction is
+// kmax: enough workgroups to fill the chip twice over (two resident per CU),
+// each part at least 128 deep, at most 8 parts.
+inline int splitk_parts(int tiles, int kmax) {
+  if (tiles <= 0) return 1;
+  int p = 1024 / tiles;
+  p = std::min(p, kmax / 128);
+  return std::max(1, std::min(8, p));
+}
 
 // Launch one group (count <= kGemmMaxGroup).  Returns the total tile count.
 // float4 global loads are used when every leading dimension is a multiple of 4
@@ -249,6 +321,33 @@ inline int launch_gemm_group(GemmGroup& g, float alpha, float beta, int kloFromM
                                                             upperOnly, dot_out);
   }
   return t;
+}
+
+// Split-K launch of a group (kStore semantics): each tile's contraction range
+// is cut into `parts`, the partial tiles go to `partial` (tiles * parts * 64 KB)
+// and are added in a fixed order by a second kernel.
+template <bool A_KMAJOR>
+inline void launch_gemm_group_splitk(GemmGroup& g, int parts, float alpha, float beta, int kloFromM,
+                                     int khiFromN, float* partial, hipStream_t s) {
+  int t = 0;
+  bool vec = true;
+  for (int i = 0; i < g.count; ++i) {
+    g.tile_start[i] = t;
+    t += gemm_tiles(g.p[i].M, g.p[i].N);
+    const GemmProblem& p = g.p[i];
+    vec = vec && (p.lda % 4 == 0) && (p.ldb % 4 == 0) &&
+          ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 15) == 0;
+  }
+  g.tile_start[g.count] = t;
+  if (t == 0) return;
+  double* pp = reinterpret_cast<double*>(partial);
+  if (vec)
+    gemm_f32_kernel<A_KMAJOR, kPartial, true><<<t * parts, 256, 0, s>>>(g, alpha, beta, kloFromM, khiFromN,
+                                                                        0, pp, parts);
+  else
+    gemm_f32_kernel<A_KMAJOR, kPartial, false><<<t * parts, 256, 0, s>>>(g, alpha, beta, kloFromM, khiFromN,
+                                                                         0, pp, parts);
+  gemm_splitk_reduce<<<t, 256, 0, s>>>(g, partial, parts, alpha, beta);
 }
 
 template <bool A_KMAJOR>

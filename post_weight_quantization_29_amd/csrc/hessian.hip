@@ -533,9 +533,10 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   const size_t item_stride4 = (size_t)ntiles * 4 * NEL / 4;
   const float4* src = reinterpret_cast<const float4*>(partial + ((size_t)q * 4 + wave) * NEL);
   const int tid = threadIdx.x;
-  float4 acc[NV];
+  // the splits are added in fp64 (in a fixed order) and rounded once
+  double acc[NV][4];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < NV; ++i) acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.0;
   for (int s = 0; s < splits; ++s) {
     const float4* ps = src + s * item_stride4;
     float4 v[NV];
@@ -543,19 +544,20 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
     for (int i = 0; i < NV; ++i) v[i] = ps[tid + 256 * i];     // all loads in flight
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      acc[i].x += v[i].x; acc[i].y += v[i].y; acc[i].z += v[i].z; acc[i].w += v[i].w;
+      acc[i][0] += v[i].x; acc[i][1] += v[i].y; acc[i][2] += v[i].z; acc[i][3] += v[i].w;
     }
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const float a4[4] = {acc[i].x, acc[i].y, acc[i].z, acc[i].w};
+    const float a4[4] = {(float)(2.0 * acc[i][0]), (float)(2.0 * acc[i][1]), (float)(2.0 * acc[i][2]),
+                         (float)(2.0 * acc[i][3])};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = 4 * (tid + 256 * i) + u;
       const int blk = e >> 10, r = (e >> 6) & 15, lane = e & 63;
       const int m = (blk / WB) * 32 + mfma32_row(r, lane);
       const int n = (blk % WB) * 32 + mfma32_col(lane);
-      sub[m][n] = 2.0f * a4[u];
+      sub[m][n] = a4[u];
     }
   }
   __syncthreads();

@@ -384,8 +384,31 @@ __global__ __launch_bounds__(256) void flip_out_kernel(const float* __restrict__
 // ---------------------------------------------------------------- planning
 struct HinvLayout {
   int n, np, nblk, ldz;
-  size_t off_A, off_Z, off_lam, off_flag, total;
+  size_t off_A, off_Z, off_sk, off_lam, off_flag, total;
 };
+
+struct TreeNode { int a, mid, b; };
+
+static void build_levels(int lo, int hi, int depth, std::vector<std::vector<TreeNode>>& lv) {
+  if (hi - lo <= 1) return;
+  const int mid = lo + (hi - lo) / 2;
+  if ((int)lv.size() <= depth) lv.resize(depth + 1);
+  lv[depth].push_back(TreeNode{lo, mid, hi});
+  build_levels(lo, mid, depth + 1, lv);
+  build_levels(mid, hi, depth + 1, lv);
+}
+
+// tiles and longest contraction of one launch of tree nodes [c0, c0 + cnt)
+static void tree_launch_shape(const std::vector<TreeNode>& nodes, size_t c0, int cnt, int& tiles, int& kmax) {
+  tiles = 0;
+  kmax = 0;
+  for (int i = 0; i < cnt; ++i) {
+    const TreeNode& t = nodes[c0 + i];
+    const int M = (t.mid - t.a) * kNB, N = (t.b - t.mid) * kNB;
+    tiles += gemm_tiles(M, N);
+    kmax = std::max(kmax, std::max(M, N));
+  }
+}
 
 static HinvLayout hinv_layout(int n) {
   HinvLayout L;
@@ -398,23 +421,28 @@ static HinvLayout hinv_layout(int n) {
   off = align_up(off + (size_t)L.np * L.np * sizeof(float));
   L.off_Z = off;
   off = align_up(off + (size_t)L.np * L.ldz * sizeof(float));
+  // split-K partial tiles of the tree levels that have few tiles
+  size_t sk = 0;
+  {
+    std::vector<std::vector<TreeNode>> levels;
+    build_levels(0, L.nblk, 0, levels);
+    for (const auto& nodes : levels)
+      for (size_t c0 = 0; c0 < nodes.size(); c0 += kGemmMaxGroup) {
+        const int cnt = (int)std::min<size_t>(kGemmMaxGroup, nodes.size() - c0);
+        int tiles, kmax;
+        tree_launch_shape(nodes, c0, cnt, tiles, kmax);
+        const int parts = splitk_parts(tiles, kmax);
+        if (parts > 1) sk = std::max(sk, (size_t)tiles * parts * kGT * kGT * sizeof(float));
+      }
+  }
+  L.off_sk = off;
+  off = align_up(off + sk);
   L.off_lam = off;
   off = align_up(off + sizeof(double));
   L.off_flag = off;
   off = align_up(off + sizeof(int));
   L.total = off;
   return L;
-}
-
-struct TreeNode { int a, mid, b; };
-
-static void build_levels(int lo, int hi, int depth, std::vector<std::vector<TreeNode>>& lv) {
-  if (hi - lo <= 1) return;
-  const int mid = lo + (hi - lo) / 2;
-  if ((int)lv.size() <= depth) lv.resize(depth + 1);
-  lv[depth].push_back(TreeNode{lo, mid, hi});
-  build_levels(lo, mid, depth + 1, lv);
-  build_levels(mid, hi, depth + 1, lv);
 }
 
 }  // namespace gptq
@@ -437,6 +465,7 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
   char* base = static_cast<char*>(ws);
   float* A = reinterpret_cast<float*>(base + L.off_A);
   float* Z = reinterpret_cast<float*>(base + L.off_Z);
+  float* SK = reinterpret_cast<float*>(base + L.off_sk);
   double* lam = reinterpret_cast<double*>(base + L.off_lam);
   int* flag = reinterpret_cast<int*>(base + L.off_flag);
   const int n = L.n, np = L.np, nb = L.nblk;
@@ -487,10 +516,21 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
         g2.p[i] = GemmProblem{Zn, A + (size_t)r1 * np + r1, A + (size_t)r0 * np + r1, nullptr,
                               L.ldz, np, np, M, N, N};
       }
-      launch_gemm_group<false, kStore>(g1, 1.0f, 0.0f, 1, 0, 0, nullptr, s);
-      GPTQ_LAUNCH_CHECK();
-      launch_gemm_group<false, kStore>(g2, -1.0f, 0.0f, 0, 1, 0, nullptr, s);
-      GPTQ_LAUNCH_CHECK();
+      int tiles, kmax;
+      tree_launch_shape(nodes, c0, cnt, tiles, kmax);
+      const int parts = splitk_parts(tiles, kmax);
+      if (parts > 1) {
+        // few tiles with long contractions: split them (partials in SK)
+        launch_gemm_group_splitk<false>(g1, parts, 1.0f, 0.0f, 1, 0, SK, s);
+        GPTQ_LAUNCH_CHECK();
+        launch_gemm_group_splitk<false>(g2, parts, -1.0f, 0.0f, 0, 1, SK, s);
+        GPTQ_LAUNCH_CHECK();
+      } else {
+        launch_gemm_group<false, kStore>(g1, 1.0f, 0.0f, 1, 0, 0, nullptr, s);
+        GPTQ_LAUNCH_CHECK();
+        launch_gemm_group<false, kStore>(g2, -1.0f, 0.0f, 0, 1, 0, nullptr, s);
+        GPTQ_LAUNCH_CHECK();
+      }
     }
   }
 

@@ -13,8 +13,8 @@
 //                   per workgroup; U's diagonal block in LDS; column j's
 //                   weight is broadcast across the row's lanes with DPP,
 //                   quantized, its scaled error e = (w - q)/U[j][j] pushed onto
-//                   the later columns of the block (w -= e*U[j][.]) and kept in
-//                   ErrT.
+//                   the later columns of the block (w -= e*U[j][.], in fp64)
+//                   and kept in ErrT.
 //   trailing GEMM:  W[:, b1:] -= Err * U[b0:b1, b1:] (fp32 MFMA).
 #include "gemm_f32.h"
 
@@ -65,6 +65,13 @@ GPTQ_DEV float row_bcast16(float v) {
   x = dpp_upd<0x128, (1 << (B0 ^ 2))>(x, x);
   x = dpp_upd<0x124, (1 << (B0 ^ 1)) | (1 << (B0 ^ 3))>(x, x);
   return __builtin_bit_cast(float, x);
+}
+template <int P>
+GPTQ_DEV double row_bcast16d(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_bit_cast(uint32_t, row_bcast16<P>(__builtin_bit_cast(float, (uint32_t)b)));
+  const uint32_t hi = __builtin_bit_cast(uint32_t, row_bcast16<P>(__builtin_bit_cast(float, (uint32_t)(b >> 32))));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 GPTQ_DEV float row_min16(float v) {
   v = fminf(v, dpp_f<0xB1>(v));
@@ -120,7 +127,7 @@ struct PanelArgs {
 template <int GT>
 __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
   __shared__ float4 sU4[kQB][kQS / 4][kQL];   // sU4[j][t/4][q] = U[b0+j][b0+16t+q], t..t+3
-  __shared__ float sInv[kQB];
+  __shared__ double sInv[kQB];
   __shared__ int sPerm[kQB];
 
   const int tid = threadIdx.x;
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
     }
   }
   for (int j = tid; j < kQB; j += 256) {
-    sInv[j] = (j < a.bw) ? 1.0f / a.U[(size_t)(a.b0 + j) * a.d + a.b0 + j] : 0.0f;
+    sInv[j] = (j < a.bw) ? 1.0 / (double)a.U[(size_t)(a.b0 + j) * a.d + a.b0 + j] : 0.0;
     sPerm[j] = (j < a.bw) ? a.perm[a.b0 + j] : 0;
   }
   __syncthreads();
@@ -174,9 +181,11 @@ __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
   const float* wrow = a.Wp + (size_t)rowc * a.d + a.b0;
   const int bw = a.bw;
 
-  float w[kQS];
+  // The block's running weights are kept in fp64: its 127 in-block updates
+  // are where fp32 rounding would move near-ties to the other side.
+  double w[kQS];
 #pragma unroll
-  for (int t = 0; t < kQS; ++t) w[t] = (kQL * t + q < bw) ? wrow[kQL * t + q] : 0.0f;
+  for (int t = 0; t < kQS; ++t) w[t] = (kQL * t + q < bw) ? (double)wrow[kQL * t + q] : 0.0;
 
   float scale = 1.0f, zero = 0.0f, rscale = 1.0f;
   if (GT == 0 && a.b0 % a.G != 0) {
@@ -200,16 +209,16 @@ __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
 #pragma unroll
       for (int t = I; t < I + GT / kQL; ++t) {
         if (kQL * t + q < bw) {
-          mn = fminf(mn, w[t]);
-          mx = fmaxf(mx, w[t]);
+          mn = fminf(mn, (float)w[t]);
+          mx = fmaxf(mx, (float)w[t]);
         }
       }
     } else if constexpr (GT > 0) {
       // a group inside one slot: lanes J%16 .. J%16 + GT - 1
       constexpr int L0 = J % kQL;
       if (q >= L0 && q < L0 + GT && J + (q - L0) < bw) {
-        mn = w[I];
-        mx = w[I];
+        mn = (float)w[I];
+        mx = (float)w[I];
       }
     } else {
       // J == 0: the whole block (columns < bw), then the rest of the group
@@ -217,8 +226,8 @@ __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
 #pragma unroll
       for (int t = 0; t < kQS; ++t) {
         if (kQL * t + q < bw) {
-          mn = fminf(mn, w[t]);
-          mx = fmaxf(mx, w[t]);
+          mn = fminf(mn, (float)w[t]);
+          mx = fmaxf(mx, (float)w[t]);
         }
       }
       const int gend = min(a.b0 + a.G, a.d);
@@ -250,17 +259,19 @@ __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
         if (a.b0 % a.G == 0) group_start.template operator()<0>();
       }
     }
-    const float wj = row_bcast16<P>(w[I]);
-    // correctly rounded wj/scale from the reciprocal (one residual correction)
-    const float t0 = wj * rscale;
-    const float res = fmaf(-t0, scale, wj);
+    const double wj = row_bcast16d<P>(w[I]);
+    // the code is decided in fp32: correctly rounded fp32(wj)/scale from the
+    // reciprocal (one residual correction)
+    const float wf = (float)wj;
+    const float t0 = wf * rscale;
+    const float res = fmaf(-t0, scale, wf);
     const float tq = fmaf(res, rscale, t0);
     const float c = fminf(fmaxf(rintf(tq) + zero, 0.0f), a.maxq);
-    const float qv = scale * (c - zero);
-    const float e = (wj - qv) * sInv[J];
+    const double qv = (double)scale * (double)(c - zero);    // exact
+    const double e = (wj - qv) * sInv[J];
     if (q == P) {
-      eown[I] = e;
-      qown[I] = qv;
+      eown[I] = (float)e;
+      qown[I] = (float)qv;
       cown[I >> 2] |= (uint32_t)c << (8 * (I & 3));
     }
     // w[t] -= e * U[J][16t+q] for the later columns of the block (slots t >= I;
@@ -268,10 +279,10 @@ __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
 #pragma unroll
     for (int t = (I & ~3); t < kQS; t += 4) {
       const float4 u4 = sU4[J][t >> 2][q];
-      if (t + 0 >= I) w[t + 0] = fmaf(-e, u4.x, w[t + 0]);
-      if (t + 1 >= I) w[t + 1] = fmaf(-e, u4.y, w[t + 1]);
-      if (t + 2 >= I) w[t + 2] = fmaf(-e, u4.z, w[t + 2]);
-      if (t + 3 >= I) w[t + 3] = fmaf(-e, u4.w, w[t + 3]);
+      if (t + 0 >= I) w[t + 0] = fma(-e, (double)u4.x, w[t + 0]);
+      if (t + 1 >= I) w[t + 1] = fma(-e, (double)u4.y, w[t + 1]);
+      if (t + 2 >= I) w[t + 2] = fma(-e, (double)u4.z, w[t + 2]);
+      if (t + 3 >= I) w[t + 3] = fma(-e, (double)u4.w, w[t + 3]);
     }
   };
   [&]<int... Js>(std::integer_sequence<int, Js...>) {
