@@ -137,13 +137,23 @@ def _f(x, decision):
     return np.asarray(x, dtype=np.float32 if decision == "f32" else np.float64)
 
 
-def group_params(seg: np.ndarray, maxq: int, decision: str = "f32"):
+def group_params(seg: np.ndarray, maxq: int, decision: str = "f32", sym: bool = False):
     """Per row of seg [rows, g]: scale = (max - min)/maxq, zero = rint(-min/scale).
     Returns (scale, zero) with scale in the decision precision and zero an
-    integer-valued array of the same type."""
+    integer-valued array of the same type.
+
+    sym ([P4]'s GptqConfig sym=True; the pages define no formula, the plainest
+    symmetric reading is taken): the grid spans [-m, m] with
+    m = max(|min|, |max|), scale = 2m/maxq, and the zero point is the middle
+    code (maxq + 1)/2; an all-zero group gets scale 1."""
     xmin = _f(seg.min(axis=-1), decision)
     xmax = _f(seg.max(axis=-1), decision)
     zero_t = _f(0.0, decision)
+    if sym:
+        m = np.maximum(np.abs(xmin), np.abs(xmax))
+        scale = np.where(m == zero_t, _f(1.0, decision), (m + m) / _f(maxq, decision))
+        zero = np.full_like(scale, (maxq + 1) // 2)
+        return scale.astype(xmin.dtype), zero.astype(xmin.dtype)
     deg = xmax == xmin
     xmin = np.where(deg, np.minimum(xmin, zero_t), xmin)
     xmax = np.where(deg, np.maximum(xmax, zero_t), xmax)
@@ -207,7 +217,8 @@ def prepare(H: np.ndarray, damp_percent: float = 0.01, desc_act: bool = False) -
 
 def gptq(W: np.ndarray, H: np.ndarray, *, bits: int = 4, group_size: int = 128,
          block_size: int = 128, damp_percent: float = 0.01, desc_act: bool = False,
-         decision: str = "f32", prepared: Optional[Prepared] = None) -> GPTQResult:
+         decision: str = "f32", prepared: Optional[Prepared] = None,
+         sym: bool = False) -> GPTQResult:
     """The column loop.  ``prepared`` (from ``prepare(H, damp_percent,
     desc_act)``) lets several quantizer settings share one H's order and
     factor; without it they are computed here."""
@@ -235,7 +246,7 @@ def gptq(W: np.ndarray, H: np.ndarray, *, bits: int = 4, group_size: int = 128,
         Err = np.zeros((d_out, b1 - b0), dtype=np.float64)
         for j in range(b0, b1):
             if j % G == 0:
-                s, z = group_params(Wp[:, j:min(j + G, d)], maxq, decision)
+                s, z = group_params(Wp[:, j:min(j + G, d)], maxq, decision, sym)
                 scales[:, j // G] = s
                 zeros[:, j // G] = z.astype(np.int64)
             w = Wp[:, j]
@@ -260,7 +271,7 @@ def gptq(W: np.ndarray, H: np.ndarray, *, bits: int = 4, group_size: int = 128,
 
 
 def rtn(W: np.ndarray, *, bits: int = 4, group_size: int = 128,
-        perm: Optional[np.ndarray] = None, decision: str = "f32"):
+        perm: Optional[np.ndarray] = None, decision: str = "f32", sym: bool = False):
     """Round-to-nearest baseline ([P2] section 二, the naive min-max grid; [P5]
     2.3 compares GPTQ against it): same grid and grouping, no compensation.
     Returns (codes, Q) in original column order."""
@@ -274,7 +285,7 @@ def rtn(W: np.ndarray, *, bits: int = 4, group_size: int = 128,
     Qp = np.zeros((d_out, d), dtype=np.float64)
     for g0 in range(0, d, G):
         g1 = min(g0 + G, d)
-        s, z = group_params(Wp[:, g0:g1], maxq, decision)
+        s, z = group_params(Wp[:, g0:g1], maxq, decision, sym)
         for j in range(g0, g1):
             c, q = quantize(Wp[:, j], s, z, maxq, decision)
             codes_p[:, j] = c
@@ -314,4 +325,40 @@ def unpack_int4(packed: np.ndarray, cols: int) -> np.ndarray:
     out = np.zeros((rows, cols), dtype=np.int64)
     for k in range(8):
         out[:, k::8] = (packed >> np.uint32(4 * k)) & np.uint32(0xF)
+    return out
+
+
+def pack_dense(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Dense packing of bits-wide codes (2, 3, 4 or 8): each row is one bit
+    stream, code k in bits [k*bits, (k+1)*bits) counted from the least
+    significant bit of word 0, so a 3-bit code may straddle two words
+    (3/8 byte per weight, [P5] section 1.1's accounting).  cols*bits must be
+    a multiple of 32.  At 4 bits this is pack_int4's layout."""
+    codes = np.asarray(codes, dtype=np.uint64)
+    rows, cols = codes.shape
+    assert bits in (2, 3, 4, 8) and (cols * bits) % 32 == 0
+    nw = cols * bits // 32
+    out = np.zeros((rows, nw), dtype=np.uint64)
+    mask = np.uint64((1 << bits) - 1)
+    for k in range(cols):
+        pos = k * bits
+        w, sh = pos // 32, pos % 32
+        v = codes[:, k] & mask
+        out[:, w] |= (v << np.uint64(sh)) & np.uint64(0xFFFFFFFF)
+        if sh + bits > 32:                      # the high part goes to the next word
+            out[:, w + 1] |= v >> np.uint64(32 - sh)
+    return out.astype(np.uint32)
+
+
+def unpack_dense(packed: np.ndarray, cols: int, bits: int) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint64)
+    rows = packed.shape[0]
+    out = np.zeros((rows, cols), dtype=np.int64)
+    for k in range(cols):
+        pos = k * bits
+        w, sh = pos // 32, pos % 32
+        v = packed[:, w] >> np.uint64(sh)
+        if sh + bits > 32:
+            v |= packed[:, w + 1] << np.uint64(32 - sh)
+        out[:, k] = (v & np.uint64((1 << bits) - 1)).astype(np.int64)
     return out
