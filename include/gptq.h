@@ -61,7 +61,11 @@ typedef enum {
  *  block_size    lazy-batch width; this build supports 128 only.
  *  damp_percent  lambda = damp_percent * mean(diag H) is added to diag(H).
  *  desc_act      0/1: process columns by descending diag(H).
- *  sym           0 = asymmetric min-max grid (the only mode implemented). */
+ *  sym           0 = asymmetric min-max grid: scale = (max - min)/maxq,
+ *                zero = rint(-min/scale).  1 = symmetric grid (the ms-swift
+ *                review page's sym=True; no formula is given, the plainest
+ *                reading is used): m = max(|min|, |max|), scale = 2m/maxq,
+ *                zero = (maxq + 1)/2 (scale 1 for an all-zero group). */
 typedef struct {
   int32_t bits;
   int32_t group_size;
@@ -142,6 +146,17 @@ int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_
  *  3-bit codes are stored as nibbles too. */
 int gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_t cols, uint32_t* packed,
                    hipStream_t s);
+
+/* Dense packing for 2, 3, 4 or 8 bits (practice page section 1.1 counts
+ * bits/8 byte per weight): each row is one bit stream, code k at bits
+ * [k*bits, (k+1)*bits) from the least significant bit of the row's word 0; a
+ * 3-bit code may straddle two words.  At 4 bits the layout equals
+ * gptq_pack_int4's.  Each code is masked to its low `bits` bits.
+ *  codes [rows x cols] uint8, packed [rows x cols*bits/32] uint32.
+ *  INVALID_ARG: bits not in {2, 3, 4, 8}, (cols * bits) % 32 != 0, null
+ *  pointers, negative sizes. */
+int gptq_pack_dense(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits,
+                    uint32_t* packed, hipStream_t s);
 
 /* ---------------------------------------------------------------- layer error
  * out_host[0] = ||(W - Q) X^T||_F^2 = 1/2 tr((W - Q) H (W - Q)^T) with the

@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
                                                    ctypes.POINTER(gptq_config), vp, vp, vp, vp, vp,
                                                    vp, sz, vp]),
             "gptq_pack_int4": (ctypes.c_int, [vp, i64, i64, vp, vp]),
+            "gptq_pack_dense": (ctypes.c_int, [vp, i64, i64, i32, vp, vp]),
             "gptq_layer_error_workspace_size": (sz, [i32, i32]),
             "gptq_layer_error": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, i32, i32,
                                                 ctypes.POINTER(ctypes.c_double), vp, sz, vp]),
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("gptq_hessian_workspace_size", "gptq_hessian_accumulate",
             "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
             "gptq_quantize_workspace_size", "gptq_quantize_layer", "gptq_pack_int4",
+            "gptq_pack_dense",
             "gptq_layer_error_workspace_size", "gptq_layer_error", "gptq_status_string",
             "gptq_abi_version")
 
@@ -187,6 +189,14 @@ def gptq_pack_int4(codes: torch.Tensor, packed: torch.Tensor, stream=None) -> No
     assert packed.dtype == torch.int32 or packed.dtype == torch.uint32
     _check(lib().gptq_pack_int4(_ptr(codes), rows, cols, _ptr(packed), _stream(stream)),
            "gptq_pack_int4")
+
+
+def gptq_pack_dense(codes: torch.Tensor, packed: torch.Tensor, bits: int, stream=None) -> None:
+    _dev(codes, "codes"); _dev(packed, "packed")
+    rows, cols = codes.shape
+    assert packed.dtype == torch.int32 or packed.dtype == torch.uint32
+    _check(lib().gptq_pack_dense(_ptr(codes), rows, cols, int(bits), _ptr(packed), _stream(stream)),
+           "gptq_pack_dense")
 
 
 def gptq_layer_error_workspace_size(d_out: int, d_in: int) -> int:

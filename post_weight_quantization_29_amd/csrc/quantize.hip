@@ -115,6 +115,7 @@ struct PanelArgs {
   int* zeros;
   float* ErrT;          // [128 x d_out]
   int d_out, d, b0, bw, G, ng;
+  int sym;
   float maxq;
 };
 
@@ -240,7 +241,14 @@ __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
     }
     mn = row_min16(mn);
     mx = row_max16(mx);
-    grid_params(mn, mx, a.maxq, scale, zero);
+    if (a.sym) {
+      // symmetric: [-m, m], the middle code is zero
+      const float m = fmaxf(fabsf(mn), fabsf(mx));
+      scale = (m == 0.0f) ? 1.0f : (m + m) / a.maxq;
+      zero = 0.5f * (a.maxq + 1.0f);
+    } else {
+      grid_params(mn, mx, a.maxq, scale, zero);
+    }
     rscale = 1.0f / scale;
     const int gi = (GT > 0) ? (a.b0 + J) / GT : a.b0 / a.G;
     if (rv && q == 0) {
@@ -339,6 +347,28 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const uint8_t* __restric
   }
 }
 
+// dense packing: one thread per output word; word w of a row holds bits
+// [32w, 32w + 32) of the row's stream, i.e. codes floor(32w/bits) ..
+// floor((32w + 31)/bits), the first and last possibly in part.
+__global__ __launch_bounds__(256) void pack_dense_kernel(const uint8_t* __restrict__ codes, int64_t rows,
+                                                         int64_t cols, int bits, int64_t nw,
+                                                         uint32_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * nw) return;
+  const int64_t r = idx / nw, w = idx - r * nw;
+  const uint8_t* row = codes + r * cols;
+  const int64_t bit0 = 32 * w;
+  const int64_t k0 = bit0 / bits, k1 = (bit0 + 31) / bits;
+  const uint32_t mask = (1u << bits) - 1u;
+  uint64_t acc = 0;
+  for (int64_t k = k0; k <= k1; ++k) {
+    const uint64_t v = (uint64_t)(row[k] & mask);
+    const int64_t pos = k * bits - bit0;         // -bits < pos < 32
+    acc |= (pos >= 0) ? (v << pos) : (v >> (-pos));
+  }
+  out[idx] = (uint32_t)acc;
+}
+
 // ---------------------------------------------------------------- planning
 struct QuantLayout {
   size_t off_wp, off_err, total;
@@ -363,7 +393,6 @@ static int check_config(const gptq_config* c, int d) {
   const int G = c->group_size;
   if (G != -1 && G <= 0) return GPTQ_ERR_INVALID_ARG;
   if (c->block_size != kQB) return GPTQ_ERR_UNSUPPORTED;
-  if (c->sym != 0) return GPTQ_ERR_UNSUPPORTED;
   if (G != -1) {
     const bool inside = (kQB % G == 0) && (G % 4 == 0);
     const bool spans = (G % kQB == 0);
@@ -415,6 +444,7 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   pa.scales = scales; pa.zeros = zeros; pa.ErrT = ErrT;
   pa.d_out = d_out; pa.d = d; pa.G = G; pa.ng = ng;
   pa.maxq = (float)((1 << cfg->bits) - 1);
+  pa.sym = cfg->sym;
   const int nrow_blocks = (d_out + kQRows - 1) / kQRows;
   // in-block group sizes are compile-time; wider groups (or one per row) use 0
   const int gt = (G <= kQB && kQB % G == 0 && G % 4 == 0) ? G : 0;
@@ -453,6 +483,21 @@ extern "C" int gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_t cols, 
   const int64_t nq = std::max<int64_t>(1, nwords / 4);
   const int blocks = (int)std::min<int64_t>((nq + 255) / 256, 8192);
   pack_int4_kernel<<<blocks, 256, 0, s>>>(codes, nwords, packed);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+extern "C" int gptq_pack_dense(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits,
+                               uint32_t* packed, hipStream_t s) {
+  if (!codes || !packed || rows < 0 || cols < 0) return GPTQ_ERR_INVALID_ARG;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_ERR_INVALID_ARG;
+  if ((cols * bits) % 32 != 0) return GPTQ_ERR_INVALID_ARG;
+  const int64_t nw = cols * bits / 32;
+  const int64_t total = rows * nw;
+  if (total == 0) return GPTQ_OK;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7fffffff) return GPTQ_ERR_INVALID_ARG;
+  pack_dense_kernel<<<(unsigned)blocks, 256, 0, s>>>(codes, rows, cols, bits, nw, packed);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }

@@ -75,8 +75,13 @@ def test_argument_validation_before_any_launch(L):
     assert q(P.make_config(bits=9)) == P._lib.ERR_INVALID_ARG
     assert q(P.make_config(group_size=96)) == P._lib.ERR_INVALID_ARG
     assert q(P.make_config(group_size=0)) == P._lib.ERR_INVALID_ARG
-    assert q(P.make_config(sym=1)) == P._lib.ERR_UNSUPPORTED
+    assert q(P.make_config(sym=2)) == P._lib.ERR_INVALID_ARG
     assert q(P.make_config(block_size=64)) == P._lib.ERR_UNSUPPORTED
+    # dense packing: bit widths, whole words per row, null pointers
+    assert L.gptq_pack_dense(fake, 4, 32, 5, fake, None) == P._lib.ERR_INVALID_ARG
+    assert L.gptq_pack_dense(fake, 4, 40, 3, fake, None) == P._lib.ERR_INVALID_ARG
+    assert L.gptq_pack_dense(None, 4, 32, 3, fake, None) == P._lib.ERR_INVALID_ARG
+    assert L.gptq_pack_dense(fake, 0, 32, 3, fake, None) == P._lib.OK
     # layer error: null output pointer
     assert L.gptq_layer_error(fake, fake, 1, fake, 4, 8, None, fake, 1 << 20, None) == P._lib.ERR_INVALID_ARG
 
