@@ -362,3 +362,25 @@ def unpack_dense(packed: np.ndarray, cols: int, bits: int) -> np.ndarray:
             v |= packed[:, w + 1] << np.uint64(32 - sh)
         out[:, k] = (v & np.uint64((1 << bits) - 1)).astype(np.int64)
     return out
+
+
+# ----------------------------------------------------------------------------
+# 7. using the packed layer: y = x W_q^T  ([P5] 4.3: at inference the 4-bit
+#    weights are dequantized to 16-bit and multiplied; the saving is in the
+#    bytes moved)
+# ----------------------------------------------------------------------------
+
+def dequantize(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, g_idx: np.ndarray,
+               cols: int) -> np.ndarray:
+    """W_q[r][c] = scales[r][g_idx[c]] * (code[r][c] - zeros[r][g_idx[c]]), float64,
+    codes from pack_int4's layout."""
+    codes = unpack_int4(packed, cols).astype(np.float64)
+    g = np.asarray(g_idx, dtype=np.int64)
+    return np.asarray(scales, np.float64)[:, g] * (codes - np.asarray(zeros, np.float64)[:, g])
+
+
+def w4a16_matmul(X: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                 g_idx: np.ndarray) -> np.ndarray:
+    """Y [m x d_out] = X [m x d_in] @ W_q^T in float64."""
+    X64 = np.asarray(X, dtype=np.float64)
+    return X64 @ dequantize(packed, scales, zeros, g_idx, X64.shape[1]).T

@@ -406,3 +406,22 @@ def test_pack_dense_layouts():
         p = o.pack_dense(r, bits)
         assert p.nbytes * 8 == r.size * bits             # bits/8 byte per weight
         assert np.array_equal(o.unpack_dense(p, cols, bits), r)
+
+
+# ---------------------------------------------------------------- using the packed layer
+
+def test_w4a16_matmul_equals_dequantized_gptq_output():
+    """The packed codes + scales/zeros/g_idx of a GPTQ run dequantize to its Q
+    exactly, and the product is X Q^T (element loops on a tiny case)."""
+    W, X = _case(12, 64, 300, seed=51, outlier_frac=0.05, outlier_factor=20.0)
+    H = o.hessian([X], 64)
+    r = o.gptq(W, H, bits=4, group_size=16, block_size=32, desc_act=True)
+    packed = o.pack_int4(r.codes)
+    Wq = o.dequantize(packed, r.scales, r.zeros, r.g_idx, 64)
+    np.testing.assert_array_equal(Wq, r.Q)
+    x = X[:3]
+    Y = o.w4a16_matmul(x, packed, r.scales, r.zeros, r.g_idx)
+    for i in range(3):
+        for j in range(12):
+            ref = sum(x[i, c] * r.Q[j, c] for c in range(64))
+            assert Y[i, j] == pytest.approx(ref, rel=1e-12, abs=1e-15)
