@@ -379,8 +379,34 @@ def dequantize(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, g_idx:
     return np.asarray(scales, np.float64)[:, g] * (codes - np.asarray(zeros, np.float64)[:, g])
 
 
+def _round16(a32: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> nearest (ties to even) 16-bit value of dtype, as float64."""
+    a32 = np.asarray(a32, dtype=np.float32)
+    if dtype == "f16":
+        return a32.astype(np.float16).astype(np.float64)
+    u = a32.view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return (r.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def dequantize16(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, g_idx: np.ndarray,
+                 cols: int, dtype: str) -> np.ndarray:
+    """The weights as the product uses them: [P5] 4.3 has the 4-bit weights
+    dequantized to a 16-bit type first.  Each is the float32 product
+    scale * (code - zero) rounded to dtype ("f16" or "bf16")."""
+    codes = unpack_int4(packed, cols)
+    g = np.asarray(g_idx, dtype=np.int64)
+    s32 = np.asarray(scales, dtype=np.float32)[:, g]
+    cz = (codes - np.asarray(zeros, dtype=np.int64)[:, g]).astype(np.float32)
+    return _round16(s32 * cz, dtype)
+
+
 def w4a16_matmul(X: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
-                 g_idx: np.ndarray) -> np.ndarray:
-    """Y [m x d_out] = X [m x d_in] @ W_q^T in float64."""
+                 g_idx: np.ndarray, dtype: Optional[str] = None) -> np.ndarray:
+    """Y [m x d_out] = X [m x d_in] @ W^T in float64, W = dequantize (dtype None)
+    or dequantize16 (dtype "f16"/"bf16")."""
     X64 = np.asarray(X, dtype=np.float64)
-    return X64 @ dequantize(packed, scales, zeros, g_idx, X64.shape[1]).T
+    d_in = X64.shape[1]
+    Wd = (dequantize(packed, scales, zeros, g_idx, d_in) if dtype is None
+          else dequantize16(packed, scales, zeros, g_idx, d_in, dtype))
+    return X64 @ Wd.T

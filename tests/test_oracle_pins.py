@@ -425,3 +425,22 @@ def test_w4a16_matmul_equals_dequantized_gptq_output():
         for j in range(12):
             ref = sum(x[i, c] * r.Q[j, c] for c in range(64))
             assert Y[i, j] == pytest.approx(ref, rel=1e-12, abs=1e-15)
+
+
+def test_dequantize16_rounding():
+    """scale * (code - zero) in float32, then ties-to-even to the 16-bit type."""
+    packed = o.pack_int4(np.array([[3, 0, 15, 8, 1, 2, 4, 5]]))
+    g = np.zeros(8, dtype=np.int64)
+    s = np.array([[1.0 + 2.0 ** -8]], dtype=np.float32)      # one bf16 ulp above 1 is 2^-7
+    z = np.array([[1]])
+    w = o.dequantize16(packed, s, z, g, 8, "bf16")[0]
+    # code 3: 2*(1+2^-8) = 2 + 2^-7 is a tie between 2 and 2 + 2^-6 -> even -> 2
+    assert w[0] == 2.0
+    # code 0: -(1+2^-8): tie between -1 and -(1+2^-7) -> even -> -1
+    assert w[1] == -1.0
+    # code 15: 14*(1+2^-8) = 14 + 14/256 -> nearest bf16 step (1/16 at 14) -> 14.0625
+    assert w[2] == 14.0625
+    wf = o.dequantize16(packed, s, z, g, 8, "f16")[0]
+    assert wf[0] == np.float64(np.float16(2.0 + 2.0 ** -7))
+    np.testing.assert_array_equal(o.dequantize16(packed, np.array([[0.5]], np.float32), z, g, 8, "bf16"),
+                                  o.dequantize(packed, np.array([[0.5]]), z, g, 8))
