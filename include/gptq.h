@@ -158,6 +158,26 @@ int gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_t cols, uint32_t* p
 int gptq_pack_dense(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits,
                     uint32_t* packed, hipStream_t s);
 
+/* ---------------------------------------------------------------- using the packed layer
+ * Y = X W^T with W dequantized from the packed 4-bit layer (practice page
+ * section 4.3: at inference the 4-bit weights are dequantized to a 16-bit type,
+ * then multiplied).  W[r][c] = round16(scales[r][g] * (code[r][c] - zeros[r][g])),
+ * the product taken in fp32 and rounded (ties to even) to x_dtype, with
+ * code[r][c] = (packed[r][c/8] >> 4(c%8)) & 15 and g = g_idx[c] (clamped to
+ * [0, n_groups)), or, with g_idx NULL, g = c / group_size (group_size a
+ * multiple of 8, or -1 for one group per row).  Products accumulate in fp32;
+ * Y is rounded once to y_dtype.
+ *  X [m x d_in] f16/bf16 row-major, 16-byte aligned; packed [d_out x d_in/8]
+ *  uint32; scales [d_out x n_groups] fp32; zeros [d_out x n_groups] int32;
+ *  Y [m x d_out] of y_dtype (F32, F16 or BF16).  d_in % 8 == 0.
+ *  INVALID_ARG: null pointers, bad sizes or dtypes, misaligned X, with g_idx
+ *  NULL a group size that is not a multiple of 8 or an n_groups that does not
+ *  match it. */
+int gptq_w4a16_gemm(const void* X, gptq_dtype x_dtype, int64_t m, int32_t d_in,
+                    const uint32_t* packed, const float* scales, const int32_t* zeros,
+                    const int32_t* g_idx, int32_t group_size, int32_t n_groups, int32_t d_out,
+                    void* Y, gptq_dtype y_dtype, hipStream_t s);
+
 /* ---------------------------------------------------------------- layer error
  * out_host[0] = ||(W - Q) X^T||_F^2 = 1/2 tr((W - Q) H (W - Q)^T) with the
  * undamped H (practice page section 5.5: measure the loss, do not eyeball it).

@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     EXPORTED, GPTQError, LIB_PATH, NotPositiveDefinite, gptq_abi_version, gptq_config,
     gptq_hessian_accumulate, gptq_hessian_workspace_size, gptq_layer_error,
     gptq_layer_error_workspace_size, gptq_pack_dense, gptq_pack_int4, gptq_prepare_hinv,
+    gptq_w4a16_gemm,
     gptq_prepare_hinv_workspace_size, gptq_quantize_layer, gptq_quantize_workspace_size,
     gptq_status_string, lib, make_config,
 )

@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
                                                    vp, sz, vp]),
             "gptq_pack_int4": (ctypes.c_int, [vp, i64, i64, vp, vp]),
             "gptq_pack_dense": (ctypes.c_int, [vp, i64, i64, i32, vp, vp]),
+            "gptq_w4a16_gemm": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, vp, vp, vp, vp, i32, i32,
+                                               i32, vp, ctypes.c_int, vp]),
             "gptq_layer_error_workspace_size": (sz, [i32, i32]),
             "gptq_layer_error": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, i32, i32,
                                                 ctypes.POINTER(ctypes.c_double), vp, sz, vp]),
@@ -76,7 +78,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("gptq_hessian_workspace_size", "gptq_hessian_accumulate",
             "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
             "gptq_quantize_workspace_size", "gptq_quantize_layer", "gptq_pack_int4",
-            "gptq_pack_dense",
+            "gptq_pack_dense", "gptq_w4a16_gemm",
             "gptq_layer_error_workspace_size", "gptq_layer_error", "gptq_status_string",
             "gptq_abi_version")
 
@@ -197,6 +199,22 @@ def gptq_pack_dense(codes: torch.Tensor, packed: torch.Tensor, bits: int, stream
     assert packed.dtype == torch.int32 or packed.dtype == torch.uint32
     _check(lib().gptq_pack_dense(_ptr(codes), rows, cols, int(bits), _ptr(packed), _stream(stream)),
            "gptq_pack_dense")
+
+
+def gptq_w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                    Y: torch.Tensor, g_idx: Optional[torch.Tensor] = None, group_size: int = 128,
+                    stream=None) -> None:
+    for t, n in ((X, "X"), (packed, "packed"), (scales, "scales"), (zeros, "zeros"), (Y, "Y")):
+        _dev(t, n)
+    m, d_in = X.shape
+    d_out, n_groups = scales.shape
+    assert Y.shape == (m, d_out) and zeros.shape == scales.shape
+    if g_idx is not None:
+        _dev(g_idx, "g_idx")
+    _check(lib().gptq_w4a16_gemm(_ptr(X), _DTYPE[X.dtype], m, d_in, _ptr(packed), _ptr(scales),
+                                 _ptr(zeros), _ptr(g_idx) if g_idx is not None else None,
+                                 int(group_size), n_groups, d_out, _ptr(Y), _DTYPE[Y.dtype],
+                                 _stream(stream)), "gptq_w4a16_gemm")
 
 
 def gptq_layer_error_workspace_size(d_out: int, d_in: int) -> int:
