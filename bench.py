@@ -114,6 +114,50 @@ def cpu_baseline(W, X, wl, args):
     }
 
 
+def w4a16_measure(P, torch, packed, scales, zeros, group_size, reps=24):
+    """Decode-shaped product on packed layers (one activation row, bf16 in, fp32
+    out): the quantized layer of this step, and a 70B down_proj-shaped packed
+    layer (8192 x 28672, random codes) for the HBM roofline.  The large layer
+    is held in three copies used in turn, 3 x 132 MB, more than the 256 MB
+    last-level cache, so each call streams its weights from HBM.  HIP events
+    on the launch stream, mean over reps after a warm-up."""
+    out = []
+    dev = packed.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    big_rows, big_cols, G = 8192, 28672, 128
+
+    def layer():
+        return (torch.randint(-2**31, 2**31 - 1, (big_rows, big_cols // 8), dtype=torch.int32,
+                              device=dev, generator=g),
+                torch.rand((big_rows, big_cols // G), device=dev, generator=g) * 0.01 + 1e-3,
+                torch.randint(0, 16, (big_rows, big_cols // G), dtype=torch.int32, device=dev,
+                              generator=g))
+
+    stream = torch.cuda.current_stream()
+    for copies, gs in (([(packed, scales, zeros)], group_size), ([layer() for _ in range(3)], G)):
+        pk, sc, zr = copies[0]
+        d_out, d_in = pk.shape[0], pk.shape[1] * 8
+        X = torch.randn((1, d_in), device=dev, generator=g).to(torch.bfloat16)
+        Y = torch.empty((1, d_out), dtype=torch.float32, device=dev)
+        for c in copies:
+            P.gptq_w4a16_gemm(X, c[0], c[1], c[2], Y, group_size=gs)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            c = copies[i % len(copies)]
+            P.gptq_w4a16_gemm(X, c[0], c[1], c[2], Y, group_size=gs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = pk.numel() * 4 + sc.numel() * 4 + zr.numel() * 4 + X.numel() * 2 + Y.numel() * 4
+        out.append({"shape": f"{d_out}x{d_in}", "m": 1, "us": round(us, 2), "bytes": nbytes,
+                    "GB_per_s": round(nbytes / us / 1e3, 1),
+                    "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)})
+        del copies
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -250,6 +294,7 @@ def main():
                                 "+ diag_reduce_kernel"),
                      "work_per_launch": f"N*d*(d+1) = {h_flops:.4g} flop"},
     }
+    out["w4a16_decode"] = w4a16_measure(P, torch, packed, scales, zeros, q.group_size)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(W, X, wl, args)

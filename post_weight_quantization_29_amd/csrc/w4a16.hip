@@ -3,103 +3,183 @@
 // and then multiplied; what the 4 bits save is the bytes moved, so at small
 // batch this product is bound by HBM).
 //
-// One wave per output row r: each lane streams words of the row's packed codes
-// (8 codes per word, the gptq_pack_int4 layout), forms each weight as the fp32
-// product scale * (code - zero) rounded to the activation's 16-bit type, and
-// multiplies it with up to 8 activation rows at a time, accumulating in fp32;
-// a wave reduction finishes each dot product.
+// RPW output rows per wave (1 for one or two activation rows, where the
+// weight stream alone sets the pace, else 4): each lane streams 16-byte groups
+// of the rows' packed codes (8 codes per word, the gptq_pack_int4 layout), forms each weight
+// as the fp32 product scale * (code - zero) (the code made an exact float by
+// OR-ing it into the mantissa of 2^23), rounds pairs of them to the
+// activation's 16-bit type with one packed conversion, and multiplies them
+// with up to 8 activation rows at a time with the 2-term dot instruction
+// (fp32 accumulation); a wave reduction finishes each dot product.  Each
+// activation chunk is loaded once per wave and serves all RPW rows.
 #include "common.h"
 
 namespace gptq {
 
 constexpr int kWRows = 8;   // activation rows per pass over the weights
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Per activation type: a pair of dequantized fp32 weights rounded (ties to
+// even) into the type's packed pair, and the 2-term dot product with fp32
+// accumulation.
 template <typename T> struct Act;
 template <> struct Act<__bf16> {
-  static GPTQ_DEV float to_f(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
-  static GPTQ_DEV float round16(float x) {     // ties to even
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
-    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
-    return __builtin_bit_cast(float, u);
+  typedef bf16x2_t v2;
+  static GPTQ_DEV v2 pack(float a, float b) {
+    v2 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return r;
+  }
+  static GPTQ_DEV float dot2(uint32_t x, v2 w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2, x), w, acc, false);
   }
 };
 template <> struct Act<_Float16> {
-  static GPTQ_DEV float to_f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
-  static GPTQ_DEV float round16(float x) { return (float)(_Float16)x; }
+  typedef f16x2_t v2;
+  static GPTQ_DEV v2 pack(float a, float b) {
+    v2 r;
+    r[0] = (_Float16)a;
+    r[1] = (_Float16)b;
+    return r;
+  }
+  static GPTQ_DEV float dot2(uint32_t x, v2 w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2, x), w, acc, false);
+  }
 };
 
 template <typename TY> GPTQ_DEV TY out_cast(float v);
 template <> GPTQ_DEV float out_cast<float>(float v) { return v; }
-template <> GPTQ_DEV __bf16 out_cast<__bf16>(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, Act<__bf16>::round16(v));
-  return __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
-}
+template <> GPTQ_DEV __bf16 out_cast<__bf16>(float v) { return (__bf16)v; }
 template <> GPTQ_DEV _Float16 out_cast<_Float16>(float v) { return (_Float16)v; }
+
+// code k of word p as an exact float: 2^23 + code is 0x4B000000 | code, and
+// subtracting 2^23 + zero leaves code - zero exactly
+GPTQ_DEV float code_minus_zero(uint32_t p, int k, float zb) {
+  return __builtin_bit_cast(float, ((p >> (4 * k)) & 15u) | 0x4B000000u) - zb;
+}
+
+// The eight weights of word p, in packed pairs.  NATURAL: one group for the
+// word (scale s, zb = 2^23 + zero); otherwise a group per code from g_idx.
+template <typename T, bool NATURAL>
+GPTQ_DEV void dequant_word(uint32_t p, int c0, float s, float zb, const float* srow, const int32_t* zrow,
+                           const int32_t* g_idx, int ng, typename Act<T>::v2 (&w)[4]) {
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (NATURAL) {
+      v[k] = s * code_minus_zero(p, k, zb);
+    } else {
+      const int g = min(max(g_idx[c0 + k], 0), ng - 1);
+      v[k] = srow[g] * code_minus_zero(p, k, 8388608.0f + (float)zrow[g]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = Act<T>::pack(v[2 * j], v[2 * j + 1]);
+}
 
 // NATURAL: column c is in group c / G (G a multiple of 8, so a word's eight
 // codes share a group); otherwise group g_idx[c], clamped to [0, ng).
-template <typename T, typename TY, bool NATURAL>
+// WPL words (8 codes each) per lane per step: 4 when the rows allow 16-byte
+// loads, else 1.  Wave w of block b takes output rows RPW(4b + w) .. +RPW-1;
+// the step's weights of all RPW rows are dequantized into registers first,
+// then each activation row's chunk is loaded once and dotted with all of them.
+template <typename T, typename TY, bool NATURAL, int WPL, int RPW>
 __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__ X, int64_t m, int d_in,
                                                     const uint32_t* __restrict__ packed,
                                                     const float* __restrict__ scales,
                                                     const int32_t* __restrict__ zeros,
                                                     const int32_t* __restrict__ g_idx, int G, int ng,
                                                     int d_out, TY* __restrict__ Y) {
+  typedef typename Act<T>::v2 v2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = blockIdx.x * 4 + wave;
-  if (r >= d_out) return;
+  const int r0 = (blockIdx.x * 4 + wave) * RPW;
+  if (r0 >= d_out) return;
   const int nw = d_in >> 3;
-  const uint32_t* prow = packed + (size_t)r * nw;
-  const float* srow = scales + (size_t)r * ng;
-  const int32_t* zrow = zeros + (size_t)r * ng;
   const float invG = 1.0f / (float)G;
   for (int64_t m0 = 0; m0 < m; m0 += kWRows) {
     const int mc = (int)min<int64_t>(kWRows, m - m0);
     const uint16_t* xb = X + m0 * d_in;
-    float acc[kWRows];
+    float acc[RPW][kWRows];
 #pragma unroll
-    for (int i = 0; i < kWRows; ++i) acc[i] = 0.0f;
-#pragma unroll 4
-    for (int q = lane; q < nw; q += 64) {
-      const uint32_t p = prow[q];
-      const int c0 = q * 8;
-      float w[8];
-      if (NATURAL) {
-        int g = (int)((float)c0 * invG);          // exact quotient after one correction
-        if (g * G > c0) --g;
-        if ((g + 1) * G <= c0) ++g;
-        const float s = srow[g], z = (float)zrow[g];
+    for (int j = 0; j < RPW; ++j)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) w[k] = Act<T>::round16(s * ((float)((p >> (4 * k)) & 15u) - z));
-      } else {
+      for (int i = 0; i < kWRows; ++i) acc[j][i] = 0.0f;
+    for (int q = lane * WPL; q < nw; q += 64 * WPL) {
+      v2 w[RPW][WPL][4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int g = min(max(g_idx[c0 + k], 0), ng - 1);
-          w[k] = Act<T>::round16(srow[g] * ((float)((p >> (4 * k)) & 15u) - (float)zrow[g]));
+      for (int j = 0; j < RPW; ++j) {
+        const int r = min(r0 + j, d_out - 1);       // rows past the end: computed, not stored
+        const uint32_t* prow = packed + (size_t)r * nw;
+        uint32_t pw[WPL];
+        if (WPL == 4) {
+          const uint4 p4 = *reinterpret_cast<const uint4*>(prow + q);
+          pw[0] = p4.x; pw[WPL > 1 ? 1 : 0] = p4.y; pw[WPL > 2 ? 2 : 0] = p4.z; pw[WPL > 3 ? 3 : 0] = p4.w;
+        } else {
+          pw[0] = prow[q];
+        }
+        const float* srow = scales + (size_t)r * ng;
+        const int32_t* zrow = zeros + (size_t)r * ng;
+#pragma unroll
+        for (int u = 0; u < WPL; ++u) {
+          const int c0 = (q + u) * 8;
+          float sc = 0.0f, zb = 0.0f;
+          if (NATURAL) {
+            int g = (int)((float)c0 * invG);      // exact quotient after one correction
+            if (g * G > c0) --g;
+            if ((g + 1) * G <= c0) ++g;
+            sc = srow[g];
+            zb = 8388608.0f + (float)zrow[g];
+          }
+          dequant_word<T, NATURAL>(pw[u], c0, sc, zb, srow, zrow, g_idx, ng, w[j][u]);
         }
       }
 #pragma unroll
       for (int i = 0; i < kWRows; ++i) {
         if (i < mc) {
-          const uint4 xv = *reinterpret_cast<const uint4*>(xb + (size_t)i * d_in + c0);
-          const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-          float a = acc[i];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            a = fmaf(Act<T>::to_f(xs[k] & 0xFFFFu), w[2 * k], a);
-            a = fmaf(Act<T>::to_f(xs[k] >> 16), w[2 * k + 1], a);
+          for (int u = 0; u < WPL; ++u) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(xb + (size_t)i * d_in + (q + u) * 8);
+#pragma unroll
+            for (int j = 0; j < RPW; ++j) {
+              float a = acc[j][i];
+              a = Act<T>::dot2(xv.x, w[j][u][0], a);
+              a = Act<T>::dot2(xv.y, w[j][u][1], a);
+              a = Act<T>::dot2(xv.z, w[j][u][2], a);
+              a = Act<T>::dot2(xv.w, w[j][u][3], a);
+              acc[j][i] = a;
+            }
           }
-          acc[i] = a;
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < kWRows; ++i) {
-      float v = acc[i];
+    for (int j = 0; j < RPW; ++j)
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0 && i < mc) Y[(size_t)(m0 + i) * d_out + r] = out_cast<TY>(v);
-    }
+      for (int i = 0; i < kWRows; ++i) {
+        float v = acc[j][i];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0 && i < mc && r0 + j < d_out) Y[(size_t)(m0 + i) * d_out + r0 + j] = out_cast<TY>(v);
+      }
+  }
+}
+
+template <typename T, typename TY, int RPW>
+static void launch_w4a16_rpw(const uint16_t* x, int64_t m, int d_in, const uint32_t* packed, const float* scales,
+                             const int32_t* zeros, const int32_t* g_idx, int G, int ng, int d_out, TY* y,
+                             hipStream_t s) {
+  const unsigned grid = (unsigned)((d_out + 4 * RPW - 1) / (4 * RPW));
+  // 16-byte packed loads when every row starts 16-byte aligned
+  const bool vec = ((d_in / 8) % 4 == 0) && (reinterpret_cast<uintptr_t>(packed) & 15) == 0;
+  if (g_idx) {
+    if (vec) w4a16_kernel<T, TY, false, 4, RPW><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y);
+    else w4a16_kernel<T, TY, false, 1, RPW><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y);
+  } else {
+    if (vec) w4a16_kernel<T, TY, true, 4, RPW><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, nullptr, G, ng, d_out, y);
+    else w4a16_kernel<T, TY, true, 1, RPW><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, nullptr, G, ng, d_out, y);
   }
 }
 
@@ -107,14 +187,10 @@ template <typename T, typename TY>
 static void launch_w4a16(const void* X, int64_t m, int d_in, const uint32_t* packed, const float* scales,
                          const int32_t* zeros, const int32_t* g_idx, int G, int ng, int d_out, void* Y,
                          hipStream_t s) {
-  const unsigned grid = (unsigned)((d_out + 3) / 4);
   const uint16_t* x = static_cast<const uint16_t*>(X);
-  if (g_idx)
-    w4a16_kernel<T, TY, false><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out,
-                                                    static_cast<TY*>(Y));
-  else
-    w4a16_kernel<T, TY, true><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, nullptr, G, ng, d_out,
-                                                   static_cast<TY*>(Y));
+  TY* y = static_cast<TY*>(Y);
+  if (m <= 2) launch_w4a16_rpw<T, TY, 1>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y, s);
+  else launch_w4a16_rpw<T, TY, 4>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y, s);
 }
 
 }  // namespace gptq
