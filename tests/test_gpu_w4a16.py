@@ -102,6 +102,27 @@ def test_w4a16_70b_down_proj_shape_sampled_rows():
     _check(Y.cpu().numpy()[:, rows].astype(np.float64), Yref, bound, "f32")
 
 
+def test_w4a16_70b_gate_proj_shape_batch16_sampled_rows():
+    """28672 x 8192 with contiguous groups and 16 activation rows (four output
+    rows per wave, each activation load shared by them)."""
+    import post_weight_quantization_29_amd as P
+    d_out, d_in, G, m = 28672, 8192, 128, 16
+    packed, scales, zeros, g_idx = _layer(d_out, d_in, G, 0, seed=79)
+    rng = np.random.default_rng(80)
+    X = gi.cast_storage(rng.standard_normal((m, d_in)).astype(np.float32), "bf16")
+    Y = torch.empty((m, d_out), dtype=torch.bfloat16, device="cuda")
+    P.gptq_w4a16_gemm(to_dev(X, "bf16"), torch.from_numpy(packed.view(np.int32)).cuda(),
+                      torch.from_numpy(scales).cuda(), torch.from_numpy(zeros).cuda(), Y,
+                      group_size=G)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(d_out, 96, replace=False))
+    X64 = gi.to_float64(X, "bf16")
+    Yref = o.w4a16_matmul(X64, packed[rows], scales[rows], zeros[rows], g_idx, dtype="bf16")
+    bound = np.abs(X64) @ np.abs(o.dequantize16(packed[rows], scales[rows], zeros[rows], g_idx, d_in,
+                                               "bf16")).T
+    _check(Y.float().cpu().numpy()[:, rows].astype(np.float64), Yref, bound, "bf16")
+
+
 def test_w4a16_end_to_end_small_layer():
     """Quantize, pack and multiply on each side (the 256 x 256 workload)."""
     import post_weight_quantization_29_amd as P
