@@ -16,11 +16,20 @@
  *
  * Conventions shared by every call:
  *  - Pointers are device pointers owned by the caller, except out_host in
- *    gptq_layer_error, which is host memory.  The library keeps no state and
- *    allocates no device memory; scratch memory comes in through ws/ws_bytes,
- *    sized by the matching *_workspace_size query.  Workspaces need 256-byte
- *    alignment (any hipMalloc / torch allocation satisfies this).
- *  - All work is enqueued on stream s, in stream order.  Only
+ *    gptq_layer_error, which is host memory.  The library allocates no device
+ *    memory; scratch memory comes in through ws/ws_bytes, sized by the
+ *    matching *_workspace_size query.  Workspaces need 256-byte alignment
+ *    (any hipMalloc / torch allocation satisfies this).  Its only state is,
+ *    per device, one extra stream and two events, created on first use.
+ *  - All work is ordered on stream s: it starts after the work already on s
+ *    and is complete, as seen from s, before anything enqueued on s later.
+ *    gptq_quantize_layer, for layers of 2^25 weights or more, puts part of
+ *    its blocked loop on the device's extra stream (a trailing update
+ *    overlapping the next block's panel), ordered against s with events and
+ *    joined back to s before it returns; the results are the same bit for
+ *    bit as on one stream (GPTQ_LOOKAHEAD=0 in the environment keeps
+ *    everything on s).
+ *    The enqueue of such a call holds a per-device lock.  Only
  *    gptq_prepare_hinv and gptq_layer_error synchronize s (to read one
  *    device flag or scalar).
  *  - Argument errors return GPTQ_ERR_INVALID_ARG (or GPTQ_ERR_WORKSPACE)

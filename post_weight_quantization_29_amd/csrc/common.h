@@ -21,7 +21,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 namespace gptq {
 
-// hipError_t -> status, remembering nothing (the library is stateless)
+// hipError_t -> status (no error state is kept between calls)
 #define GPTQ_HIP_TRY(expr)                                  \
   do {                                                      \
     hipError_t e_ = (expr);                                 \
