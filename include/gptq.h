@@ -198,6 +198,55 @@ int gptq_layer_error(const float* H, const void* W, gptq_dtype w_dtype, const fl
                      int32_t d_out, int32_t d_in, double* out_host, void* ws, size_t ws_bytes,
                      hipStream_t s);
 
+/* ---------------------------------------------------------------- AWQ
+ * Activation-aware weight quantization, the second method of the pages
+ * ("GPTQ/AWQ量化导出：让大模型在消费级显卡上跑起来", its AWQ steps: per-channel RMS
+ * of the calibration activations, the top 5 % of channels get a larger factor,
+ * the factor is undone at inference; "大模型压缩量化技术：GPTQ 与 AWQ 原理详解 +
+ * Python 实战教程" section 四: weights of the large-activation channels times
+ * s > 1, quantize, activations divided by s, the best factor chosen; no
+ * Hessian).  The grid is the asymmetric min-max grid of the GPTQ calls, with
+ * correctly rounded fp32 divisions. */
+
+/* a[j] += sum_t X[t][j]^2 in fp64 (exact squares; the token splits are added
+ * in a fixed order), the square of the RMS times n_tokens.  Accumulates, like
+ * the Hessian: zero a before the first chunk.
+ *  a   [d_in] fp64 (device).  X [n_tokens x d_in] of x_dtype.
+ *  ws  scratch of gptq_awq_sumsq_workspace_size(n_tokens, d_in) bytes.
+ *  n_tokens == 0 leaves a untouched. */
+size_t gptq_awq_sumsq_workspace_size(int64_t n_tokens, int32_t d_in);
+int gptq_awq_act_sumsq(double* a, const void* X, gptq_dtype x_dtype, int64_t n_tokens,
+                       int32_t d_in, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* The factor search.  Salient channels: the k = floor(top_frac * d_in + 0.5)
+ * channels with the largest a[j] (ties to the lower index).  For each
+ * candidate sigma = grid[i]: s_j = sigma on salient channels, 1 elsewhere;
+ * per group of group_size consecutive columns (-1: the whole row) the grid of
+ * fp32(W[r][j] * s_j); Qhat = scale * (code - zero) / s_j (fp64); and
+ * scores[i] = sum_j a[j] sum_r (W[r][j] - Qhat[r][j])^2 (fp64, rows added in a
+ * fixed order).  The first smallest score wins: s_out[j] = its sigma on
+ * salient channels, 1 elsewhere; *best = its index (best may be NULL).
+ *  W [d_out x d_in] of w_dtype; a [d_in] fp64 from gptq_awq_act_sumsq;
+ *  grid: HOST array of n_grid (1..32) finite factors > 0;
+ *  s_out [d_in] fp32, scores [n_grid] fp64, best [1] int32 (device).
+ *  ws  scratch of gptq_awq_search_workspace_size(d_out, d_in) bytes.
+ *  INVALID_ARG: bits outside 2..8, group_size 0 or < -1, top_frac outside
+ *  [0, 1], a bad grid, null pointers, non-positive sizes. */
+size_t gptq_awq_search_workspace_size(int32_t d_out, int32_t d_in);
+int gptq_awq_search(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in,
+                    const double* a, int32_t bits, int32_t group_size, float top_frac,
+                    const float* grid, int32_t n_grid, float* s_out, double* scores,
+                    int32_t* best, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Quantize with given channel factors: per group the grid of
+ * fp32(W[r][j] * s[j]); codes [d_out x d_in] uint8; scales/zeros
+ * [d_out x n_groups] fp32/int32 (the grid of the scaled weights; at inference
+ * the activations are divided by s); Qhat (may be NULL) [d_out x d_in] fp32,
+ * the effective weights scale * (code - zero) / s[j] rounded from fp64. */
+int gptq_awq_quantize(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in,
+                      const float* s, int32_t bits, int32_t group_size, uint8_t* codes,
+                      float* scales, int32_t* zeros, float* Qhat, hipStream_t s_stream);
+
 /* ---------------------------------------------------------------- misc */
 const char* gptq_status_string(int status);
 int gptq_abi_version(void);

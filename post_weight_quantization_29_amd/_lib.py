@@ -62,6 +62,14 @@ def lib() -> ctypes.CDLL:
             "gptq_pack_dense": (ctypes.c_int, [vp, i64, i64, i32, vp, vp]),
             "gptq_w4a16_gemm": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, vp, vp, vp, vp, i32, i32,
                                                i32, vp, ctypes.c_int, vp]),
+            "gptq_awq_sumsq_workspace_size": (sz, [i64, i32]),
+            "gptq_awq_act_sumsq": (ctypes.c_int, [vp, vp, ctypes.c_int, i64, i32, vp, sz, vp]),
+            "gptq_awq_search_workspace_size": (sz, [i32, i32]),
+            "gptq_awq_search": (ctypes.c_int, [vp, ctypes.c_int, i32, i32, vp, i32, i32, ctypes.c_float,
+                                               ctypes.POINTER(ctypes.c_float), i32, vp, vp, vp, vp, sz,
+                                               vp]),
+            "gptq_awq_quantize": (ctypes.c_int, [vp, ctypes.c_int, i32, i32, vp, i32, i32, vp, vp, vp,
+                                                 vp, vp]),
             "gptq_layer_error_workspace_size": (sz, [i32, i32]),
             "gptq_layer_error": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, i32, i32,
                                                 ctypes.POINTER(ctypes.c_double), vp, sz, vp]),
@@ -78,7 +86,9 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("gptq_hessian_workspace_size", "gptq_hessian_accumulate",
             "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
             "gptq_quantize_workspace_size", "gptq_quantize_layer", "gptq_pack_int4",
-            "gptq_pack_dense", "gptq_w4a16_gemm",
+            "gptq_pack_dense", "gptq_w4a16_gemm", "gptq_awq_sumsq_workspace_size",
+            "gptq_awq_act_sumsq", "gptq_awq_search_workspace_size", "gptq_awq_search",
+            "gptq_awq_quantize",
             "gptq_layer_error_workspace_size", "gptq_layer_error", "gptq_status_string",
             "gptq_abi_version")
 
@@ -215,6 +225,54 @@ def gptq_w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
                                  _ptr(zeros), _ptr(g_idx) if g_idx is not None else None,
                                  int(group_size), n_groups, d_out, _ptr(Y), _DTYPE[Y.dtype],
                                  _stream(stream)), "gptq_w4a16_gemm")
+
+
+AWQ_DEFAULT_GRID = tuple(1.0 + 0.125 * k for k in range(25))
+
+
+def gptq_awq_sumsq_workspace_size(n_tokens: int, d_in: int) -> int:
+    return int(lib().gptq_awq_sumsq_workspace_size(n_tokens, d_in))
+
+
+def gptq_awq_act_sumsq(a: torch.Tensor, X: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    _dev(a, "a"); _dev(X, "X")
+    n, d_in = X.shape
+    assert a.dtype == torch.float64 and a.shape == (d_in,)
+    ws = _ws(gptq_awq_sumsq_workspace_size(n, d_in), ws, X.device)
+    _check(lib().gptq_awq_act_sumsq(_ptr(a), _ptr(X), _DTYPE[X.dtype], n, d_in, _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)),
+           "gptq_awq_act_sumsq")
+
+
+def gptq_awq_search_workspace_size(d_out: int, d_in: int) -> int:
+    return int(lib().gptq_awq_search_workspace_size(d_out, d_in))
+
+
+def gptq_awq_search(W: torch.Tensor, a: torch.Tensor, s_out: torch.Tensor, scores: torch.Tensor,
+                    best: Optional[torch.Tensor] = None, bits: int = 4, group_size: int = 128,
+                    top_frac: float = 0.05, grid=AWQ_DEFAULT_GRID, ws: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    for t, n in ((W, "W"), (a, "a"), (s_out, "s_out"), (scores, "scores")):
+        _dev(t, n)
+    d_out, d_in = W.shape
+    g = (ctypes.c_float * len(grid))(*[float(v) for v in grid])
+    ws = _ws(gptq_awq_search_workspace_size(d_out, d_in), ws, W.device)
+    _check(lib().gptq_awq_search(_ptr(W), _DTYPE[W.dtype], d_out, d_in, _ptr(a), bits, group_size,
+                                 float(top_frac), g, len(grid), _ptr(s_out), _ptr(scores), _ptr(best),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "gptq_awq_search")
+
+
+def gptq_awq_quantize(W: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                      zeros: torch.Tensor, Qhat: Optional[torch.Tensor] = None, bits: int = 4,
+                      group_size: int = 128, stream=None) -> None:
+    for t, n in ((W, "W"), (s, "s"), (codes, "codes"), (scales, "scales"), (zeros, "zeros")):
+        _dev(t, n)
+    d_out, d_in = W.shape
+    _check(lib().gptq_awq_quantize(_ptr(W), _DTYPE[W.dtype], d_out, d_in, _ptr(s), bits, group_size,
+                                   _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(Qhat),
+                                   _stream(stream)), "gptq_awq_quantize")
 
 
 def gptq_layer_error_workspace_size(d_out: int, d_in: int) -> int:

@@ -1,0 +1,426 @@
+// Activation-aware weight quantization (AWQ) of one linear layer, the second
+// method the pages set beside GPTQ.  Steps, after "GPTQ/AWQ量化导出：让大模型在
+// 消费级显卡上跑起来" (the AWQ list: per-channel RMS of the calibration
+// activations, the top 5 % of channels, a larger factor for them, the factor
+// undone at inference) and "大模型压缩量化技术：GPTQ 与 AWQ 原理详解 + Python
+// 实战教程" section 四 (weights of the large-activation channels times s > 1,
+// quantize, activations divided by s; the best factor is chosen; no Hessian):
+//
+//   gptq_awq_act_sumsq  a_j += sum_t x_tj^2 (the RMS squared times N), fp64
+//   gptq_awq_search     salient set = top-k channels by a_j; for every
+//                       candidate sigma: the group grid of fp32(w * s_j),
+//                       s_j = sigma on salient channels and 1 elsewhere, and
+//                       E(sigma) = sum_j a_j sum_i (w_ij - Qhat_ij)^2 with
+//                       Qhat = scale * (code - zero) / s_j; the smallest E wins
+//   gptq_awq_quantize   the group grid of fp32(w * s_j) for given factors
+//
+// The grid is the asymmetric min-max grid of the GPTQ path (zero point not
+// clamped; a constant group a uses [min(a,0), max(a,0)]; all zero: scale 1),
+// here with correctly rounded fp32 divisions for the scale, the zero point and
+// each code.
+#include "common.h"
+
+namespace gptq {
+
+constexpr int kAwqMaxGrid = 32;    // candidates per search
+constexpr int kSqCh = 8;           // channels per thread in the statistics pass
+constexpr int kSqBlockCh = 256 * kSqCh;
+
+template <int DT>
+GPTQ_DEV float ld(const void* p, size_t i) {
+  if constexpr (DT == GPTQ_F32) return static_cast<const float*>(p)[i];
+  else if constexpr (DT == GPTQ_F16) return (float)static_cast<const _Float16*>(p)[i];
+  else return __builtin_bit_cast(float, (uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
+}
+
+// Eight consecutive values of X starting at element i (16-bit types: one
+// 16-byte load; fp32: two).  VEC: i is a multiple of 8 and rows are aligned.
+template <int DT, bool VEC>
+GPTQ_DEV void ld8(const void* p, size_t i, int nvalid, float (&v)[kSqCh]) {
+  if constexpr (VEC) {
+    if constexpr (DT == GPTQ_F32) {
+      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+      const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (DT == GPTQ_F16) {
+          v[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[k] & 0xFFFFu));
+          v[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[k] >> 16));
+        } else {
+          v[2 * k] = __builtin_bit_cast(float, u[k] << 16);
+          v[2 * k + 1] = __builtin_bit_cast(float, u[k] & 0xFFFF0000u);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSqCh; ++k) v[k] = (k < nvalid) ? ld<DT>(p, i + k) : 0.0f;
+  }
+}
+
+// Split s of the tokens, 2048 channels per block: each thread sums the exact
+// fp64 squares of its eight channels over the split's tokens in token order.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void sumsq_kernel(const void* __restrict__ X, int64_t n, int d,
+                                                    int64_t per_split, double* __restrict__ part) {
+  const int c0 = (blockIdx.x * 256 + threadIdx.x) * kSqCh;
+  if (c0 >= d) return;
+  const int nvalid = min(kSqCh, d - c0);
+  const int64_t t0 = (int64_t)blockIdx.y * per_split;
+  const int64_t t1 = min(n, t0 + per_split);
+  double acc[kSqCh];
+#pragma unroll
+  for (int k = 0; k < kSqCh; ++k) acc[k] = 0.0;
+#pragma unroll 4
+  for (int64_t t = t0; t < t1; ++t) {
+    float v[kSqCh];
+    ld8<DT, VEC>(X, (size_t)t * d + c0, nvalid, v);
+#pragma unroll
+    for (int k = 0; k < kSqCh; ++k) {
+      const double x = (double)v[k];
+      acc[k] += x * x;
+    }
+  }
+  double* out = part + (size_t)blockIdx.y * d + c0;
+#pragma unroll
+  for (int k = 0; k < kSqCh; ++k)
+    if (k < nvalid) out[k] = acc[k];
+}
+
+// a_j += the splits' partial sums, added in split order.
+__global__ __launch_bounds__(256) void sumsq_reduce_kernel(const double* __restrict__ part, int splits, int d,
+                                                           double* __restrict__ a) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= d) return;
+  double s = 0.0;
+  for (int p = 0; p < splits; ++p) s += part[(size_t)p * d + j];
+  a[j] += s;
+}
+
+// mask_j = 1 when fewer than ktop channels rank above j (a larger a, or an
+// equal a at a lower index): the top-ktop channels, ties to the lower index.
+__global__ __launch_bounds__(256) void rank_kernel(const double* __restrict__ a, int d, int ktop,
+                                                   uint8_t* __restrict__ mask) {
+  __shared__ double sa[256];
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  const double aj = (j < d) ? a[j] : 0.0;
+  int above = 0;
+  for (int k0 = 0; k0 < d; k0 += 256) {
+    __syncthreads();
+    sa[threadIdx.x] = (k0 + (int)threadIdx.x < d) ? a[k0 + threadIdx.x] : 0.0;
+    __syncthreads();
+    const int kn = min(256, d - k0);
+    for (int u = 0; u < kn; ++u) {
+      const double ak = sa[u];
+      above += (ak > aj) || (ak == aj && k0 + u < j);
+    }
+  }
+  if (j < d) mask[j] = (above < ktop) ? 1 : 0;
+}
+
+// The asymmetric min-max grid of [mn, mx] with correctly rounded divisions.
+GPTQ_DEV void awq_grid(float mn, float mx, float maxq, float& scale, float& zero) {
+  if (mx == mn) {
+    mn = fminf(mn, 0.0f);
+    mx = fmaxf(mx, 0.0f);
+  }
+  const float rng = (mx == mn) ? maxq : mx - mn;
+  scale = __fdiv_rn(rng, maxq);
+  zero = rintf(__fdiv_rn(-mn, scale));
+}
+
+GPTQ_DEV float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+GPTQ_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+struct AwqGrid {
+  float v[kAwqMaxGrid];
+};
+
+// One wave per weight row.  Per group: min/max of the salient and of the other
+// channels' weights once (w -> fp32(w * sigma) is monotone, so the scaled
+// group's extremes follow from them for every sigma), then for each candidate
+// the codes and the weighted squared error of the group's columns, summed per
+// lane in fp64; the wave's sums per candidate go to part[row][k].
+template <int DT>
+__global__ __launch_bounds__(256) void awq_search_kernel(const void* __restrict__ W, int d_out, int d,
+                                                         const double* __restrict__ a,
+                                                         const uint8_t* __restrict__ mask, AwqGrid grid,
+                                                         int n_grid, int G, float maxq,
+                                                         double* __restrict__ part) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= d_out) return;
+  const size_t rb = (size_t)row * d;
+  double acc[kAwqMaxGrid];
+#pragma unroll
+  for (int k = 0; k < kAwqMaxGrid; ++k) acc[k] = 0.0;
+  for (int c0 = 0; c0 < d; c0 += G) {
+    const int c1 = min(d, c0 + G);
+    float mn0 = INFINITY, mx0 = -INFINITY, mns = INFINITY, mxs = -INFINITY;
+    for (int c = c0 + lane; c < c1; c += 64) {
+      const float w = ld<DT>(W, rb + c);
+      if (mask[c]) {
+        mns = fminf(mns, w);
+        mxs = fmaxf(mxs, w);
+      } else {
+        mn0 = fminf(mn0, w);
+        mx0 = fmaxf(mx0, w);
+      }
+    }
+    mn0 = wave_min(mn0);
+    mx0 = wave_max(mx0);
+    mns = wave_min(mns);
+    mxs = wave_max(mxs);
+#pragma unroll
+    for (int k = 0; k < kAwqMaxGrid; ++k) {
+      if (k < n_grid) {
+        const float sg = grid.v[k];
+        // fp32(mns * sg) is +inf * sg = +inf when the group has no salient channel
+        const float mn = fminf(mn0, mns * sg), mx = fmaxf(mx0, mxs * sg);
+        float scale, zero;
+        awq_grid(mn, mx, maxq, scale, zero);
+        const double sd = (double)scale, zd = (double)zero, sgd = (double)sg;
+        double e = 0.0;
+        for (int c = c0 + lane; c < c1; c += 64) {
+          const float w = ld<DT>(W, rb + c);
+          const bool sal = mask[c] != 0;
+          const float ws = sal ? w * sg : w;
+          const float code = fminf(fmaxf(rintf(__fdiv_rn(ws, scale)) + zero, 0.0f), maxq);
+          double qh = sd * ((double)code - zd);
+          if (sal) qh = qh / sgd;
+          const double df = (double)w - qh;
+          e = e + (a[c] * df) * df;
+        }
+        acc[k] = acc[k] + e;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kAwqMaxGrid; ++k) {
+    if (k < n_grid) {
+      double v = acc[k];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v = v + __shfl_xor(v, o);
+      if (lane == 0) part[(size_t)row * kAwqMaxGrid + k] = v;
+    }
+  }
+}
+
+// scores[k] = sum over rows of part[row][k], in a fixed order.
+__global__ __launch_bounds__(256) void awq_score_kernel(const double* __restrict__ part, int d_out,
+                                                        double* __restrict__ scores) {
+  __shared__ double red[256];
+  const int k = blockIdx.x;
+  double s = 0.0;
+  for (int r = threadIdx.x; r < d_out; r += 256) s += part[(size_t)r * kAwqMaxGrid + k];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) scores[k] = red[0];
+}
+
+// The first candidate with the smallest score; s_j = its sigma on salient
+// channels, 1 elsewhere.
+__global__ __launch_bounds__(256) void awq_select_kernel(const double* __restrict__ scores, int n_grid,
+                                                         AwqGrid grid, const uint8_t* __restrict__ mask,
+                                                         int d, float* __restrict__ s_out,
+                                                         int32_t* __restrict__ best) {
+  int bi = 0;
+  for (int k = 1; k < n_grid; ++k)
+    if (scores[k] < scores[bi]) bi = k;
+  const float sg = grid.v[bi];
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < d) s_out[j] = mask[j] ? sg : 1.0f;
+  if (j == 0 && best) *best = bi;
+}
+
+// One wave per row: per group the grid of fp32(w * s_j), codes, and the
+// effective weights scale * (code - zero) / s_j.
+template <int DT>
+__global__ __launch_bounds__(256) void awq_quant_kernel(const void* __restrict__ W, int d_out, int d,
+                                                        const float* __restrict__ s, int G, int ng, float maxq,
+                                                        uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                                        int32_t* __restrict__ zeros, float* __restrict__ Qhat) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= d_out) return;
+  const size_t rb = (size_t)row * d;
+  for (int c0 = 0, g = 0; c0 < d; c0 += G, ++g) {
+    const int c1 = min(d, c0 + G);
+    float mn = INFINITY, mx = -INFINITY;
+    for (int c = c0 + lane; c < c1; c += 64) {
+      const float ws = ld<DT>(W, rb + c) * s[c];
+      mn = fminf(mn, ws);
+      mx = fmaxf(mx, ws);
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    float scale, zero;
+    awq_grid(mn, mx, maxq, scale, zero);
+    if (lane == 0) {
+      scales[(size_t)row * ng + g] = scale;
+      zeros[(size_t)row * ng + g] = (int32_t)zero;
+    }
+    for (int c = c0 + lane; c < c1; c += 64) {
+      const float sc = s[c];
+      const float ws = ld<DT>(W, rb + c) * sc;
+      const float code = fminf(fmaxf(rintf(__fdiv_rn(ws, scale)) + zero, 0.0f), maxq);
+      codes[rb + c] = (uint8_t)code;
+      if (Qhat) Qhat[rb + c] = (float)(((double)scale * ((double)code - (double)zero)) / (double)sc);
+    }
+  }
+}
+
+struct SumsqShape {
+  int cblocks;
+  int splits;
+  int64_t per_split;
+};
+
+static SumsqShape sumsq_shape(int64_t n, int d) {
+  SumsqShape sh;
+  sh.cblocks = (d + kSqBlockCh - 1) / kSqBlockCh;
+  const int64_t max_splits = std::max<int64_t>(1, (n + 63) / 64);       // at least 64 tokens a split
+  sh.splits = (int)std::max<int64_t>(1, std::min<int64_t>(1024 / sh.cblocks, max_splits));
+  sh.per_split = (n + sh.splits - 1) / sh.splits;
+  sh.splits = (int)std::max<int64_t>(1, (n + sh.per_split - 1) / sh.per_split);
+  return sh;
+}
+
+struct SearchLayout {
+  size_t off_mask, off_part, total;
+};
+
+static SearchLayout search_layout(int d_out, int d) {
+  SearchLayout L;
+  L.off_mask = 0;
+  L.off_part = align_up((size_t)d);
+  L.total = align_up(L.off_part + (size_t)d_out * kAwqMaxGrid * sizeof(double));
+  return L;
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_awq_sumsq_workspace_size(int64_t n_tokens, int32_t d_in) {
+  if (n_tokens <= 0 || d_in <= 0) return 0;
+  const SumsqShape sh = sumsq_shape(n_tokens, d_in);
+  return align_up((size_t)sh.splits * d_in * sizeof(double));
+}
+
+extern "C" int gptq_awq_act_sumsq(double* sumsq, const void* X, gptq_dtype x_dtype, int64_t n_tokens,
+                                  int32_t d_in, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!sumsq || d_in <= 0 || n_tokens < 0) return GPTQ_ERR_INVALID_ARG;
+  if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_F16 && x_dtype != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return GPTQ_OK;
+  if (!X) return GPTQ_ERR_INVALID_ARG;
+  const SumsqShape sh = sumsq_shape(n_tokens, d_in);
+  if (!ws || ws_bytes < (size_t)sh.splits * d_in * sizeof(double)) return GPTQ_ERR_WORKSPACE;
+  double* part = static_cast<double*>(ws);
+  const bool aligned = (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+  const bool vec = aligned && (x_dtype == GPTQ_F32 ? (d_in % 4 == 0) : (d_in % 8 == 0));
+  const dim3 grid(sh.cblocks, sh.splits);
+#define GPTQ_SUMSQ(DT)                                                                             \
+  (vec ? sumsq_kernel<DT, true><<<grid, 256, 0, s>>>(X, n_tokens, d_in, sh.per_split, part)         \
+       : sumsq_kernel<DT, false><<<grid, 256, 0, s>>>(X, n_tokens, d_in, sh.per_split, part))
+  if (x_dtype == GPTQ_F32) GPTQ_SUMSQ(GPTQ_F32);
+  else if (x_dtype == GPTQ_F16) GPTQ_SUMSQ(GPTQ_F16);
+  else GPTQ_SUMSQ(GPTQ_BF16);
+#undef GPTQ_SUMSQ
+  GPTQ_LAUNCH_CHECK();
+  sumsq_reduce_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(part, sh.splits, d_in, sumsq);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+extern "C" size_t gptq_awq_search_workspace_size(int32_t d_out, int32_t d_in) {
+  if (d_out <= 0 || d_in <= 0) return 0;
+  return search_layout(d_out, d_in).total;
+}
+
+static int awq_common_checks(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in, int32_t bits,
+                             int32_t group_size) {
+  if (!W || d_out <= 0 || d_in <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (w_dtype != GPTQ_F32 && w_dtype != GPTQ_F16 && w_dtype != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
+  if (bits < 2 || bits > 8) return GPTQ_ERR_INVALID_ARG;
+  if (group_size != -1 && group_size <= 0) return GPTQ_ERR_INVALID_ARG;
+  return GPTQ_OK;
+}
+
+extern "C" int gptq_awq_search(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in,
+                               const double* sumsq, int32_t bits, int32_t group_size, float top_frac,
+                               const float* grid, int32_t n_grid, float* s_out, double* scores,
+                               int32_t* best, void* ws, size_t ws_bytes, hipStream_t s) {
+  const int st = awq_common_checks(W, w_dtype, d_out, d_in, bits, group_size);
+  if (st != GPTQ_OK) return st;
+  if (!sumsq || !grid || !s_out || !scores) return GPTQ_ERR_INVALID_ARG;
+  if (n_grid < 1 || n_grid > kAwqMaxGrid) return GPTQ_ERR_INVALID_ARG;
+  if (!(top_frac >= 0.0f && top_frac <= 1.0f)) return GPTQ_ERR_INVALID_ARG;
+  AwqGrid gv{};
+  for (int k = 0; k < n_grid; ++k) {
+    if (!(grid[k] > 0.0f) || !std::isfinite(grid[k])) return GPTQ_ERR_INVALID_ARG;
+    gv.v[k] = grid[k];
+  }
+  const SearchLayout L = search_layout(d_out, d_in);
+  if (!ws || ws_bytes < L.total) return GPTQ_ERR_WORKSPACE;
+  uint8_t* mask = static_cast<uint8_t*>(ws) + L.off_mask;
+  double* part = reinterpret_cast<double*>(static_cast<char*>(ws) + L.off_part);
+  const int G = (group_size == -1) ? d_in : group_size;
+  const float maxq = (float)((1 << bits) - 1);
+  // k = top_frac * d_in rounded to nearest, halves up, in double
+  const int ktop = (int)std::min<double>(d_in, std::floor((double)top_frac * d_in + 0.5));
+
+  rank_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(sumsq, d_in, ktop, mask);
+  GPTQ_LAUNCH_CHECK();
+  const unsigned rows_grid = (unsigned)((d_out + 3) / 4);
+  if (w_dtype == GPTQ_F32)
+    awq_search_kernel<GPTQ_F32><<<rows_grid, 256, 0, s>>>(W, d_out, d_in, sumsq, mask, gv, n_grid, G, maxq, part);
+  else if (w_dtype == GPTQ_F16)
+    awq_search_kernel<GPTQ_F16><<<rows_grid, 256, 0, s>>>(W, d_out, d_in, sumsq, mask, gv, n_grid, G, maxq, part);
+  else
+    awq_search_kernel<GPTQ_BF16><<<rows_grid, 256, 0, s>>>(W, d_out, d_in, sumsq, mask, gv, n_grid, G, maxq, part);
+  GPTQ_LAUNCH_CHECK();
+  awq_score_kernel<<<n_grid, 256, 0, s>>>(part, d_out, scores);
+  GPTQ_LAUNCH_CHECK();
+  awq_select_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(scores, n_grid, gv, mask, d_in, s_out, best);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+extern "C" int gptq_awq_quantize(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in,
+                                 const float* s_in, int32_t bits, int32_t group_size, uint8_t* codes,
+                                 float* scales, int32_t* zeros, float* Qhat, hipStream_t s) {
+  const int st = awq_common_checks(W, w_dtype, d_out, d_in, bits, group_size);
+  if (st != GPTQ_OK) return st;
+  if (!s_in || !codes || !scales || !zeros) return GPTQ_ERR_INVALID_ARG;
+  const int G = (group_size == -1) ? d_in : group_size;
+  const int ng = (d_in + G - 1) / G;
+  const float maxq = (float)((1 << bits) - 1);
+  const unsigned rows_grid = (unsigned)((d_out + 3) / 4);
+  if (w_dtype == GPTQ_F32)
+    awq_quant_kernel<GPTQ_F32><<<rows_grid, 256, 0, s>>>(W, d_out, d_in, s_in, G, ng, maxq, codes, scales, zeros, Qhat);
+  else if (w_dtype == GPTQ_F16)
+    awq_quant_kernel<GPTQ_F16><<<rows_grid, 256, 0, s>>>(W, d_out, d_in, s_in, G, ng, maxq, codes, scales, zeros, Qhat);
+  else
+    awq_quant_kernel<GPTQ_BF16><<<rows_grid, 256, 0, s>>>(W, d_out, d_in, s_in, G, ng, maxq, codes, scales, zeros, Qhat);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}

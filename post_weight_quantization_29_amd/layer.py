@@ -58,3 +58,45 @@ def quantize_layer_outputs(W: torch.Tensor, H: torch.Tensor, cfg: L.gptq_config,
         L.gptq_pack_int4(out["codes"], packed)
     return GPTQLayerResult(out["codes"], out["scales"], out["zeros"], out["g_idx"], perm, U,
                            out["Q"], packed)
+
+
+@dataclass
+class AWQLayerResult:
+    s: torch.Tensor          # [d_in] fp32 channel factors (activations are divided by them)
+    best: int                # index of the chosen factor in the grid
+    scores: torch.Tensor     # [n_grid] fp64 activation-weighted error of every candidate
+    codes: torch.Tensor      # [d_out, d_in] uint8
+    scales: torch.Tensor     # [d_out, n_groups] fp32
+    zeros: torch.Tensor      # [d_out, n_groups] int32
+    Qhat: Optional[torch.Tensor]
+    packed: Optional[torch.Tensor]
+
+
+def awq_quantize_layer(W: torch.Tensor, x_chunks, bits: int = 4, group_size: int = 128,
+                       top_frac: float = 0.05, grid=L.AWQ_DEFAULT_GRID, with_q: bool = True,
+                       pack: bool = True, a: Optional[torch.Tensor] = None) -> AWQLayerResult:
+    """gptq_awq_act_sumsq over the calibration chunks (unless the statistic a
+    is given) -> gptq_awq_search -> gptq_awq_quantize -> gptq_pack_int4."""
+    d_out, d_in = W.shape
+    dev = W.device
+    if a is None:
+        a = torch.zeros((d_in,), dtype=torch.float64, device=dev)
+        for x in x_chunks:
+            L.gptq_awq_act_sumsq(a, x)
+    s = torch.empty((d_in,), dtype=torch.float32, device=dev)
+    scores = torch.empty((len(grid),), dtype=torch.float64, device=dev)
+    best = torch.empty((1,), dtype=torch.int32, device=dev)
+    L.gptq_awq_search(W, a, s, scores, best, bits=bits, group_size=group_size, top_frac=top_frac,
+                      grid=grid)
+    G = d_in if group_size == -1 else group_size
+    ng = (d_in + G - 1) // G
+    codes = torch.empty((d_out, d_in), dtype=torch.uint8, device=dev)
+    scales = torch.empty((d_out, ng), dtype=torch.float32, device=dev)
+    zeros = torch.empty((d_out, ng), dtype=torch.int32, device=dev)
+    Qhat = torch.empty((d_out, d_in), dtype=torch.float32, device=dev) if with_q else None
+    L.gptq_awq_quantize(W, s, codes, scales, zeros, Qhat, bits=bits, group_size=group_size)
+    packed = None
+    if pack and bits <= 4 and d_in % 8 == 0:
+        packed = torch.empty((d_out, d_in // 8), dtype=torch.int32, device=dev)
+        L.gptq_pack_int4(codes, packed)
+    return AWQLayerResult(s, int(best.item()), scores, codes, scales, zeros, Qhat, packed)

@@ -84,6 +84,29 @@ def test_argument_validation_before_any_launch(L):
     assert L.gptq_pack_dense(fake, 0, 32, 3, fake, None) == P._lib.OK
     # layer error: null output pointer
     assert L.gptq_layer_error(fake, fake, 1, fake, 4, 8, None, fake, 1 << 20, None) == P._lib.ERR_INVALID_ARG
+    # AWQ statistics: bad dtype, zero tokens is a no-op, workspace too small
+    assert L.gptq_awq_act_sumsq(fake, fake, 7, 16, 64, fake, 1 << 20, None) == P._lib.ERR_INVALID_ARG
+    assert L.gptq_awq_act_sumsq(fake, None, 2, 0, 64, None, 0, None) == P._lib.OK
+    assert L.gptq_awq_act_sumsq(fake, fake, 2, 4096, 64, fake, 8, None) == P._lib.ERR_WORKSPACE
+    # AWQ search: grid size and values, top_frac range, bits
+    G = (ctypes.c_float * 3)(1.0, 1.5, 2.0)
+    bad = (ctypes.c_float * 2)(1.0, -1.0)
+    big = (ctypes.c_float * 33)(*([1.0] * 33))
+
+    def srch(grid, n, frac=0.05, bits=4, gs=128, ws=1 << 30):
+        return L.gptq_awq_search(fake, 1, 8, 256, fake, bits, gs, frac, grid, n, fake, fake, None,
+                                 fake, ws, None)
+    assert srch(G, 0) == P._lib.ERR_INVALID_ARG
+    assert srch(big, 33) == P._lib.ERR_INVALID_ARG
+    assert srch(bad, 2) == P._lib.ERR_INVALID_ARG
+    assert srch(G, 3, frac=1.5) == P._lib.ERR_INVALID_ARG
+    assert srch(G, 3, bits=9) == P._lib.ERR_INVALID_ARG
+    assert srch(G, 3, gs=0) == P._lib.ERR_INVALID_ARG
+    assert srch(G, 3, ws=16) == P._lib.ERR_WORKSPACE
+    assert P.gptq_awq_search_workspace_size(4096, 4096) >= 4096 * 32 * 8
+    assert P.gptq_awq_sumsq_workspace_size(262144, 4096) > 0
+    # AWQ quantize: null factors
+    assert L.gptq_awq_quantize(fake, 1, 8, 256, None, 4, 128, fake, fake, fake, None, None) == P._lib.ERR_INVALID_ARG
 
 
 def test_package_fails_loudly_without_library(tmp_path, monkeypatch):
