@@ -9,7 +9,10 @@ H = 0; H += 2 X^T X; damp + order + U; column loop with lazy updates; pack.
 Prints one JSON line.  The roofline object is for the dominant stage (the
 Hessian: the SYRK kernel plus its fixed-order split reduction), timed with HIP
 events on the stream the library launches on.  The cpu_baseline object times
-the float64 CPU oracle on a bounded sample of the same workload.
+the float64 CPU oracle on a bounded sample of the same workload.  Two more
+objects time the widened rows on the same inputs: w4a16_decode (the product on
+the packed layer at one activation row) and awq (the activation-aware
+quantization of the same layer from the same calibration tokens).
 """
 from __future__ import annotations
 
@@ -158,6 +161,63 @@ def w4a16_measure(P, torch, packed, scales, zeros, group_size, reps=24):
     return out
 
 
+def awq_measure(P, torch, Wg, Xg, reps=5):
+    """The AWQ path on the same layer and calibration tokens (both already in
+    HBM): the channel statistic over all tokens, the factor search (25
+    candidates, top 5 %, 4-bit groups of 128), the scaled quantization and
+    the packing.  HIP events on the launch stream, mean over reps after a
+    warm-up.  The statistic reads X once (2 bytes per element): its HBM rate
+    is reported against 8 TB/s."""
+    d_out, d = Wg.shape
+    N = Xg.shape[0]
+    dev = Wg.device
+    grid = P.AWQ_DEFAULT_GRID
+    a = torch.zeros((d,), dtype=torch.float64, device=dev)
+    s = torch.empty((d,), dtype=torch.float32, device=dev)
+    scores = torch.empty((len(grid),), dtype=torch.float64, device=dev)
+    best = torch.empty((1,), dtype=torch.int32, device=dev)
+    codes = torch.empty((d_out, d), dtype=torch.uint8, device=dev)
+    scales = torch.empty((d_out, d // 128), dtype=torch.float32, device=dev)
+    zeros = torch.empty((d_out, d // 128), dtype=torch.int32, device=dev)
+    packed = torch.empty((d_out, d // 8), dtype=torch.int32, device=dev)
+    ws_a = torch.empty(P.gptq_awq_sumsq_workspace_size(N, d), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(P.gptq_awq_search_workspace_size(d_out, d, 128), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run(ev=None):
+        if ev:
+            ev[0].record(stream)
+        a.zero_()
+        P.gptq_awq_act_sumsq(a, Xg, ws_a)
+        if ev:
+            ev[1].record(stream)
+        P.gptq_awq_search(Wg, a, s, scores, best, grid=grid, ws=ws_s)
+        if ev:
+            ev[2].record(stream)
+        P.gptq_awq_quantize(Wg, s, codes, scales, zeros, None)
+        if ev:
+            ev[3].record(stream)
+        P.gptq_pack_int4(codes, packed)
+        if ev:
+            ev[4].record(stream)
+
+    run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    names = ["statistic", "search", "quantize", "pack"]
+    ms = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / reps for k, n in enumerate(names)}
+    total = sum(ms.values())
+    x_bytes = N * d * Xg.element_size()
+    gbs = x_bytes / (ms["statistic"] / 1e3) / 1e9
+    return {"stages_ms": {k: round(v, 4) for k, v in ms.items()}, "ms_per_layer": round(total, 4),
+            "weights_per_s": d_out * d / (total / 1e3), "best_factor": float(grid[int(best.item())]),
+            "statistic_GB_per_s": round(gbs, 1), "statistic_frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "grid": len(grid)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -295,6 +355,7 @@ def main():
                      "work_per_launch": f"N*d*(d+1) = {h_flops:.4g} flop"},
     }
     out["w4a16_decode"] = w4a16_measure(P, torch, packed, scales, zeros, q.group_size)
+    out["awq"] = awq_measure(P, torch, Wg, Xg)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(W, X, wl, args)

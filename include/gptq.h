@@ -229,10 +229,10 @@ int gptq_awq_act_sumsq(double* a, const void* X, gptq_dtype x_dtype, int64_t n_t
  *  W [d_out x d_in] of w_dtype; a [d_in] fp64 from gptq_awq_act_sumsq;
  *  grid: HOST array of n_grid (1..32) finite factors > 0;
  *  s_out [d_in] fp32, scores [n_grid] fp64, best [1] int32 (device).
- *  ws  scratch of gptq_awq_search_workspace_size(d_out, d_in) bytes.
+ *  ws  scratch of gptq_awq_search_workspace_size(d_out, d_in, group_size) bytes.
  *  INVALID_ARG: bits outside 2..8, group_size 0 or < -1, top_frac outside
  *  [0, 1], a bad grid, null pointers, non-positive sizes. */
-size_t gptq_awq_search_workspace_size(int32_t d_out, int32_t d_in);
+size_t gptq_awq_search_workspace_size(int32_t d_out, int32_t d_in, int32_t group_size);
 int gptq_awq_search(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in,
                     const double* a, int32_t bits, int32_t group_size, float top_frac,
                     const float* grid, int32_t n_grid, float* s_out, double* scores,

@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
                                                i32, vp, ctypes.c_int, vp]),
             "gptq_awq_sumsq_workspace_size": (sz, [i64, i32]),
             "gptq_awq_act_sumsq": (ctypes.c_int, [vp, vp, ctypes.c_int, i64, i32, vp, sz, vp]),
-            "gptq_awq_search_workspace_size": (sz, [i32, i32]),
+            "gptq_awq_search_workspace_size": (sz, [i32, i32, i32]),
             "gptq_awq_search": (ctypes.c_int, [vp, ctypes.c_int, i32, i32, vp, i32, i32, ctypes.c_float,
                                                ctypes.POINTER(ctypes.c_float), i32, vp, vp, vp, vp, sz,
                                                vp]),
@@ -245,8 +245,8 @@ def gptq_awq_act_sumsq(a: torch.Tensor, X: torch.Tensor, ws: Optional[torch.Tens
            "gptq_awq_act_sumsq")
 
 
-def gptq_awq_search_workspace_size(d_out: int, d_in: int) -> int:
-    return int(lib().gptq_awq_search_workspace_size(d_out, d_in))
+def gptq_awq_search_workspace_size(d_out: int, d_in: int, group_size: int = 128) -> int:
+    return int(lib().gptq_awq_search_workspace_size(d_out, d_in, group_size))
 
 
 def gptq_awq_search(W: torch.Tensor, a: torch.Tensor, s_out: torch.Tensor, scores: torch.Tensor,
@@ -257,7 +257,7 @@ def gptq_awq_search(W: torch.Tensor, a: torch.Tensor, s_out: torch.Tensor, score
         _dev(t, n)
     d_out, d_in = W.shape
     g = (ctypes.c_float * len(grid))(*[float(v) for v in grid])
-    ws = _ws(gptq_awq_search_workspace_size(d_out, d_in), ws, W.device)
+    ws = _ws(gptq_awq_search_workspace_size(d_out, d_in, group_size), ws, W.device)
     _check(lib().gptq_awq_search(_ptr(W), _DTYPE[W.dtype], d_out, d_in, _ptr(a), bits, group_size,
                                  float(top_frac), g, len(grid), _ptr(s_out), _ptr(scores), _ptr(best),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),

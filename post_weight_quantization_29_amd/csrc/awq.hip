@@ -23,8 +23,10 @@
 namespace gptq {
 
 constexpr int kAwqMaxGrid = 32;    // candidates per search
+constexpr int kAwqBatch = 8;       // candidates per pass over a group in the search
 constexpr int kSqCh = 8;           // channels per thread in the statistics pass
 constexpr int kSqBlockCh = 256 * kSqCh;
+constexpr int kSqTok = 8;          // tokens loaded together per thread
 
 template <int DT>
 GPTQ_DEV float ld(const void* p, size_t i) {
@@ -75,8 +77,21 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const void* __restrict__ X, 
   double acc[kSqCh];
 #pragma unroll
   for (int k = 0; k < kSqCh; ++k) acc[k] = 0.0;
-#pragma unroll 4
-  for (int64_t t = t0; t < t1; ++t) {
+  // eight tokens' loads in flight, then their squares in token order
+  int64_t t = t0;
+  for (; t + kSqTok <= t1; t += kSqTok) {
+    float v[kSqTok][kSqCh];
+#pragma unroll
+    for (int i = 0; i < kSqTok; ++i) ld8<DT, VEC>(X, (size_t)(t + i) * d + c0, nvalid, v[i]);
+#pragma unroll
+    for (int i = 0; i < kSqTok; ++i)
+#pragma unroll
+      for (int k = 0; k < kSqCh; ++k) {
+        const double x = (double)v[i][k];
+        acc[k] += x * x;
+      }
+  }
+  for (; t < t1; ++t) {
     float v[kSqCh];
     ld8<DT, VEC>(X, (size_t)t * d + c0, nvalid, v);
 #pragma unroll
@@ -145,87 +160,162 @@ GPTQ_DEV float wave_max(float v) {
 }
 
 struct AwqGrid {
-  float v[kAwqMaxGrid];
+  float v[kAwqMaxGrid];      // the candidate factors
+  double r[kAwqMaxGrid];     // their correctly rounded fp64 reciprocals
 };
 
-// One wave per weight row.  Per group: min/max of the salient and of the other
-// channels' weights once (w -> fp32(w * sigma) is monotone, so the scaled
-// group's extremes follow from them for every sigma), then for each candidate
-// the codes and the weighted squared error of the group's columns, summed per
-// lane in fp64; the wave's sums per candidate go to part[row][k].
-template <int DT>
+// rint(RN(x / y)) with y > 0 and ry = RN(1/y), without a division in almost
+// every case: t = RN(x * ry) is within 2^-23 |t| of the real quotient and the
+// correctly rounded quotient within 2^-24 of it, so unless a half-integer
+// lies within 4e-7 |t| + 1e-6 of t (then the correctly rounded quotient is
+// formed and decides) both round to the same integer.  For |t| >= 1.25e6 the
+// division is always taken.
+GPTQ_DEV float rint_quot(float x, float y, float ry) {
+  const float t = x * ry;
+  const float r = rintf(t);
+  if (fabsf(fabsf(t - r) - 0.5f) <= 4e-7f * fabsf(t) + 1e-6f) return rintf(__fdiv_rn(x, y));
+  return r;
+}
+
+// RN(a / b) for b a float32 value > 0 (as a double) and rb = RN(1/b): the
+// quotient of the reciprocal, corrected once with the exact remainder
+// (Markstein's correction; it rounds correctly unless b's 53-bit significand
+// is all ones, which a float32 value cannot have).
+GPTQ_DEV double quot64(double a, double b, double rb) {
+  const double q0 = a * rb;
+  const double rem = __builtin_fma(-q0, b, a);
+  return __builtin_fma(rem, rb, q0);
+}
+
+// Lanes are weight rows: wave w of block (rb, gb, kb) takes rows 64 rb .. +63,
+// group 4 gb + w and candidates 8 kb .. 8 kb + 7, so every column's statistic
+// and salient flag are the same for the whole wave.  Per lane: the extremes of the salient and of the
+// other weights of its row's group (w -> fp32(w * sigma) is monotone, so the
+// scaled group's extremes follow from them for every sigma), the grid of
+// its candidates, then one pass over the group's columns, eight at a time,
+// accumulating each candidate's weighted squared error in fp64.  The wave's
+// sums per candidate go to part[(rb * ng + g) * 32 + k].  VEC: 16-byte loads
+// (groups and rows start at multiples of 8 columns, W 16-byte aligned).
+template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void awq_search_kernel(const void* __restrict__ W, int d_out, int d,
                                                          const double* __restrict__ a,
                                                          const uint8_t* __restrict__ mask, AwqGrid grid,
-                                                         int n_grid, int G, float maxq,
+                                                         int n_grid, int G, int ng, float maxq,
                                                          double* __restrict__ part) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= d_out) return;
-  const size_t rb = (size_t)row * d;
-  double acc[kAwqMaxGrid];
+  const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * 4 + (threadIdx.x >> 6));
+  if (g >= ng) return;
+  const int row = blockIdx.x * 64 + lane;
+  const bool live = row < d_out;
+  const size_t rb = (size_t)min(row, d_out - 1) * d;
+  const int c0 = g * G, c1 = min(d, c0 + G);
+
+  auto load8 = [&](int cc, int nv, float (&wv)[8]) {
+    if constexpr (VEC) {
+      ld8<DT, true>(W, rb + cc, 8, wv);
+    } else {
 #pragma unroll
-  for (int k = 0; k < kAwqMaxGrid; ++k) acc[k] = 0.0;
-  for (int c0 = 0; c0 < d; c0 += G) {
-    const int c1 = min(d, c0 + G);
-    float mn0 = INFINITY, mx0 = -INFINITY, mns = INFINITY, mxs = -INFINITY;
-    for (int c = c0 + lane; c < c1; c += 64) {
-      const float w = ld<DT>(W, rb + c);
-      if (mask[c]) {
-        mns = fminf(mns, w);
-        mxs = fmaxf(mxs, w);
-      } else {
-        mn0 = fminf(mn0, w);
-        mx0 = fmaxf(mx0, w);
-      }
+      for (int u = 0; u < 8; ++u) wv[u] = (u < nv) ? ld<DT>(W, rb + cc + u) : 0.0f;
     }
-    mn0 = wave_min(mn0);
-    mx0 = wave_max(mx0);
-    mns = wave_min(mns);
-    mxs = wave_max(mxs);
+  };
+
+  float mn0 = INFINITY, mx0 = -INFINITY, mns = INFINITY, mxs = -INFINITY;
+  for (int cc = c0; cc < c1; cc += 8) {
+    const int nv = min(8, c1 - cc);
+    float wv[8];
+    load8(cc, nv, wv);
 #pragma unroll
-    for (int k = 0; k < kAwqMaxGrid; ++k) {
-      if (k < n_grid) {
-        const float sg = grid.v[k];
-        // fp32(mns * sg) is +inf * sg = +inf when the group has no salient channel
-        const float mn = fminf(mn0, mns * sg), mx = fmaxf(mx0, mxs * sg);
-        float scale, zero;
-        awq_grid(mn, mx, maxq, scale, zero);
-        const double sd = (double)scale, zd = (double)zero, sgd = (double)sg;
-        double e = 0.0;
-        for (int c = c0 + lane; c < c1; c += 64) {
-          const float w = ld<DT>(W, rb + c);
-          const bool sal = mask[c] != 0;
-          const float ws = sal ? w * sg : w;
-          const float code = fminf(fmaxf(rintf(__fdiv_rn(ws, scale)) + zero, 0.0f), maxq);
-          double qh = sd * ((double)code - zd);
-          if (sal) qh = qh / sgd;
-          const double df = (double)w - qh;
-          e = e + (a[c] * df) * df;
+    for (int u = 0; u < 8; ++u) {
+      if (u < nv) {
+        if (mask[cc + u]) {
+          mns = fminf(mns, wv[u]);
+          mxs = fmaxf(mxs, wv[u]);
+        } else {
+          mn0 = fminf(mn0, wv[u]);
+          mx0 = fmaxf(mx0, wv[u]);
         }
-        acc[k] = acc[k] + e;
       }
     }
   }
+  // candidates k0 .. k0 + kAwqBatch - 1 (blockIdx.z = batch), their grids and
+  // sums in registers
+  double* out = part + ((size_t)blockIdx.x * ng + g) * kAwqMaxGrid;
+  {
+    const int k0 = blockIdx.z * kAwqBatch;
+    float scl[kAwqBatch], zer[kAwqBatch], rsc[kAwqBatch], sgv[kAwqBatch];
+    double acc[kAwqBatch], rsg[kAwqBatch];
 #pragma unroll
-  for (int k = 0; k < kAwqMaxGrid; ++k) {
-    if (k < n_grid) {
-      double v = acc[k];
+    for (int kk = 0; kk < kAwqBatch; ++kk) {
+      acc[kk] = 0.0;
+      scl[kk] = 1.0f;
+      zer[kk] = 0.0f;
+      rsc[kk] = 1.0f;
+      sgv[kk] = 1.0f;
+      rsg[kk] = 1.0;
+      if (k0 + kk < n_grid) {
+        sgv[kk] = grid.v[k0 + kk];
+        rsg[kk] = grid.r[k0 + kk];
+        // fp32(mns * sg) is +inf when the group has no salient channel
+        awq_grid(fminf(mn0, mns * sgv[kk]), fmaxf(mx0, mxs * sgv[kk]), maxq, scl[kk], zer[kk]);
+        rsc[kk] = __fdiv_rn(1.0f, scl[kk]);
+      }
+    }
+    for (int cc = c0; cc < c1; cc += 8) {
+      const int nv = min(8, c1 - cc);
+      float wv[8];
+      load8(cc, nv, wv);
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v = v + __shfl_xor(v, o);
-      if (lane == 0) part[(size_t)row * kAwqMaxGrid + k] = v;
+      for (int u = 0; u < 8; ++u) {
+        if (u < nv) {
+          const int c = cc + u;
+          const double ac = a[c];
+          const double wd = (double)wv[u];
+          if (mask[c]) {
+#pragma unroll
+            for (int kk = 0; kk < kAwqBatch; ++kk) {
+              if (k0 + kk < n_grid) {
+                const float code =
+                    fminf(fmaxf(rint_quot(wv[u] * sgv[kk], scl[kk], rsc[kk]) + zer[kk], 0.0f), maxq);
+                const double qh =
+                    quot64((double)scl[kk] * ((double)code - (double)zer[kk]), (double)sgv[kk], rsg[kk]);
+                const double df = wd - qh;
+                acc[kk] = acc[kk] + (ac * df) * df;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int kk = 0; kk < kAwqBatch; ++kk) {
+              if (k0 + kk < n_grid) {
+                const float code = fminf(fmaxf(rint_quot(wv[u], scl[kk], rsc[kk]) + zer[kk], 0.0f), maxq);
+                const double df = wd - (double)scl[kk] * ((double)code - (double)zer[kk]);
+                acc[kk] = acc[kk] + (ac * df) * df;
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < kAwqBatch; ++kk) {
+      if (k0 + kk < n_grid) {
+        double v = live ? acc[kk] : 0.0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v = v + __shfl_xor(v, o);
+        if (lane == 0) out[k0 + kk] = v;
+      }
     }
   }
 }
 
-// scores[k] = sum over rows of part[row][k], in a fixed order.
-__global__ __launch_bounds__(256) void awq_score_kernel(const double* __restrict__ part, int d_out,
+// scores[k] = sum over the n_part (row block, group) partials part[p][k], in
+// a fixed order.
+__global__ __launch_bounds__(256) void awq_score_kernel(const double* __restrict__ part, int n_part,
                                                         double* __restrict__ scores) {
   __shared__ double red[256];
   const int k = blockIdx.x;
   double s = 0.0;
-  for (int r = threadIdx.x; r < d_out; r += 256) s += part[(size_t)r * kAwqMaxGrid + k];
+  for (int r = threadIdx.x; r < n_part; r += 256) s += part[(size_t)r * kAwqMaxGrid + k];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
@@ -298,7 +388,7 @@ static SumsqShape sumsq_shape(int64_t n, int d) {
   SumsqShape sh;
   sh.cblocks = (d + kSqBlockCh - 1) / kSqBlockCh;
   const int64_t max_splits = std::max<int64_t>(1, (n + 63) / 64);       // at least 64 tokens a split
-  sh.splits = (int)std::max<int64_t>(1, std::min<int64_t>(1024 / sh.cblocks, max_splits));
+  sh.splits = (int)std::max<int64_t>(1, std::min<int64_t>(512 / sh.cblocks, max_splits));
   sh.per_split = (n + sh.splits - 1) / sh.splits;
   sh.splits = (int)std::max<int64_t>(1, (n + sh.per_split - 1) / sh.per_split);
   return sh;
@@ -308,11 +398,13 @@ struct SearchLayout {
   size_t off_mask, off_part, total;
 };
 
-static SearchLayout search_layout(int d_out, int d) {
+// partials: one per (64-row block, group)
+static SearchLayout search_layout(int d_out, int d, int G) {
   SearchLayout L;
   L.off_mask = 0;
   L.off_part = align_up((size_t)d);
-  L.total = align_up(L.off_part + (size_t)d_out * kAwqMaxGrid * sizeof(double));
+  const size_t nparts = (size_t)((d_out + 63) / 64) * ((d + G - 1) / G);
+  L.total = align_up(L.off_part + nparts * kAwqMaxGrid * sizeof(double));
   return L;
 }
 
@@ -351,9 +443,9 @@ extern "C" int gptq_awq_act_sumsq(double* sumsq, const void* X, gptq_dtype x_dty
   return GPTQ_OK;
 }
 
-extern "C" size_t gptq_awq_search_workspace_size(int32_t d_out, int32_t d_in) {
-  if (d_out <= 0 || d_in <= 0) return 0;
-  return search_layout(d_out, d_in).total;
+extern "C" size_t gptq_awq_search_workspace_size(int32_t d_out, int32_t d_in, int32_t group_size) {
+  if (d_out <= 0 || d_in <= 0 || group_size == 0 || group_size < -1) return 0;
+  return search_layout(d_out, d_in, group_size == -1 ? d_in : group_size).total;
 }
 
 static int awq_common_checks(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in, int32_t bits,
@@ -378,27 +470,34 @@ extern "C" int gptq_awq_search(const void* W, gptq_dtype w_dtype, int32_t d_out,
   for (int k = 0; k < n_grid; ++k) {
     if (!(grid[k] > 0.0f) || !std::isfinite(grid[k])) return GPTQ_ERR_INVALID_ARG;
     gv.v[k] = grid[k];
+    gv.r[k] = 1.0 / (double)grid[k];
   }
-  const SearchLayout L = search_layout(d_out, d_in);
+  const int G = (group_size == -1) ? d_in : group_size;
+  const SearchLayout L = search_layout(d_out, d_in, G);
   if (!ws || ws_bytes < L.total) return GPTQ_ERR_WORKSPACE;
   uint8_t* mask = static_cast<uint8_t*>(ws) + L.off_mask;
   double* part = reinterpret_cast<double*>(static_cast<char*>(ws) + L.off_part);
-  const int G = (group_size == -1) ? d_in : group_size;
   const float maxq = (float)((1 << bits) - 1);
   // k = top_frac * d_in rounded to nearest, halves up, in double
   const int ktop = (int)std::min<double>(d_in, std::floor((double)top_frac * d_in + 0.5));
 
   rank_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(sumsq, d_in, ktop, mask);
   GPTQ_LAUNCH_CHECK();
-  const unsigned rows_grid = (unsigned)((d_out + 3) / 4);
-  if (w_dtype == GPTQ_F32)
-    awq_search_kernel<GPTQ_F32><<<rows_grid, 256, 0, s>>>(W, d_out, d_in, sumsq, mask, gv, n_grid, G, maxq, part);
-  else if (w_dtype == GPTQ_F16)
-    awq_search_kernel<GPTQ_F16><<<rows_grid, 256, 0, s>>>(W, d_out, d_in, sumsq, mask, gv, n_grid, G, maxq, part);
-  else
-    awq_search_kernel<GPTQ_BF16><<<rows_grid, 256, 0, s>>>(W, d_out, d_in, sumsq, mask, gv, n_grid, G, maxq, part);
+  const int ng = (d_in + G - 1) / G;
+  const dim3 sgrid((unsigned)((d_out + 63) / 64), (unsigned)((ng + 3) / 4),
+                   (unsigned)((n_grid + kAwqBatch - 1) / kAwqBatch));
+  const bool vec = (G % 8 == 0) && (d_in % 8 == 0) && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+#define GPTQ_SEARCH(DT)                                                                                      \
+  (vec ? awq_search_kernel<DT, true><<<sgrid, 256, 0, s>>>(W, d_out, d_in, sumsq, mask, gv, n_grid, G, ng,   \
+                                                           maxq, part)                                       \
+       : awq_search_kernel<DT, false><<<sgrid, 256, 0, s>>>(W, d_out, d_in, sumsq, mask, gv, n_grid, G, ng,  \
+                                                            maxq, part))
+  if (w_dtype == GPTQ_F32) GPTQ_SEARCH(GPTQ_F32);
+  else if (w_dtype == GPTQ_F16) GPTQ_SEARCH(GPTQ_F16);
+  else GPTQ_SEARCH(GPTQ_BF16);
+#undef GPTQ_SEARCH
   GPTQ_LAUNCH_CHECK();
-  awq_score_kernel<<<n_grid, 256, 0, s>>>(part, d_out, scores);
+  awq_score_kernel<<<n_grid, 256, 0, s>>>(part, (int)(sgrid.x * ng), scores);
   GPTQ_LAUNCH_CHECK();
   awq_select_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(scores, n_grid, gv, mask, d_in, s_out, best);
   GPTQ_LAUNCH_CHECK();

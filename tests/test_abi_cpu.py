@@ -103,7 +103,8 @@ def test_argument_validation_before_any_launch(L):
     assert srch(G, 3, bits=9) == P._lib.ERR_INVALID_ARG
     assert srch(G, 3, gs=0) == P._lib.ERR_INVALID_ARG
     assert srch(G, 3, ws=16) == P._lib.ERR_WORKSPACE
-    assert P.gptq_awq_search_workspace_size(4096, 4096) >= 4096 * 32 * 8
+    assert P.gptq_awq_search_workspace_size(4096, 4096, 128) >= 64 * 32 * 32 * 8
+    assert P.gptq_awq_search_workspace_size(4096, 4096, 0) == 0
     assert P.gptq_awq_sumsq_workspace_size(262144, 4096) > 0
     # AWQ quantize: null factors
     assert L.gptq_awq_quantize(fake, 1, 8, 256, None, 4, 128, fake, fake, fake, None, None) == P._lib.ERR_INVALID_ARG
