@@ -247,6 +247,45 @@ int gptq_awq_quantize(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t 
                       const float* s, int32_t bits, int32_t group_size, uint8_t* codes,
                       float* scales, int32_t* zeros, float* Qhat, hipStream_t s_stream);
 
+/* ---------------------------------------------------------------- one decoder block
+ * The forward pieces that layer-by-layer quantization needs between the
+ * sub-layers of a Llama decoder block ("GPTQ/AWQ量化导出：让大模型在消费级显卡上
+ * 跑起来": a calibration forward pass collects each layer's inputs and the
+ * layers are quantized one after another; "大模型压缩量化技术：GPTQ 与 AWQ 原理
+ * 详解 + Python 实战教程": one layer at a time, its curvature from running the
+ * calibration data through it).  fp32 throughout; token-major [T x d]. */
+
+/* Y[t] = X[t] / sqrt(mean_j X[t][j]^2 + eps) * gamma (gamma NULL: 1).
+ *  X [n_tokens x d] of x_dtype; Y [n_tokens x d] fp32. */
+int gptq_rmsnorm(const void* X, gptq_dtype x_dtype, int64_t n_tokens, int32_t d,
+                 const float* gamma, float eps, float* Y, hipStream_t s);
+
+/* Y = X W^T (+ R): X [n_tokens x d_in], W [d_out x d_in] (e.g. the dequantized
+ * Q of gptq_quantize_layer), R and Y [n_tokens x d_out]; R may be NULL or
+ * equal to Y (then Y is accumulated into).  n_tokens <= INT_MAX.
+ *  ws  scratch of gptq_linear_workspace_size(d_out, d_in) bytes (W^T). */
+size_t gptq_linear_workspace_size(int32_t d_out, int32_t d_in);
+int gptq_linear(const float* X, int64_t n_tokens, int32_t d_in, const float* W, int32_t d_out,
+                const float* R, float* Y, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Causal self-attention of the block: q = x1 Wq^T, k = x1 Wk^T, v = x1 Wv^T
+ * ([d x d] each); q and k rotated per head (pairs (i, i + hd/2) by
+ * p * rope_base^(-2i/hd), p = t % seq_len); per sequence of seq_len tokens and
+ * per head: softmax(q_h k_h^T / sqrt(hd)) over positions <= the query's,
+ * times v_h; out [n_tokens x d] is the heads side by side (the o projection's
+ * input).  hd = d / n_heads must be even; n_tokens a multiple of seq_len and
+ * at most 65535 * 32.
+ *  ws  scratch of gptq_block_attention_workspace_size(...) bytes (W^T, q, k,
+ *      v, k^T, one sequence's scores per head, the rotation table). */
+size_t gptq_block_attention_workspace_size(int64_t n_tokens, int32_t d, int32_t n_heads,
+                                           int32_t seq_len);
+int gptq_block_attention(const float* x1, int64_t n_tokens, int32_t d, int32_t n_heads,
+                         int32_t seq_len, const float* Wq, const float* Wk, const float* Wv,
+                         float rope_base, float* out, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* M = silu(G) * U elementwise, silu(x) = x / (1 + exp(-x)); n elements. */
+int gptq_swiglu(const float* G, const float* U, int64_t n, float* M, hipStream_t s);
+
 /* ---------------------------------------------------------------- misc */
 const char* gptq_status_string(int status);
 int gptq_abi_version(void);

@@ -70,6 +70,13 @@ def lib() -> ctypes.CDLL:
                                                vp]),
             "gptq_awq_quantize": (ctypes.c_int, [vp, ctypes.c_int, i32, i32, vp, i32, i32, vp, vp, vp,
                                                  vp, vp]),
+            "gptq_rmsnorm": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, vp, ctypes.c_float, vp, vp]),
+            "gptq_linear_workspace_size": (sz, [i32, i32]),
+            "gptq_linear": (ctypes.c_int, [vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]),
+            "gptq_block_attention_workspace_size": (sz, [i64, i32, i32, i32]),
+            "gptq_block_attention": (ctypes.c_int, [vp, i64, i32, i32, i32, vp, vp, vp, ctypes.c_float,
+                                                    vp, vp, sz, vp]),
+            "gptq_swiglu": (ctypes.c_int, [vp, vp, i64, vp, vp]),
             "gptq_layer_error_workspace_size": (sz, [i32, i32]),
             "gptq_layer_error": (ctypes.c_int, [vp, vp, ctypes.c_int, vp, i32, i32,
                                                 ctypes.POINTER(ctypes.c_double), vp, sz, vp]),
@@ -88,7 +95,8 @@ EXPORTED = ("gptq_hessian_workspace_size", "gptq_hessian_accumulate",
             "gptq_quantize_workspace_size", "gptq_quantize_layer", "gptq_pack_int4",
             "gptq_pack_dense", "gptq_w4a16_gemm", "gptq_awq_sumsq_workspace_size",
             "gptq_awq_act_sumsq", "gptq_awq_search_workspace_size", "gptq_awq_search",
-            "gptq_awq_quantize",
+            "gptq_awq_quantize", "gptq_rmsnorm", "gptq_linear_workspace_size", "gptq_linear",
+            "gptq_block_attention_workspace_size", "gptq_block_attention", "gptq_swiglu",
             "gptq_layer_error_workspace_size", "gptq_layer_error", "gptq_status_string",
             "gptq_abi_version")
 
@@ -273,6 +281,54 @@ def gptq_awq_quantize(W: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, sca
     _check(lib().gptq_awq_quantize(_ptr(W), _DTYPE[W.dtype], d_out, d_in, _ptr(s), bits, group_size,
                                    _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(Qhat),
                                    _stream(stream)), "gptq_awq_quantize")
+
+
+def gptq_rmsnorm(X: torch.Tensor, Y: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+                 eps: float = 1e-6, stream=None) -> None:
+    _dev(X, "X"); _dev(Y, "Y")
+    n, d = X.shape
+    assert Y.dtype == torch.float32 and Y.shape == (n, d)
+    _check(lib().gptq_rmsnorm(_ptr(X), _DTYPE[X.dtype], n, d, _ptr(gamma), float(eps), _ptr(Y),
+                              _stream(stream)), "gptq_rmsnorm")
+
+
+def gptq_linear_workspace_size(d_out: int, d_in: int) -> int:
+    return int(lib().gptq_linear_workspace_size(d_out, d_in))
+
+
+def gptq_linear(X: torch.Tensor, W: torch.Tensor, Y: torch.Tensor, R: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    _dev(X, "X"); _dev(W, "W"); _dev(Y, "Y")
+    n, d_in = X.shape
+    d_out = W.shape[0]
+    assert W.shape == (d_out, d_in) and Y.shape == (n, d_out)
+    assert X.dtype == W.dtype == Y.dtype == torch.float32
+    ws = _ws(gptq_linear_workspace_size(d_out, d_in), ws, X.device)
+    _check(lib().gptq_linear(_ptr(X), n, d_in, _ptr(W), d_out, _ptr(R), _ptr(Y), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)), "gptq_linear")
+
+
+def gptq_block_attention_workspace_size(n_tokens: int, d: int, n_heads: int, seq_len: int) -> int:
+    return int(lib().gptq_block_attention_workspace_size(n_tokens, d, n_heads, seq_len))
+
+
+def gptq_block_attention(x1: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor, Wv: torch.Tensor,
+                         out: torch.Tensor, n_heads: int, seq_len: int, rope_base: float = 10000.0,
+                         ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    for t, n in ((x1, "x1"), (Wq, "Wq"), (Wk, "Wk"), (Wv, "Wv"), (out, "out")):
+        _dev(t, n)
+    T, d = x1.shape
+    ws = _ws(gptq_block_attention_workspace_size(T, d, n_heads, seq_len), ws, x1.device)
+    _check(lib().gptq_block_attention(_ptr(x1), T, d, n_heads, seq_len, _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                      float(rope_base), _ptr(out), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)),
+           "gptq_block_attention")
+
+
+def gptq_swiglu(G: torch.Tensor, U: torch.Tensor, M: torch.Tensor, stream=None) -> None:
+    _dev(G, "G"); _dev(U, "U"); _dev(M, "M")
+    assert G.shape == U.shape == M.shape
+    _check(lib().gptq_swiglu(_ptr(G), _ptr(U), G.numel(), _ptr(M), _stream(stream)), "gptq_swiglu")
 
 
 def gptq_layer_error_workspace_size(d_out: int, d_in: int) -> int:

@@ -106,6 +106,20 @@ def test_argument_validation_before_any_launch(L):
     assert P.gptq_awq_search_workspace_size(4096, 4096, 128) >= 64 * 32 * 32 * 8
     assert P.gptq_awq_search_workspace_size(4096, 4096, 0) == 0
     assert P.gptq_awq_sumsq_workspace_size(262144, 4096) > 0
+    # block pieces: shapes that do not fit, null pointers, workspace
+    assert L.gptq_rmsnorm(fake, 7, 4, 16, None, ctypes.c_float(1e-6), fake, None) == P._lib.ERR_INVALID_ARG
+    assert L.gptq_rmsnorm(None, 0, 4, 16, None, ctypes.c_float(1e-6), fake, None) == P._lib.ERR_INVALID_ARG
+    assert L.gptq_linear(fake, 4, 16, fake, 8, None, fake, fake, 8, None) == P._lib.ERR_WORKSPACE
+    assert L.gptq_linear(fake, 4, 16, None, 8, None, fake, fake, 1 << 20, None) == P._lib.ERR_INVALID_ARG
+    assert P.gptq_block_attention_workspace_size(100, 256, 2, 64) == 0       # tokens not whole sequences
+    assert P.gptq_block_attention_workspace_size(128, 256, 3, 64) == 0       # heads do not divide d
+    assert P.gptq_block_attention_workspace_size(128, 256, 2, 64) > 3 * 128 * 256 * 4
+    assert L.gptq_block_attention(fake, 100, 256, 2, 64, fake, fake, fake, ctypes.c_float(1e4), fake,
+                                  fake, 1 << 30, None) == P._lib.ERR_INVALID_ARG
+    assert L.gptq_block_attention(fake, 128, 256, 2, 64, fake, fake, fake, ctypes.c_float(1e4), fake,
+                                  fake, 16, None) == P._lib.ERR_WORKSPACE
+    assert L.gptq_swiglu(fake, None, 8, fake, None) == P._lib.ERR_INVALID_ARG
+    assert L.gptq_swiglu(fake, fake, 0, fake, None) == P._lib.OK
     # AWQ quantize: null factors
     assert L.gptq_awq_quantize(fake, 1, 8, 256, None, 4, 128, fake, fake, fake, None, None) == P._lib.ERR_INVALID_ARG
 

@@ -1,0 +1,207 @@
+"""GPU parity of the decoder-block pieces and of layer-sequential GPTQ over a
+Llama-shaped block, against the float64 block oracle, through the C ABI.
+
+The pieces get identical fp32 inputs on both sides; the GPU computes in fp32,
+so they agree to fp32 rounding of sums (bars below).  Every sub-layer is held
+to the whole-layer bars of the single-layer tests (codes >= 99.9 % equal, each
+row's first disagreement a rounding tie, scales within 1e-3, the objective
+within 1e-3) and its Hessian to 1e-4 of sqrt(H_ii H_jj).
+
+End to end (each side quantizes with its own Hessians and propagates its own
+quantized sub-layers) on small blocks, where no tie flips.  On larger blocks
+one tie flip upstream changes every later stage's calibration inputs (both
+results are correct GPTQ runs), so there each stage gets the oracle's
+upstream weights and is compared with the oracle's stage."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gptq_inputs as gi
+from oracle import block_ref as B
+
+from gpu_helpers import compare_quant, say, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import post_weight_quantization_29_amd as P
+    P.lib()
+    yield
+
+
+def _dev32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_rmsnorm(dtype):
+    import post_weight_quantization_29_amd as P
+    rng = np.random.default_rng(0)
+    x = gi.cast_storage((rng.standard_normal((37, 264)) * 3).astype(np.float32), dtype)
+    gam = rng.uniform(0.5, 1.5, 264).astype(np.float32)
+    Y = torch.empty((37, 264), dtype=torch.float32, device="cuda")
+    P.gptq_rmsnorm(to_dev(x, dtype), Y, _dev32(gam))
+    ref = B.rmsnorm(gi.to_float64(x, dtype), gam.astype(np.float64))
+    rel = np.max(np.abs(Y.cpu().numpy() - ref) / (np.abs(ref) + 1e-30))
+    say(f"[rmsnorm {dtype}] max rel {rel:.2e}")
+    assert rel <= 2e-6
+
+
+def test_linear_with_residual():
+    import post_weight_quantization_29_amd as P
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((300, 264)).astype(np.float32)
+    W = (rng.standard_normal((200, 264)) * 0.05).astype(np.float32)
+    R = rng.standard_normal((300, 200)).astype(np.float32)
+    Y = torch.empty((300, 200), dtype=torch.float32, device="cuda")
+    P.gptq_linear(_dev32(x), _dev32(W), Y, R=_dev32(R))
+    Y2 = _dev32(R)
+    P.gptq_linear(_dev32(x), _dev32(W), Y2, R=Y2)            # in place accumulation
+    x64, W64 = x.astype(np.float64), W.astype(np.float64)
+    ref = x64 @ W64.T + R
+    bound = np.abs(x64) @ np.abs(W64).T + np.abs(R)
+    for out in (Y, Y2):
+        err = np.max(np.abs(out.cpu().numpy() - ref) / bound)
+        say(f"[linear] max |dY|/bound {err:.2e}")
+        assert err <= 2e-6
+
+
+@pytest.mark.parametrize("T,d,heads,S", [(512, 256, 2, 128), (320, 320, 5, 64), (96, 320, 40, 32)])
+def test_attention(T, d, heads, S):
+    import post_weight_quantization_29_amd as P
+    rng = np.random.default_rng(T + d + heads)
+    x1 = B.rmsnorm(rng.standard_normal((T, d))).astype(np.float32)
+    Ws = [(rng.standard_normal((d, d)) * 0.08).astype(np.float32) for _ in range(3)]
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    P.gptq_block_attention(_dev32(x1), *[_dev32(w) for w in Ws], out, heads, S)
+    x64 = x1.astype(np.float64)
+    q = B.rope(B.linear(x64, Ws[0]), heads, S)
+    k = B.rope(B.linear(x64, Ws[1]), heads, S)
+    v = B.linear(x64, Ws[2])
+    ref = B.causal_attention(q, k, v, heads, S)
+    err = np.max(np.abs(out.cpu().numpy() - ref)) / np.max(np.abs(ref))
+    say(f"[attention T={T} d={d} heads={heads} S={S}] max |d|/max|ref| {err:.2e}")
+    assert err <= 2e-5
+
+
+def test_swiglu():
+    import post_weight_quantization_29_amd as P
+    rng = np.random.default_rng(2)
+    g, u = (rng.standard_normal(1001).astype(np.float32) * 4 for _ in range(2))
+    m = torch.empty(1001, dtype=torch.float32, device="cuda")
+    P.gptq_swiglu(_dev32(g), _dev32(u), m)
+    ref = B.silu(g.astype(np.float64)) * u
+    assert np.max(np.abs(m.cpu().numpy() - ref) / (np.abs(ref) + 1e-30)) <= 1e-6
+
+
+def _block_case(d, heads, f, S, T, desc, seed, G=128):
+    import post_weight_quantization_29_amd as P
+    rng = np.random.default_rng(seed)
+    shape = B.BlockShape(d=d, n_heads=heads, f=f, seq_len=S)
+    W = {n: (rng.standard_normal((d, d)) * 0.02).astype(np.float16) for n in ("q", "k", "v", "o")}
+    W["gate"] = (rng.standard_normal((f, d)) * 0.02).astype(np.float16)
+    W["up"] = (rng.standard_normal((f, d)) * 0.02).astype(np.float16)
+    W["down"] = (rng.standard_normal((d, f)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    x[:, rng.choice(d, max(1, d // 64), replace=False)] *= 8.0       # a few outlier channels
+    say(f"[block] d={d} heads={heads} f={f} S={S} T={T} desc_act={desc}")
+    cfg = P.make_config(bits=4, group_size=G, desc_act=desc)
+    res = P.quantize_block_sequential(_dev32(x), {n: torch.from_numpy(w).cuda() for n, w in W.items()},
+                                      P.BlockShape(d, heads, f, S), cfg, keep=True)
+    torch.cuda.synchronize()
+    W64 = {n: w.astype(np.float64) for n, w in W.items()}
+    ref = B.sequential_gptq(x.astype(np.float64), B.BlockWeights(W64), shape,
+                            B.gptq_quantizer(bits=4, group_size=G, desc_act=bool(desc)))
+    failures = []
+    for n in B.SUBLAYERS:
+        Hg = res.H[n].cpu().numpy().astype(np.float64)
+        Hr = ref.H[n]
+        dg = np.sqrt(np.diag(Hr))
+        herr = float(np.max(np.abs(Hg - Hr) / np.outer(dg, dg)))
+        q = res.quant[n]
+        par = compare_quant(ref.quant[n], W64[n], Hr, q.codes.cpu().numpy(), q.scales.cpu().numpy(),
+                            q.zeros.cpu().numpy(), q.Q.cpu().numpy(), G)
+        say(f"  {n}: H err {herr:.1e}; {par}")
+        ok = (herr <= 1e-4 and par.agree >= 0.999 and par.first_not_tie == 0 and par.scale_rel <= 1e-3
+              and par.zero_mismatch == 0 and par.q_bad == 0 and par.obj_rel <= 1e-3)
+        if not ok:
+            failures.append(n)
+    y = res.y.cpu().numpy()
+    yerr = np.max(np.abs(y - ref.acts["y"])) / np.max(np.abs(ref.acts["y"]))
+    say(f"  block output: max |dy|/max|y| {yerr:.2e}")
+    assert not failures, failures
+    assert yerr <= 1e-3
+
+
+def _stagewise_case(d, heads, f, S, T, desc, seed, G=128):
+    """Each stage on the GPU gets the oracle's dequantized weights of the
+    stages before it (and computes the stage's own forward, Hessian and
+    quantization), so every stage is compared with the same upstream; the
+    chaotic effect of tie flips on later stages is left out."""
+    import post_weight_quantization_29_amd as P
+    from post_weight_quantization_29_amd import block as PB
+    rng = np.random.default_rng(seed)
+    shape = B.BlockShape(d=d, n_heads=heads, f=f, seq_len=S)
+    W = {n: (rng.standard_normal((d, d)) * 0.02).astype(np.float16) for n in ("q", "k", "v", "o")}
+    W["gate"] = (rng.standard_normal((f, d)) * 0.02).astype(np.float16)
+    W["up"] = (rng.standard_normal((f, d)) * 0.02).astype(np.float16)
+    W["down"] = (rng.standard_normal((d, f)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    x[:, rng.choice(d, max(1, d // 64), replace=False)] *= 8.0
+    say(f"[block stages] d={d} heads={heads} f={f} S={S} T={T} desc_act={desc}")
+    W64 = {n: w.astype(np.float64) for n, w in W.items()}
+    ref = B.sequential_gptq(x.astype(np.float64), B.BlockWeights(W64), shape,
+                            B.gptq_quantizer(bits=4, group_size=G, desc_act=bool(desc)))
+    RQ = {n: _dev32(ref.quant[n].Q) for n in B.SUBLAYERS}
+    cfg = P.make_config(bits=4, group_size=G, desc_act=desc)
+    Wd = {n: torch.from_numpy(w).cuda() for n, w in W.items()}
+    xd = _dev32(x)
+    pshape = P.BlockShape(d, heads, f, S)
+    x1, H1, q1 = PB.stage_qkv(xd, Wd, cfg)
+    attn, H2, q2 = PB.stage_o(x1, RQ["q"], RQ["k"], RQ["v"], Wd, cfg, pshape)
+    h, x2, H3, q3 = PB.stage_gate_up(xd, attn, RQ["o"], Wd, cfg)
+    m, H4, q4 = PB.stage_down(x2, RQ["gate"], RQ["up"], Wd, cfg, pshape)
+    y = PB.block_output(m, h, RQ["down"])
+    torch.cuda.synchronize()
+    got = {**q1, **q2, **q3, **q4}
+    Hg = dict(q=H1, k=H1, v=H1, o=H2, gate=H3, up=H3, down=H4)
+    failures = []
+    for n in B.SUBLAYERS:
+        Hn = Hg[n].cpu().numpy().astype(np.float64)
+        Hr = ref.H[n]
+        dg = np.sqrt(np.diag(Hr))
+        herr = float(np.max(np.abs(Hn - Hr) / np.outer(dg, dg)))
+        q = got[n]
+        # down's input m = silu(x2 Qg^T) * (x2 Qu^T) comes out of two fp32 GEMMs
+        # and a gate: its H is ~5x further from the float64 one (3.5e-6 against
+        # 6e-7 for the other inputs), and after 2752 columns of compensation a
+        # row's first differing code can sit just outside the 1e-3 tie window;
+        # the window is 1e-2 there, as for the ill-conditioned single-layer cases
+        tie = 1e-2 if n == "down" else 1e-3
+        par = compare_quant(ref.quant[n], W64[n], Hr, q.codes.cpu().numpy(), q.scales.cpu().numpy(),
+                            q.zeros.cpu().numpy(), q.Q.cpu().numpy(), G, tie_tol=tie)
+        say(f"  {n}: H err {herr:.1e}; {par}")
+        if not (herr <= 1e-4 and par.agree >= 0.999 and par.first_not_tie == 0 and par.scale_rel <= 1e-3
+                and par.zero_mismatch == 0 and par.q_bad == 0 and par.obj_rel <= 1e-3):
+            failures.append(n)
+    yerr = np.max(np.abs(y.cpu().numpy() - ref.acts["y"])) / np.max(np.abs(ref.acts["y"]))
+    say(f"  block output: max |dy|/max|y| {yerr:.2e}")
+    assert not failures, failures
+    assert yerr <= 1e-5
+
+
+@pytest.mark.parametrize("desc", [0, 1])
+def test_sequential_small_block(desc):
+    _block_case(d=256, heads=2, f=512, S=128, T=1024, desc=desc, seed=10 + desc)
+
+
+def test_block_stages_llama_head_dim():
+    """Eight heads of 128, an intermediate of 2752 (the 7B model's ratio), 4096
+    calibration tokens in 16 sequences of 256, desc_act; stage by stage."""
+    _stagewise_case(d=1024, heads=8, f=2752, S=256, T=4096, desc=1, seed=20)
