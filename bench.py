@@ -12,7 +12,9 @@ events on the stream the library launches on.  The cpu_baseline object times
 the float64 CPU oracle on a bounded sample of the same workload.  Two more
 objects time the widened rows on the same inputs: w4a16_decode (the product on
 the packed layer at one activation row) and awq (the activation-aware
-quantization of the same layer from the same calibration tokens).
+quantization of the same layer from the same calibration tokens); a third,
+block_sequential, times layer-by-layer GPTQ over a Llama-7B-shaped decoder
+block on 32,768 of the calibration tokens.
 """
 from __future__ import annotations
 
@@ -218,6 +220,58 @@ def awq_measure(P, torch, Wg, Xg, reps=5):
             "grid": len(grid)}
 
 
+def block_measure(P, torch, Xg, n_tokens=32768, seq_len=2048):
+    """Layer-sequential GPTQ over one Llama-7B-shaped decoder block (d 4096,
+    32 heads of 128, intermediate 11008; random fp16 weights N(0, 0.02)) on
+    the first n_tokens calibration tokens (as fp32), 4-bit groups of 128:
+    q/k/v share one Hessian and factor, then o, gate/up, down, each from the
+    quantized stages before it.  HIP events per stage, one warm-up run."""
+    from post_weight_quantization_29_amd import block as PB
+    d, f, heads = 4096, 11008, 32
+    dev = Xg.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    shapes = {"q": (d, d), "k": (d, d), "v": (d, d), "o": (d, d), "gate": (f, d), "up": (f, d),
+              "down": (d, f)}
+    W = {n: (torch.randn(s, device=dev, generator=g) * 0.02).half() for n, s in shapes.items()}
+    x = Xg[:n_tokens].float().contiguous()
+    cfg = P.make_config(bits=4, group_size=128)
+    shape = PB.BlockShape(d, heads, f, seq_len)
+    stream = torch.cuda.current_stream()
+
+    def run(ev=None):
+        if ev:
+            ev[0].record(stream)
+        x1, _, qz = PB.stage_qkv(x, W, cfg)
+        if ev:
+            ev[1].record(stream)
+        attn, _, qo = PB.stage_o(x1, qz["q"].Q, qz["k"].Q, qz["v"].Q, W, cfg, shape)
+        if ev:
+            ev[2].record(stream)
+        h, x2, _, qgu = PB.stage_gate_up(x, attn, qo["o"].Q, W, cfg)
+        if ev:
+            ev[3].record(stream)
+        m, _, qd = PB.stage_down(x2, qgu["gate"].Q, qgu["up"].Q, W, cfg, shape)
+        if ev:
+            ev[4].record(stream)
+        PB.block_output(m, h, qd["down"].Q)
+        if ev:
+            ev[5].record(stream)
+
+    run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    run(ev)
+    torch.cuda.synchronize()
+    names = ["qkv", "o", "gate_up", "down", "output"]
+    ms = {n: ev[k].elapsed_time(ev[k + 1]) for k, n in enumerate(names)}
+    total = sum(ms.values())
+    weights = sum(a * b for a, b in shapes.values())
+    return {"shape": {"d": d, "heads": heads, "f": f, "seq_len": seq_len, "n_tokens": n_tokens},
+            "stages_ms": {k: round(v, 3) for k, v in ms.items()}, "ms_per_block": round(total, 3),
+            "weights_per_s": weights / (total / 1e3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -356,6 +410,7 @@ def main():
     }
     out["w4a16_decode"] = w4a16_measure(P, torch, packed, scales, zeros, q.group_size)
     out["awq"] = awq_measure(P, torch, Wg, Xg)
+    out["block_sequential"] = block_measure(P, torch, Xg)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(W, X, wl, args)
