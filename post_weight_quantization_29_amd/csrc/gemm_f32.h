@@ -244,43 +244,38 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
   }
 }
 
-// C = alpha * sum_p partial[tile][p] + beta * C, parts added in order.  One
-// workgroup per tile; thread t handles elements t + 256i of the tile's 16384
-// in partial order (reads fully coalesced).
+// C = alpha * sum_p partial[tile][p] + beta * C, parts added in order.
+// kRedSlices workgroups per tile (so that launches of a few tiles still spread
+// over the chip); thread t of slice s handles elements s*1024 + t + 256u,
+// u = 0..3, of the tile's 16384 in partial order (reads fully coalesced).
+constexpr int kRedSlices = 16;
 static __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmGroup grp, const float* __restrict__ partial,
                                                           int parts, float alpha, float beta) {
-  const int wg = blockIdx.x;
+  const int wg = blockIdx.x / kRedSlices, slice = blockIdx.x % kRedSlices;
   int pi = 0;
   while (pi + 1 < grp.count && grp.tile_start[pi + 1] <= wg) ++pi;
   const GemmProblem P = grp.p[pi];
   const int local = wg - grp.tile_start[pi];
   const int tn = (P.N + kGT - 1) / kGT;
   const int m0 = (local / tn) * kGT, n0 = (local % tn) * kGT;
-  const float* src = partial + (size_t)wg * parts * 16384;
-  for (int i = 0; i < 64; i += 16) {
-    float sum[16];
+  const float* src = partial + (size_t)wg * parts * 16384 + slice * 1024;
+  float sum[4];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) sum[u] = 0.0f;
-    for (int p = 0; p < parts; ++p) {
+  for (int u = 0; u < 4; ++u) sum[u] = 0.0f;
+  for (int p = 0; p < parts; ++p) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) sum[u] += src[(size_t)p * 16384 + threadIdx.x + 256 * (i + u)];
+    for (int u = 0; u < 4; ++u) sum[u] += src[(size_t)p * 16384 + threadIdx.x + 256 * u];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = slice * 1024 + threadIdx.x + 256 * u;
+    const int w = e >> 12, blk = (e >> 10) & 3, r = (e >> 6) & 15, lane = e & 63;
+    const int m = m0 + (w >> 1) * 64 + (blk >> 1) * 32 + mfma32_row(r, lane);
+    const int n = n0 + (w & 1) * 64 + (blk & 1) * 32 + mfma32_col(lane);
+    if (m < P.M && n < P.N) {
+      const size_t off = (size_t)m * P.ldc + n;
+      P.C[off] = (beta != 0.0f) ? alpha * sum[u] + beta * P.C[off] : alpha * sum[u];
     }
-    float cold[16];
-    size_t off[16];
-    bool ok[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = threadIdx.x + 256 * (i + u);
-      const int w = e >> 12, blk = (e >> 10) & 3, r = (e >> 6) & 15, lane = e & 63;
-      const int m = m0 + (w >> 1) * 64 + (blk >> 1) * 32 + mfma32_row(r, lane);
-      const int n = n0 + (w & 1) * 64 + (blk & 1) * 32 + mfma32_col(lane);
-      ok[u] = m < P.M && n < P.N;
-      off[u] = ok[u] ? (size_t)m * P.ldc + n : 0;
-      cold[u] = (ok[u] && beta != 0.0f) ? P.C[off[u]] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (ok[u]) P.C[off[u]] = alpha * sum[u] + beta * cold[u];
   }
 }
 
@@ -347,7 +342,7 @@ inline void launch_gemm_group_splitk(GemmGroup& g, int parts, float alpha, float
   else
     gemm_f32_kernel<A_KMAJOR, kPartial, false><<<t * parts, 256, 0, s>>>(g, alpha, beta, kloFromM, khiFromN,
                                                                          0, pp, parts);
-  gemm_splitk_reduce<<<t, 256, 0, s>>>(g, partial, parts, alpha, beta);
+  gemm_splitk_reduce<<<t * kRedSlices, 256, 0, s>>>(g, partial, parts, alpha, beta);
 }
 
 template <bool A_KMAJOR>
