@@ -279,6 +279,90 @@ static __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmGroup grp, 
   }
 }
 
+// ---------------------------------------------------------------- small tiles
+// The same product in 64x64 tiles (four waves of 32x32, one MFMA accumulator
+// each), for launches with fewer 128x128 tiles than the chip has CUs: four
+// times the workgroups, a quarter of the work each.  Every element takes the
+// same MFMA steps in the same k order as in the 128x128 kernel, so the results
+// are identical.  upperOnly skips at 128-column-block granularity, like the
+// large kernel (the diagonal 128-blocks are computed whole).
+constexpr int kST = 64;            // small tile edge
+constexpr int kSP = kST + 4;       // LDS pitch (floats)
+
+template <bool A_KMAJOR, bool VEC>
+__global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmProblem P, float alpha, float beta,
+                                                             int upperOnly) {
+  __shared__ __attribute__((aligned(16))) float sA[kGK * kSP];
+  __shared__ __attribute__((aligned(16))) float sB[kGK * kSP];
+  const int tn = (P.N + kST - 1) / kST;
+  const int m0 = ((int)blockIdx.x / tn) * kST, n0 = ((int)blockIdx.x % tn) * kST;
+  if (upperOnly && (n0 / kGT) < (m0 / kGT)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  float cold[16];
+  if (beta != 0.0f) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 32 + mfma32_row(r, lane), n = n0 + wn * 32 + mfma32_col(lane);
+      cold[r] = (m < P.M && n < P.N) ? P.C[(size_t)m * P.ldc + n] : 0.0f;
+    }
+  }
+  // chunk loads: B (and k-major A) rows k = tid/16 + 16i, columns 4(tid%16) .. +3;
+  // m-major A rows m = tid/16 + 16i, k = 4(tid%16) .. +3
+  auto gload = [&](int k0, float4 (&ra)[4], float4 (&rb)[4]) {
+    const int c4 = 4 * (tid & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + (tid >> 4) + 16 * i;
+      const bool kv = k < P.K;
+      rb[i] = kv ? load4<VEC>(P.B + (size_t)k * P.ldb + n0 + c4, P.N - n0 - c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (A_KMAJOR)
+        ra[i] = kv ? load4<VEC>(P.A + (size_t)k * P.lda + m0 + c4, P.M - m0 - c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      else {
+        const int m = m0 + (tid >> 4) + 16 * i, kq = k0 + c4;
+        ra[i] = (m < P.M) ? load4<VEC>(P.A + (size_t)m * P.lda + kq, P.K - kq) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  float4 ra[4], rb[4];
+  gload(0, ra, rb);
+  for (int k0 = 0; k0 < P.K; k0 += kGK) {
+    __syncthreads();
+    {
+      const int c4 = 4 * (tid & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kr = (tid >> 4) + 16 * i;
+        *reinterpret_cast<float4*>(sB + kr * kSP + c4) = rb[i];
+        if (A_KMAJOR) {
+          *reinterpret_cast<float4*>(sA + kr * kSP + c4) = ra[i];
+        } else {
+          sA[(c4 + 0) * kSP + kr] = ra[i].x;
+          sA[(c4 + 1) * kSP + kr] = ra[i].y;
+          sA[(c4 + 2) * kSP + kr] = ra[i].z;
+          sA[(c4 + 3) * kSP + kr] = ra[i].w;
+        }
+      }
+    }
+    __syncthreads();
+    if (k0 + kGK < P.K) gload(k0 + kGK, ra, rb);
+    const int kn = min(kGK, P.K - k0);
+#pragma unroll 4
+    for (int k2 = 0; k2 < kn; k2 += 2) {
+      const int row = (k2 + (lane >> 5)) * kSP + (lane & 31);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[row + wm * 32], sB[row + wn * 32], acc, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + wm * 32 + mfma32_row(r, lane), n = n0 + wn * 32 + mfma32_col(lane);
+    if (m < P.M && n < P.N) P.C[(size_t)m * P.ldc + n] = (beta != 0.0f) ? alpha * acc[r] + beta * cold[r] : alpha * acc[r];
+  }
+}
+
 inline int gemm_tiles(int M, int N) { return ((M + kGT - 1) / kGT) * ((N + kGT - 1) / kGT); }
 
 // Parts per tile for a launch of `tiles` tiles whose longest contraction is
@@ -350,6 +434,24 @@ inline void gemm_f32(const float* A, int lda, const float* B, int ldb, float* C,
                      int N, int K, float alpha, float beta, int kloFromM, int khiFromN, int upperOnly,
                      hipStream_t s) {
   if (M <= 0 || N <= 0) return;
+  // launches of few large tiles (counting only those upperOnly keeps) take 64x64 tiles
+  if (!kloFromM && !khiFromN) {
+    const int tm = (M + kGT - 1) / kGT, tn = (N + kGT - 1) / kGT;
+    int t128 = tm * tn;
+    if (upperOnly) {
+      t128 = 0;
+      for (int i = 0; i < tm; ++i) t128 += std::max(0, tn - i);
+    }
+    if (t128 < 192) {
+      const GemmProblem P{A, B, C, nullptr, lda, ldb, ldc, M, N, K};
+      const unsigned grid = (unsigned)(((M + kST - 1) / kST) * ((N + kST - 1) / kST));
+      const bool vec = (lda % 4 == 0) && (ldb % 4 == 0) &&
+                       ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+      if (vec) gemm_f32_small_kernel<A_KMAJOR, true><<<grid, 256, 0, s>>>(P, alpha, beta, upperOnly);
+      else gemm_f32_small_kernel<A_KMAJOR, false><<<grid, 256, 0, s>>>(P, alpha, beta, upperOnly);
+      return;
+    }
+  }
   GemmGroup g;
   g.count = 1;
   g.p[0] = GemmProblem{A, B, C, nullptr, lda, ldb, ldc, M, N, K};
