@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows in the oracle's column-loop sample (result scaled to all rows)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hessian_c2_traffic.json"))
+    ap.add_argument("--no-extras", action="store_true",
+                    help="report the GPTQ step only (no w4a16_decode, awq, block_sequential objects), "
+                         "e.g. for a kernel trace of the step alone")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -408,9 +411,10 @@ def main():
                                 "+ diag_reduce_kernel"),
                      "work_per_launch": f"N*d*(d+1) = {h_flops:.4g} flop"},
     }
-    out["w4a16_decode"] = w4a16_measure(P, torch, packed, scales, zeros, q.group_size)
-    out["awq"] = awq_measure(P, torch, Wg, Xg)
-    out["block_sequential"] = block_measure(P, torch, Xg)
+    if not args.no_extras:
+        out["w4a16_decode"] = w4a16_measure(P, torch, packed, scales, zeros, q.group_size)
+        out["awq"] = awq_measure(P, torch, Wg, Xg)
+        out["block_sequential"] = block_measure(P, torch, Xg)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(W, X, wl, args)

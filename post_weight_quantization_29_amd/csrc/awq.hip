@@ -116,25 +116,37 @@ __global__ __launch_bounds__(256) void sumsq_reduce_kernel(const double* __restr
   a[j] += s;
 }
 
-// mask_j = 1 when fewer than ktop channels rank above j (a larger a, or an
-// equal a at a lower index): the top-ktop channels, ties to the lower index.
-__global__ __launch_bounds__(256) void rank_kernel(const double* __restrict__ a, int d, int ktop,
-                                                   uint8_t* __restrict__ mask) {
-  __shared__ double sa[256];
+// above_j = the number of channels ranking above j (a larger a, or an equal a
+// at a lower index), counted over channel chunks of kRankChunk (grid.y) and
+// added with integer atomics (exact in any order); then mask_j = 1 when
+// above_j < ktop: the top-ktop channels, ties to the lower index.
+constexpr int kRankChunk = 256;
+__global__ __launch_bounds__(256) void rank_count_kernel(const double* __restrict__ a, int d,
+                                                         int* __restrict__ above) {
+  __shared__ double sa[kRankChunk];
   const int j = blockIdx.x * 256 + threadIdx.x;
+  const int k0 = blockIdx.y * kRankChunk;
   const double aj = (j < d) ? a[j] : 0.0;
-  int above = 0;
-  for (int k0 = 0; k0 < d; k0 += 256) {
-    __syncthreads();
-    sa[threadIdx.x] = (k0 + (int)threadIdx.x < d) ? a[k0 + threadIdx.x] : 0.0;
-    __syncthreads();
-    const int kn = min(256, d - k0);
-    for (int u = 0; u < kn; ++u) {
-      const double ak = sa[u];
-      above += (ak > aj) || (ak == aj && k0 + u < j);
-    }
+  sa[threadIdx.x] = (k0 + (int)threadIdx.x < d) ? a[k0 + threadIdx.x] : 0.0;
+  __syncthreads();
+  const int kn = min(kRankChunk, d - k0);
+  int cnt = 0;
+  for (int u = 0; u < kn; ++u) {
+    const double ak = sa[u];
+    cnt += (ak > aj) || (ak == aj && k0 + u < j);
   }
-  if (j < d) mask[j] = (above < ktop) ? 1 : 0;
+  if (j < d && cnt) atomicAdd(above + j, cnt);
+}
+
+__global__ __launch_bounds__(256) void rank_mask_kernel(int* __restrict__ above, int d, int ktop,
+                                                        uint8_t* __restrict__ mask) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < d) mask[j] = (above[j] < ktop) ? 1 : 0;
+}
+
+__global__ __launch_bounds__(256) void zero_int_kernel(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 // The asymmetric min-max grid of [mn, mx] with correctly rounded divisions.
@@ -395,14 +407,15 @@ static SumsqShape sumsq_shape(int64_t n, int d) {
 }
 
 struct SearchLayout {
-  size_t off_mask, off_part, total;
+  size_t off_mask, off_above, off_part, total;
 };
 
 // partials: one per (64-row block, group)
 static SearchLayout search_layout(int d_out, int d, int G) {
   SearchLayout L;
   L.off_mask = 0;
-  L.off_part = align_up((size_t)d);
+  L.off_above = align_up((size_t)d);
+  L.off_part = align_up(L.off_above + (size_t)d * sizeof(int));
   const size_t nparts = (size_t)((d_out + 63) / 64) * ((d + G - 1) / G);
   L.total = align_up(L.off_part + nparts * kAwqMaxGrid * sizeof(double));
   return L;
@@ -481,7 +494,11 @@ extern "C" int gptq_awq_search(const void* W, gptq_dtype w_dtype, int32_t d_out,
   // k = top_frac * d_in rounded to nearest, halves up, in double
   const int ktop = (int)std::min<double>(d_in, std::floor((double)top_frac * d_in + 0.5));
 
-  rank_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(sumsq, d_in, ktop, mask);
+  int* above = reinterpret_cast<int*>(static_cast<char*>(ws) + L.off_above);
+  zero_int_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(above, d_in);
+  rank_count_kernel<<<dim3((d_in + 255) / 256, (d_in + kRankChunk - 1) / kRankChunk), 256, 0, s>>>(sumsq, d_in,
+                                                                                                 above);
+  rank_mask_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(above, d_in, ktop, mask);
   GPTQ_LAUNCH_CHECK();
   const int ng = (d_in + G - 1) / G;
   const dim3 sgrid((unsigned)((d_out + 63) / 64), (unsigned)((ng + 3) / 4),
