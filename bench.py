@@ -125,7 +125,9 @@ def cpu_baseline(W, X, wl, args):
 def w4a16_measure(P, torch, packed, scales, zeros, group_size, reps=24):
     """Decode-shaped product on packed layers (one activation row, bf16 in, fp32
     out): the quantized layer of this step, and a 70B down_proj-shaped packed
-    layer (8192 x 28672, random codes) for the HBM roofline.  The large layer
+    layer (8192 x 28672, random codes) for the HBM roofline; on the latter also
+    a prefill shape (2048 activation rows, the MFMA path) against the bf16 MFMA
+    peak.  The large layer
     is held in three copies used in turn, 3 x 132 MB, more than the 256 MB
     last-level cache, so each call streams its weights from HBM.  HIP events
     on the launch stream, mean over reps after a warm-up."""
@@ -162,6 +164,23 @@ def w4a16_measure(P, torch, packed, scales, zeros, group_size, reps=24):
         out.append({"shape": f"{d_out}x{d_in}", "m": 1, "us": round(us, 2), "bytes": nbytes,
                     "GB_per_s": round(nbytes / us / 1e3, 1),
                     "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)})
+        if len(copies) == 3:
+            # prefill shape on the same copies: 2048 activation rows (the tiled MFMA product)
+            mp = 2048
+            Xp = torch.randn((mp, d_in), device=dev, generator=g).to(torch.bfloat16)
+            Yp = torch.empty((mp, d_out), dtype=torch.float32, device=dev)
+            for c in copies:
+                P.gptq_w4a16_gemm(Xp, c[0], c[1], c[2], Yp, group_size=gs)
+            e0.record(stream)
+            for i in range(6):
+                c = copies[i % 3]
+                P.gptq_w4a16_gemm(Xp, c[0], c[1], c[2], Yp, group_size=gs)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 6
+            tf = 2.0 * mp * d_out * d_in / us / 1e6
+            out.append({"shape": f"{d_out}x{d_in}", "m": mp, "us": round(us, 1), "TFLOP_per_s": round(tf, 1),
+                        "frac_bf16_mfma": round(tf / PEAK_BF16_TFLOPS, 4)})
         del copies
     return out
 

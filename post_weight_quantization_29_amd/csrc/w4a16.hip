@@ -167,6 +167,153 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
   }
 }
 
+// ---------------------------------------------------------------- many activation rows
+// The same product as a tiled MFMA GEMM, for batches of activation rows where
+// the weights are worth dequantizing once per 128 rows of X: a workgroup
+// takes 128 rows of X by 128 rows of W; per 128-wide k chunk it copies the X
+// tile to LDS, dequantizes the W tile (the same exact 16-bit weights as above)
+// into LDS, and four waves (64 x 64 each) run v_mfma_f32_32x32x16 on them
+// (A lane l = X[l%32][8(l/32) .. +7], B lane l = W[l%32][8(l/32) .. +7] along
+// k; both tiles k-contiguous, rows padded to 136 elements).  fp32 accumulation.
+constexpr int kGM = 128, kGN = 128, kGKc = 128, kGPitch = kGKc + 8;
+constexpr int kGXv = kGM * kGKc / 8 / 256;     // 16-byte X loads per thread per chunk
+constexpr int kGWw = kGKc / 16;                // code words per thread per chunk (2 threads per W row)
+
+template <typename T> struct Mfma16;
+template <> struct Mfma16<__bf16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  static GPTQ_DEV f32x16_t run(v8 a, v8 b, f32x16_t c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+};
+template <> struct Mfma16<_Float16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  static GPTQ_DEV f32x16_t run(v8 a, v8 b, f32x16_t c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+};
+
+template <typename T, typename TY, bool NATURAL, bool VEC>
+__global__ __launch_bounds__(256) void w4a16_mfma_kernel(const uint16_t* __restrict__ X, int64_t m, int d_in,
+                                                         const uint32_t* __restrict__ packed,
+                                                         const float* __restrict__ scales,
+                                                         const int32_t* __restrict__ zeros,
+                                                         const int32_t* __restrict__ g_idx, int G, int ng,
+                                                         int d_out, TY* __restrict__ Y) {
+  typedef typename Act<T>::v2 v2;
+  typedef typename Mfma16<T>::v8 v8;
+  __shared__ __attribute__((aligned(16))) uint16_t sX[kGM * kGPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[kGN * kGPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * kGN;
+  const int64_t m0 = (int64_t)blockIdx.y * kGM;
+  const int nw = d_in >> 3;
+  const float invG = 1.0f / (float)G;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // this thread's W tile part: row wr, words kGWw wh .. + kGWw - 1 of the chunk
+  const int wr = tid >> 1, wh = tid & 1;
+  const int wrow = min(n0 + wr, d_out - 1);            // rows past the end: computed, not stored
+  const uint32_t* prow = packed + (size_t)wrow * nw;
+  const float* srow = scales + (size_t)wrow * ng;
+  const int32_t* zrow = zeros + (size_t)wrow * ng;
+
+  // chunk k0's global data in registers: X (rows tid/8 + 32i, 8 elements at
+  // k0 + 8(tid%8)) and this thread's 4 code words; loaded one chunk ahead so
+  // that their latency overlaps the MFMAs of the current chunk
+  // X element columns per row of the chunk covered by one thread's loads
+  constexpr int kXT = kGKc / 8;                // threads per X row (16 bytes each)
+  uint4 xr[kGXv];
+  uint32_t pw[kGWw];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kGXv; ++i) {
+      const int r = tid / kXT + (256 / kXT) * i, kk = k0 + 8 * (tid % kXT);
+      xr[i] = (m0 + r < m && kk < d_in) ? *reinterpret_cast<const uint4*>(X + (m0 + r) * (int64_t)d_in + kk)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int q0 = (k0 >> 3) + kGWw * wh;
+#pragma unroll
+    for (int u4 = 0; u4 < kGWw; u4 += 4) {
+      if (VEC && q0 + u4 + 3 < nw) {
+        const uint4 p4 = *reinterpret_cast<const uint4*>(prow + q0 + u4);
+        pw[u4] = p4.x; pw[u4 + 1] = p4.y; pw[u4 + 2] = p4.z; pw[u4 + 3] = p4.w;
+      } else {
+#pragma unroll
+        for (int u = u4; u < u4 + 4; ++u) pw[u] = (q0 + u < nw) ? prow[q0 + u] : 0u;
+      }
+    }
+  };
+  gload(0);
+  for (int k0 = 0; k0 < d_in; k0 += kGKc) {
+#pragma unroll
+    for (int i = 0; i < kGXv; ++i)
+      *reinterpret_cast<uint4*>(sX + (tid / kXT + (256 / kXT) * i) * kGPitch + 8 * (tid % kXT)) = xr[i];
+    // W tile: dequantize this thread's words of row wr
+    {
+      const int q0 = (k0 >> 3) + kGWw * wh;
+#pragma unroll
+      for (int u = 0; u < kGWw; ++u) {
+        v2 w[4];
+        const int c0 = (q0 + u) * 8;
+        if (q0 + u < nw) {
+          float sc = 0.0f, zb = 0.0f;
+          if (NATURAL) {
+            int g = (int)((float)c0 * invG);
+            if (g * G > c0) --g;
+            if ((g + 1) * G <= c0) ++g;
+            sc = srow[g];
+            zb = 8388608.0f + (float)zrow[g];
+          }
+          dequant_word<T, NATURAL>(pw[u], c0, sc, zb, srow, zrow, g_idx, ng, w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = Act<T>::pack(0.0f, 0.0f);
+        }
+        uint4 o;
+        o.x = __builtin_bit_cast(uint32_t, w[0]);
+        o.y = __builtin_bit_cast(uint32_t, w[1]);
+        o.z = __builtin_bit_cast(uint32_t, w[2]);
+        o.w = __builtin_bit_cast(uint32_t, w[3]);
+        *reinterpret_cast<uint4*>(sW + wr * kGPitch + 8 * kGWw * wh + 8 * u) = o;
+      }
+    }
+    __syncthreads();
+    if (k0 + kGKc < d_in) gload(k0 + kGKc);
+#pragma unroll
+    for (int ks = 0; ks < kGKc / 16; ++ks) {
+      const int kc = 16 * ks + 8 * (lane >> 5);
+      v8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = __builtin_bit_cast(v8, *reinterpret_cast<const uint4*>(sX + (wm * 64 + 32 * i + (lane & 31)) * kGPitch + kc));
+        b[i] = __builtin_bit_cast(v8, *reinterpret_cast<const uint4*>(sW + (wn * 64 + 32 * i + (lane & 31)) * kGPitch + kc));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = Mfma16<T>::run(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t mm = m0 + wm * 64 + 32 * i + mfma32_row(r, lane);
+        const int nn = n0 + wn * 64 + 32 * j + mfma32_col(lane);
+        if (mm < m && nn < d_out) Y[mm * d_out + nn] = out_cast<TY>(acc[i][j][r]);
+      }
+}
+
+// activation rows from which the tiled MFMA product is used
+constexpr int64_t kMfmaMinRows = 64;
+
 template <typename T, typename TY, int RPW>
 static void launch_w4a16_rpw(const uint16_t* x, int64_t m, int d_in, const uint32_t* packed, const float* scales,
                              const int32_t* zeros, const int32_t* g_idx, int G, int ng, int d_out, TY* y,
@@ -189,8 +336,21 @@ static void launch_w4a16(const void* X, int64_t m, int d_in, const uint32_t* pac
                          hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
   TY* y = static_cast<TY*>(Y);
-  if (m <= 2) launch_w4a16_rpw<T, TY, 1>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y, s);
-  else launch_w4a16_rpw<T, TY, 4>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y, s);
+  if (m >= kMfmaMinRows) {
+    const dim3 grid((unsigned)((d_out + kGN - 1) / kGN), (unsigned)((m + kGM - 1) / kGM));
+    const bool vec = ((d_in / 8) % 4 == 0) && (reinterpret_cast<uintptr_t>(packed) & 15) == 0;
+    if (g_idx) {
+      if (vec) w4a16_mfma_kernel<T, TY, false, true><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y);
+      else w4a16_mfma_kernel<T, TY, false, false><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y);
+    } else {
+      if (vec) w4a16_mfma_kernel<T, TY, true, true><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, nullptr, G, ng, d_out, y);
+      else w4a16_mfma_kernel<T, TY, true, false><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, nullptr, G, ng, d_out, y);
+    }
+  } else if (m <= 2) {
+    launch_w4a16_rpw<T, TY, 1>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y, s);
+  } else {
+    launch_w4a16_rpw<T, TY, 4>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y, s);
+  }
 }
 
 }  // namespace gptq

@@ -60,6 +60,12 @@ CASES = [
     (13, 100, 512, -1, 0, "bf16", "f16"),
     (5, 70, 4104, 8, 1, "f16", "f16"),
     (2, 33, 96, 32, 0, "f16", "bf16"),
+    # 32 or more activation rows: the tiled MFMA product
+    (200, 300, 1024, 64, 1, "f16", "f32"),
+    (128, 4096, 4096, 128, 0, "bf16", "bf16"),
+    (100, 70, 4104, 8, 1, "bf16", "f16"),
+    (333, 129, 640, -1, 0, "f16", "f16"),
+    (2048, 4096, 4096, 128, 0, "bf16", "f32"),
 ]
 
 
