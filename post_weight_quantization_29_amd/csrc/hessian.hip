@@ -516,13 +516,13 @@ __global__ __launch_bounds__(256, 2) void syrk32_kernel(const float* __restrict_
 // H += 2 * sum_s partial[s]  (fixed order), mirrored for off-diagonal tiles.
 // One workgroup per (tile, wave sub-tile); WB = 32-blocks per sub-tile edge.
 // ---------------------------------------------------------------------------
-template <int WB>
-__global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ partial,
-                                                          float* __restrict__ H, int d, int ntiles,
-                                                          int splits) {
+template <int WB, int NT>
+__global__ __launch_bounds__(NT) void syrk_reduce_kernel(const float* __restrict__ partial,
+                                                         float* __restrict__ H, int d, int ntiles,
+                                                         int splits) {
   constexpr int E = 32 * WB;            // sub-tile edge
   constexpr int NEL = WB * WB * 1024;   // elements per wave sub-tile
-  constexpr int NV = NEL / 1024;        // float4 per thread
+  constexpr int NV = NEL / (4 * NT);    // float4 per thread
   constexpr int TILE = 2 * E;
   __shared__ float sub[E][E + 1];
   const int q = blockIdx.x >> 2, wave = blockIdx.x & 3;
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
     const float4* ps = src + s * item_stride4;
     float4 v[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) v[i] = ps[tid + 256 * i];     // all loads in flight
+    for (int i = 0; i < NV; ++i) v[i] = ps[tid + NT * i];      // all loads in flight
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       acc[i][0] += v[i].x; acc[i][1] += v[i].y; acc[i][2] += v[i].z; acc[i][3] += v[i].w;
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
                          (float)(2.0 * acc[i][3])};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int e = 4 * (tid + 256 * i) + u;
+      const int e = 4 * (tid + NT * i) + u;
       const int blk = e >> 10, r = (e >> 6) & 15, lane = e & 63;
       const int m = (blk / WB) * 32 + mfma32_row(r, lane);
       const int n = (blk % WB) * 32 + mfma32_col(lane);
@@ -566,14 +566,14 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   // its 16 writes so the read-modify-writes do not serialize
   constexpr int NB = 16;
   for (int pass = 0; pass < ((I == J) ? 1 : 2); ++pass) {
-    for (int e0 = 0; e0 < E * E; e0 += 256 * NB) {
+    for (int e0 = 0; e0 < E * E; e0 += NT * NB) {
       float old[NB];
       size_t off[NB];
       bool ok[NB];
       float add[NB];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int e = e0 + u * 256 + tid;
+        const int e = e0 + u * NT + tid;
         const int a = e / E, b = e % E;           // pass 0: (m, n) = (a, b); pass 1: (n, m)
         const int m = pass ? b : a, n = pass ? a : b;
         ok[u] = (e < E * E) && row0 + m < d && col0 + n < d;
@@ -680,9 +680,11 @@ extern "C" int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, g
   }
   GPTQ_LAUNCH_CHECK();
   if (f32)
-    syrk_reduce_kernel<2><<<p.ntiles * 4, 256, 0, s>>>(partial, H, d_in, p.ntiles, p.splits);
+    syrk_reduce_kernel<2, 256><<<p.ntiles * 4, 256, 0, s>>>(partial, H, d_in, p.ntiles, p.splits);
   else
-    syrk_reduce_kernel<4><<<p.ntiles * 4, 256, 0, s>>>(partial, H, d_in, p.ntiles, p.splits);
+    // 512 threads: the 66 KB LDS tile allows two workgroups per CU, so the
+    // loads in flight come from more threads per workgroup
+    syrk_reduce_kernel<4, 512><<<p.ntiles * 4, 512, 0, s>>>(partial, H, d_in, p.ntiles, p.splits);
   GPTQ_LAUNCH_CHECK();
   if (hdiag) {
     diag_reduce_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(pdiag, d_in, p.nt * p.tile, p.splits, hdiag);
