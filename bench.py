@@ -426,7 +426,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved_tf, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "kernel": ("gptq_hessian_accumulate: syrk16_kernel<bf16> + syrk_reduce_kernel<4> "
+                     "kernel": ("gptq_hessian_accumulate: syrk16_kernel<bf16> + syrk_reduce_kernel<4, 512> "
                                 "+ diag_reduce_kernel"),
                      "work_per_launch": f"N*d*(d+1) = {h_flops:.4g} flop"},
     }
