@@ -15,7 +15,9 @@
 // Optional triangular structure, decided per tile:
 //   kloFromM: the contraction starts at k = m0 (Aop upper triangular),
 //   khiFromN: it stops at k = n0 + 128 (Bop upper triangular),
-//   upperOnly: tiles strictly below the diagonal are skipped (symmetric update).
+//   upperOnly: only tiles on or right of the diagonal are launched (symmetric
+//              update); the grid holds no idle workgroups, which would
+//              otherwise skew how the dispatcher spreads the real ones over CUs.
 #pragma once
 #include "common.h"
 
@@ -127,7 +129,17 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
   const GemmProblem P = grp.p[pi];          // fields held in registers from here on
   const int local = wg - grp.tile_start[pi];
   const int tn = (P.N + kGT - 1) / kGT;
-  const int m0 = (local / tn) * kGT, n0 = (local % tn) * kGT;
+  int m0, n0;
+  if (upperOnly) {
+    // only the tiles on or right of the diagonal are launched, row by row
+    int r = 0, rem = local;
+    while (rem >= tn - r) { rem -= tn - r; ++r; }
+    m0 = r * kGT;
+    n0 = (r + rem) * kGT;
+  } else {
+    m0 = (local / tn) * kGT;
+    n0 = (local % tn) * kGT;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -281,11 +293,11 @@ static __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmGroup grp, 
 
 // ---------------------------------------------------------------- small tiles
 // The same product in 64x64 tiles (four waves of 32x32, one MFMA accumulator
-// each), for launches with fewer 128x128 tiles than the chip has CUs: four
-// times the workgroups, a quarter of the work each.  Every element takes the
-// same MFMA steps in the same k order as in the 128x128 kernel, so the results
-// are identical.  upperOnly skips at 128-column-block granularity, like the
-// large kernel (the diagonal 128-blocks are computed whole).
+// each), for launches of a few 128x128 tiles per CU or fewer: four times the
+// workgroups, a quarter of the work each.  Every element takes the same MFMA
+// steps in the same k order as in the 128x128 kernel, so the results are
+// identical.  upperOnly works at 128-block granularity, like the large kernel
+// (the diagonal 128-blocks are computed whole).
 constexpr int kST = 64;            // small tile edge
 constexpr int kSP = kST + 4;       // LDS pitch (floats)
 
@@ -295,7 +307,18 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmProblem P, floa
   __shared__ __attribute__((aligned(16))) float sA[kGK * kSP];
   __shared__ __attribute__((aligned(16))) float sB[kGK * kSP];
   const int tn = (P.N + kST - 1) / kST;
-  const int m0 = ((int)blockIdx.x / tn) * kST, n0 = ((int)blockIdx.x % tn) * kST;
+  int m0, n0;
+  if (upperOnly) {
+    // only the tiles of 128-blocks on or right of the diagonal are launched:
+    // tile row r starts at tile column 2*(r/2)
+    int r = 0, rem = (int)blockIdx.x;
+    while (rem >= tn - 2 * (r / 2)) { rem -= tn - 2 * (r / 2); ++r; }
+    m0 = r * kST;
+    n0 = (2 * (r / 2) + rem) * kST;
+  } else {
+    m0 = ((int)blockIdx.x / tn) * kST;
+    n0 = ((int)blockIdx.x % tn) * kST;
+  }
   if (upperOnly && (n0 / kGT) < (m0 / kGT)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -365,6 +388,14 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmProblem P, floa
 
 inline int gemm_tiles(int M, int N) { return ((M + kGT - 1) / kGT) * ((N + kGT - 1) / kGT); }
 
+// 128-tiles on or right of the diagonal (what an upperOnly launch runs)
+inline int gemm_upper_tiles(int M, int N) {
+  const int tm = (M + kGT - 1) / kGT, tn = (N + kGT - 1) / kGT;
+  int t = 0;
+  for (int r = 0; r < tm; ++r) t += std::max(0, tn - r);
+  return t;
+}
+
 // Parts per tile for a launch of `tiles` tiles whose longest contraction is
 // kmax: enough workgroups to fill the chip twice over (two resident per CU),
 // each part at least 128 deep, at most 8 parts.
@@ -385,7 +416,7 @@ inline int launch_gemm_group(GemmGroup& g, float alpha, float beta, int kloFromM
   bool vec = true;
   for (int i = 0; i < g.count; ++i) {
     g.tile_start[i] = t;
-    t += gemm_tiles(g.p[i].M, g.p[i].N);
+    t += upperOnly ? gemm_upper_tiles(g.p[i].M, g.p[i].N) : gemm_tiles(g.p[i].M, g.p[i].N);
     const GemmProblem& p = g.p[i];
     vec = vec && (p.lda % 4 == 0) && (p.ldb % 4 == 0) &&
           ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 15) == 0;
@@ -434,17 +465,18 @@ inline void gemm_f32(const float* A, int lda, const float* B, int ldb, float* C,
                      int N, int K, float alpha, float beta, int kloFromM, int khiFromN, int upperOnly,
                      hipStream_t s) {
   if (M <= 0 || N <= 0) return;
-  // launches of few large tiles (counting only those upperOnly keeps) take 64x64 tiles
+  // launches of few large tiles (counting only those upperOnly keeps) take 64x64
+  // tiles; with a short contraction (the rank-128 updates) up to ~3.5 tiles per CU
   if (!kloFromM && !khiFromN) {
-    const int tm = (M + kGT - 1) / kGT, tn = (N + kGT - 1) / kGT;
-    int t128 = tm * tn;
-    if (upperOnly) {
-      t128 = 0;
-      for (int i = 0; i < tm; ++i) t128 += std::max(0, tn - i);
-    }
-    if (t128 < 192) {
+    const int t128 = upperOnly ? gemm_upper_tiles(M, N) : gemm_tiles(M, N);
+    if (t128 < (K <= 256 ? 448 : 192)) {
       const GemmProblem P{A, B, C, nullptr, lda, ldb, ldc, M, N, K};
-      const unsigned grid = (unsigned)(((M + kST - 1) / kST) * ((N + kST - 1) / kST));
+      const int sm = (M + kST - 1) / kST, sn = (N + kST - 1) / kST;
+      unsigned grid = (unsigned)(sm * sn);
+      if (upperOnly) {
+        grid = 0;
+        for (int r = 0; r < sm; ++r) grid += (unsigned)std::max(0, sn - 2 * (r / 2));
+      }
       const bool vec = (lda % 4 == 0) && (ldb % 4 == 0) &&
                        ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
       if (vec) gemm_f32_small_kernel<A_KMAJOR, true><<<grid, 256, 0, s>>>(P, alpha, beta, upperOnly);
