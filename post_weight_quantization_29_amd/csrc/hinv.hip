@@ -150,32 +150,43 @@ GPTQ_DEV void store32(const f32x16_t& acc, float* p, int ld, int lane) {
   for (int r = 0; r < 16; ++r) p[mfma32_row(r, lane) * ld + mfma32_col(lane)] = acc[r];
 }
 
-// Cholesky and inverse of the 32x32 sub-block at Mb (pitch kLP), one wave.
-// Lane l holds row l%32 of the block, columns 16(l/32) .. +15 (v), and
-// column l%32 of the inverse, rows 16(l/32) .. +15 (y, starting from I).
-// Two columns J, J+1 per step: their pivots come through readlane, their L
-// values and the two finished inverse rows go through LDS (cb, 128 floats)
-// once, and every lane applies the rank-2 update to its part of the block
-// and of the inverse (the inverse takes the same row operations, so
-// y ends as L^-1).  Mb keeps L on and below the diagonal (the upper triangle
-// is left undefined); Vb (pitch kVP) receives L^-1 with zeros above.  bad is
-// set on a pivot that is not > 0.
-GPTQ_DEV void leaf_chol_inv(float* Mb, float* Vb, float* cb, int lane, int& bad) {
+// Cholesky and inverse of the 32x32 sub-block at Mb (pitch kLP), split over
+// two waves that run one step apart.  Two columns J, J+1 per step.
+//
+// Factor wave (leaf_factor): lane l holds row l%32 of the block, columns
+// 16(l/32) .. +15 (v).  Per step its pivots come through readlane; the two
+// finished L columns go to the step's slot of the LDS ring (ring[step][64],
+// pivots in rs[step][4]), a flag releases the step to the inverse wave, and
+// every lane reads the columns back for its rank-2 update.  Mb keeps L on and
+// below the diagonal (the upper triangle is left undefined).
+//
+// Inverse wave (leaf_inverse): lane l holds column l%32 of the inverse, rows
+// 16(l/32) .. +15 (y, starting from I).  Per step it waits for the factor
+// wave's flag, takes the same row operations (so y ends as L^-1), and
+// exchanges its two finished inverse rows between its halves through yx.  Vb
+// (pitch kVP) receives L^-1 with zeros above.
+//
+// Every value takes the same operations in the same order as when one wave
+// did both.  epoch makes each leaf's flags distinct (they are never cleared);
+// bad is set on a pivot that is not > 0, and on a wait that does not end
+// within its bound (which would mean the factor wave stopped).
+constexpr int kLeafSteps = 16;
+
+GPTQ_DEV float leaf_rsq(float p) {
+  // 1/sqrt(p): hardware estimate refined by one Newton step
+  const float dd = __builtin_amdgcn_rsqf(p);
+  return dd * fmaf(-0.5f * p * dd, dd, 1.5f);
+}
+
+GPTQ_DEV void leaf_factor(float* Mb, float (*ring)[64], float (*rs)[4], int* flags, int epoch, int lane,
+                          int& bad) {
   int i = lane & 31, h = lane >> 5;
   // opaque per call: keeps the compiler from hoisting the per-step lane masks
   // out of the caller's loop (they would spill)
   asm volatile("" : "+v"(i), "+v"(h));
-  float v[16], y[16];
+  float v[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    v[r] = Mb[i * kLP + 16 * h + r];
-    y[r] = (16 * h + r == i) ? 1.0f : 0.0f;
-  }
-  auto rsq1 = [](float p) {
-    // 1/sqrt(p): hardware estimate refined by one Newton step
-    float dd = __builtin_amdgcn_rsqf(p);
-    return dd * fmaf(-0.5f * p * dd, dd, 1.5f);
-  };
+  for (int r = 0; r < 16; ++r) v[r] = Mb[i * kLP + 16 * h + r];
   auto rl = [](float x, int ln) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), ln));
   };
@@ -184,28 +195,29 @@ GPTQ_DEV void leaf_chol_inv(float* Mb, float* Vb, float* cb, int lane, int& bad)
     const float p0 = rl(v[r0], hj * 32 + J);          // A[J][J]
     const float a10 = rl(v[r0], hj * 32 + J + 1);     // A[J+1][J]
     const float p1r = rl(v[r1], hj * 32 + J + 1);     // A[J+1][J+1]
-    const float d0 = rsq1(p0);
+    const float d0 = leaf_rsq(p0);
     const float l10 = a10 * d0;
     const float p1 = fmaf(-l10, l10, p1r);
-    const float d1 = rsq1(p1);
+    const float d1 = leaf_rsq(p1);
     if (!(p0 > 0.0f) || !(p1 > 0.0f)) bad = 1;
+    float* cb = ring[J2];
     if (h == hj) {
       const float c0 = (i == J) ? p0 * d0 : v[r0] * d0;                       // L[i][J]
       const float c1 = (i == J + 1) ? p1 * d1 : fmaf(-c0, l10, v[r1]) * d1;   // L[i][J+1]
       if (i >= J) v[r0] = c0;
       if (i >= J + 1) v[r1] = c1;
-      // inverse rows J, J+1 of this lane's column i
-      const float yj = y[r0] * d0;
-      const float yj1 = fmaf(-l10, yj, y[r1]) * d1;
-      y[r0] = yj;
-      y[r1] = yj1;
       cb[i] = c0;
       cb[32 + i] = c1;
-      cb[64 + i] = yj;
-      cb[96 + i] = yj1;
     }
+    if (lane == 0) {
+      rs[J2][0] = d0;
+      rs[J2][1] = l10;
+      rs[J2][2] = d1;
+    }
+    // the step's slot is written: release it to the inverse wave
+    if (lane == 0) __hip_atomic_store(&flags[J2], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     asm volatile("" ::: "memory");
-    const float li0 = cb[i], li1 = cb[32 + i], yJ = cb[64 + i], yJ1 = cb[96 + i];
+    const float li0 = cb[i], li1 = cb[32 + i];
     float lc0[16], lc1[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -214,18 +226,76 @@ GPTQ_DEV void leaf_chol_inv(float* Mb, float* Vb, float* cb, int lane, int& bad)
       lc0[4 * r4 + 0] = q0.x; lc0[4 * r4 + 1] = q0.y; lc0[4 * r4 + 2] = q0.z; lc0[4 * r4 + 3] = q0.w;
       lc1[4 * r4 + 0] = q1.x; lc1[4 * r4 + 1] = q1.y; lc1[4 * r4 + 2] = q1.z; lc1[4 * r4 + 3] = q1.w;
     }
-    // entries (row, c) with c, row = 16h + r > J + 1 take the rank-2 update:
-    // v(i, c) -= L[i][J] L[c][J] + L[i][J+1] L[c][J+1];
-    // y(row, i) -= L[row][J] Y[J][i] + L[row][J+1] Y[J+1][i]
+    // entries (i, c), c = 16h + r > J + 1, take the rank-2 update
+    // v(i, c) -= L[i][J] L[c][J] + L[i][J+1] L[c][J+1]
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float nv = fmaf(-li1, lc1[r], fmaf(-li0, lc0[r], v[r]));
-      const float ny = fmaf(-lc1[r], yJ1, fmaf(-lc0[r], yJ, y[r]));
       if (J + 1 < 16) {
-        if (r > J + 1) { v[r] = nv; y[r] = ny; }
-        else { v[r] = h ? nv : v[r]; y[r] = h ? ny : y[r]; }
+        if (r > J + 1) v[r] = nv;
+        else v[r] = h ? nv : v[r];
       } else if (r > J + 1 - 16) {
         v[r] = h ? nv : v[r];
+      }
+    }
+    asm volatile("" ::: "memory");
+  };
+  [&]<int... Js>(std::integer_sequence<int, Js...>) {
+    (step.template operator()<Js>(), ...);
+  }(std::make_integer_sequence<int, kLeafSteps>{});
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Mb[i * kLP + 16 * h + r] = v[r];
+}
+
+GPTQ_DEV void leaf_inverse(float* Vb, float (*ring)[64], float (*rs)[4], const int* flags, float* yx,
+                           int epoch, int lane, int& bad) {
+  int i = lane & 31, h = lane >> 5;
+  asm volatile("" : "+v"(i), "+v"(h));
+  float y[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) y[r] = (16 * h + r == i) ? 1.0f : 0.0f;
+  auto step = [&]<int J2>() {
+    constexpr int J = 2 * J2, hj = J >> 4, r0 = J & 15, r1 = r0 + 1;
+    // the factor wave never waits for this one, so the flag comes; the bound
+    // only turns a broken invariant into an error instead of a hang
+    int spins = 0;
+    while (__hip_atomic_load(&flags[J2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != epoch) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > (1 << 22)) {
+        bad = 1;
+        break;
+      }
+    }
+    const float* cb = ring[J2];
+    const float d0 = rs[J2][0], l10 = rs[J2][1], d1 = rs[J2][2];
+    if (h == hj) {
+      // inverse rows J, J+1 of this lane's column i
+      const float yj = y[r0] * d0;
+      const float yj1 = fmaf(-l10, yj, y[r1]) * d1;
+      y[r0] = yj;
+      y[r1] = yj1;
+      yx[i] = yj;
+      yx[32 + i] = yj1;
+    }
+    asm volatile("" ::: "memory");
+    const float yJ = yx[i], yJ1 = yx[32 + i];
+    float lc0[16], lc1[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 q0 = reinterpret_cast<const float4*>(cb + 16 * h)[r4];
+      const float4 q1 = reinterpret_cast<const float4*>(cb + 32 + 16 * h)[r4];
+      lc0[4 * r4 + 0] = q0.x; lc0[4 * r4 + 1] = q0.y; lc0[4 * r4 + 2] = q0.z; lc0[4 * r4 + 3] = q0.w;
+      lc1[4 * r4 + 0] = q1.x; lc1[4 * r4 + 1] = q1.y; lc1[4 * r4 + 2] = q1.z; lc1[4 * r4 + 3] = q1.w;
+    }
+    // rows 16h + r > J + 1 take the same rank-2 operation:
+    // y(row, i) -= L[row][J] Y[J][i] + L[row][J+1] Y[J+1][i]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float ny = fmaf(-lc1[r], yJ1, fmaf(-lc0[r], yJ, y[r]));
+      if (J + 1 < 16) {
+        if (r > J + 1) y[r] = ny;
+        else y[r] = h ? ny : y[r];
+      } else if (r > J + 1 - 16) {
         y[r] = h ? ny : y[r];
       }
     }
@@ -233,12 +303,9 @@ GPTQ_DEV void leaf_chol_inv(float* Mb, float* Vb, float* cb, int lane, int& bad)
   };
   [&]<int... Js>(std::integer_sequence<int, Js...>) {
     (step.template operator()<Js>(), ...);
-  }(std::make_integer_sequence<int, 16>{});
+  }(std::make_integer_sequence<int, kLeafSteps>{});
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    Mb[i * kLP + 16 * h + r] = v[r];
-    Vb[(16 * h + r) * kVP + i] = y[r];
-  }
+  for (int r = 0; r < 16; ++r) Vb[(16 * h + r) * kVP + i] = y[r];
 }
 
 __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A, int np, int k,
@@ -246,7 +313,10 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A, 
   __shared__ __attribute__((aligned(16))) float M[kNB * kLP];
   __shared__ __attribute__((aligned(16))) float T[kNB * kLP];
   __shared__ __attribute__((aligned(16))) float V[4][32 * kVP];
-  __shared__ __attribute__((aligned(16))) float cb[128];
+  __shared__ __attribute__((aligned(16))) float ring[kLeafSteps][64];
+  __shared__ __attribute__((aligned(16))) float rs[kLeafSteps][4];
+  __shared__ __attribute__((aligned(16))) float yx[64];
+  __shared__ int flags[kLeafSteps];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;                     // 0: identity, t >= 1: column block k + t
@@ -273,13 +343,15 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A, 
       pt[0] = vt[u].x; pt[1] = vt[u].y; pt[2] = vt[u].z; pt[3] = vt[u].w;
     }
   }
+  if (tid < kLeafSteps) flags[tid] = 0;     // leaf epochs start at 1
   __syncthreads();
 
   int bad = 0;
 #pragma unroll 1
   for (int b = 0; b < 4; ++b) {
     const int o = 32 * b;
-    if (wave == 0) leaf_chol_inv(M + o * kLP + o, V[b], cb, lane, bad);
+    if (wave == 0) leaf_factor(M + o * kLP + o, ring, rs, flags, b + 1, lane, bad);
+    else if (wave == 1) leaf_inverse(V[b], ring, rs, flags, yx, b + 1, lane, bad);
     __syncthreads();
     // sub-blocks below: M_ab <- M_ab L_bb^-T   (wave w: a = b + 1 + w)
     if (wave < 3 - b) {
