@@ -178,6 +178,18 @@ GPTQ_DEV float leaf_rsq(float p) {
   return dd * fmaf(-0.5f * p * dd, dd, 1.5f);
 }
 
+// Factor-wave step order.  A step's rank-2 update of the trailing columns is
+// split: the two columns the next step pivots on (J+2, J+3, when they lie in
+// the same half) are updated at once, with the four L values they need taken
+// by readlane; the rest of the update reads its L columns from the ring and is
+// applied at the start of the following step's update, after that step's
+// pivots.  So the LDS round trip overlaps the next pivot chain.  Every column
+// still takes its updates in step order, with the same operations.
+constexpr bool leaf_ahead(int J2) {
+  return (2 * J2 + 3 <= 31) && (((2 * J2 + 2) >> 4) == ((2 * J2) >> 4));
+}
+constexpr bool leaf_deferred(int J2) { return leaf_ahead(J2) && J2 + 1 < kLeafSteps; }
+
 GPTQ_DEV void leaf_factor(float* Mb, float (*ring)[64], float (*rs)[4], int* flags, int epoch, int lane,
                           int& bad) {
   int i = lane & 31, h = lane >> 5;
@@ -190,6 +202,20 @@ GPTQ_DEV void leaf_factor(float* Mb, float (*ring)[64], float (*rs)[4], int* fla
   auto rl = [](float x, int ln) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), ln));
   };
+  // v(i, c) -= li0 lc0[r] + li1 lc1[r] for the lane's columns c = 16h + r > cmin
+  auto rank2 = [&]<int CMIN>(float li0, float li1, const float (&lc0)[16], const float (&lc1)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float nv = fmaf(-li1, lc1[r], fmaf(-li0, lc0[r], v[r]));
+      if (r > CMIN) {
+        v[r] = nv;                    // both halves: columns r and 16 + r exceed CMIN
+      } else if (16 + r > CMIN) {
+        v[r] = h ? nv : v[r];         // only the upper half's column 16 + r
+      }
+    }
+  };
+  // the previous step's deferred update: its L columns and the lane's L values
+  float plc0[16], plc1[16], pli0 = 0.0f, pli1 = 0.0f;
   auto step = [&]<int J2>() {
     constexpr int J = 2 * J2, hj = J >> 4, r0 = J & 15, r1 = r0 + 1;
     const float p0 = rl(v[r0], hj * 32 + J);          // A[J][J]
@@ -201,9 +227,9 @@ GPTQ_DEV void leaf_factor(float* Mb, float (*ring)[64], float (*rs)[4], int* fla
     const float d1 = leaf_rsq(p1);
     if (!(p0 > 0.0f) || !(p1 > 0.0f)) bad = 1;
     float* cb = ring[J2];
+    const float c0 = (i == J) ? p0 * d0 : v[r0] * d0;                       // L[i][J]
+    const float c1 = (i == J + 1) ? p1 * d1 : fmaf(-c0, l10, v[r1]) * d1;   // L[i][J+1]
     if (h == hj) {
-      const float c0 = (i == J) ? p0 * d0 : v[r0] * d0;                       // L[i][J]
-      const float c1 = (i == J + 1) ? p1 * d1 : fmaf(-c0, l10, v[r1]) * d1;   // L[i][J+1]
       if (i >= J) v[r0] = c0;
       if (i >= J + 1) v[r1] = c1;
       cb[i] = c0;
@@ -217,6 +243,19 @@ GPTQ_DEV void leaf_factor(float* Mb, float (*ring)[64], float (*rs)[4], int* fla
     // the step's slot is written: release it to the inverse wave
     if (lane == 0) __hip_atomic_store(&flags[J2], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     asm volatile("" ::: "memory");
+    // the previous step's update of the columns beyond this step's two
+    if constexpr (J2 > 0 && leaf_deferred(J2 - 1)) rank2.template operator()<J + 1>(pli0, pli1, plc0, plc1);
+    if constexpr (leaf_ahead(J2)) {
+      // this step's update of the next step's two columns (lanes of half hj
+      // hold them; their own c0, c1 are L[i][J], L[i][J+1])
+      constexpr int rn0 = (J + 2) & 15, rn1 = rn0 + 1;
+      const float l20 = rl(c0, hj * 32 + J + 2), l21 = rl(c1, hj * 32 + J + 2);
+      const float l30 = rl(c0, hj * 32 + J + 3), l31 = rl(c1, hj * 32 + J + 3);
+      const float n0 = fmaf(-c1, l21, fmaf(-c0, l20, v[rn0]));
+      const float n1 = fmaf(-c1, l31, fmaf(-c0, l30, v[rn1]));
+      v[rn0] = (h == hj) ? n0 : v[rn0];
+      v[rn1] = (h == hj) ? n1 : v[rn1];
+    }
     const float li0 = cb[i], li1 = cb[32 + i];
     float lc0[16], lc1[16];
 #pragma unroll
@@ -226,17 +265,17 @@ GPTQ_DEV void leaf_factor(float* Mb, float (*ring)[64], float (*rs)[4], int* fla
       lc0[4 * r4 + 0] = q0.x; lc0[4 * r4 + 1] = q0.y; lc0[4 * r4 + 2] = q0.z; lc0[4 * r4 + 3] = q0.w;
       lc1[4 * r4 + 0] = q1.x; lc1[4 * r4 + 1] = q1.y; lc1[4 * r4 + 2] = q1.z; lc1[4 * r4 + 3] = q1.w;
     }
-    // entries (i, c), c = 16h + r > J + 1, take the rank-2 update
-    // v(i, c) -= L[i][J] L[c][J] + L[i][J+1] L[c][J+1]
+    if constexpr (leaf_deferred(J2)) {
+      // applied after the next step's pivots (columns J+2, J+3 are done)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float nv = fmaf(-li1, lc1[r], fmaf(-li0, lc0[r], v[r]));
-      if (J + 1 < 16) {
-        if (r > J + 1) v[r] = nv;
-        else v[r] = h ? nv : v[r];
-      } else if (r > J + 1 - 16) {
-        v[r] = h ? nv : v[r];
+      for (int r = 0; r < 16; ++r) {
+        plc0[r] = lc0[r];
+        plc1[r] = lc1[r];
       }
+      pli0 = li0;
+      pli1 = li1;
+    } else {
+      rank2.template operator()<J + 1>(li0, li1, lc0, lc1);
     }
     asm volatile("" ::: "memory");
   };
