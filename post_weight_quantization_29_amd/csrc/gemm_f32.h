@@ -41,7 +41,23 @@ struct GemmGroup {
   GemmProblem p[kGemmMaxGroup];
   int tile_start[kGemmMaxGroup + 1];   // prefix sums of tiles per problem
   int count;
+  int ndesc;   // set by the launchers: tiles run by column from the last one
 };
+
+// Origin of tile `local` of a problem: row by row, or (ndesc) column by column
+// from the last column, so that with khiFromN the tiles with the longest
+// contraction are dispatched first and the short ones fill in behind them.
+GPTQ_DEV void tile_origin(const GemmProblem& P, int local, int ndesc, int& m0, int& n0) {
+  if (ndesc) {
+    const int tm = (P.M + kGT - 1) / kGT, tn = (P.N + kGT - 1) / kGT;
+    m0 = (local % tm) * kGT;
+    n0 = (tn - 1 - local / tm) * kGT;
+  } else {
+    const int tn = (P.N + kGT - 1) / kGT;
+    m0 = (local / tn) * kGT;
+    n0 = (local % tn) * kGT;
+  }
+}
 
 enum GemmEpilogue { kStore = 0, kDot = 1, kPartial = 2 };
 
@@ -137,8 +153,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
     m0 = r * kGT;
     n0 = (r + rem) * kGT;
   } else {
-    m0 = (local / tn) * kGT;
-    n0 = (local % tn) * kGT;
+    tile_origin(P, local, grp.ndesc, m0, n0);
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -267,9 +282,8 @@ static __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmGroup grp, 
   int pi = 0;
   while (pi + 1 < grp.count && grp.tile_start[pi + 1] <= wg) ++pi;
   const GemmProblem P = grp.p[pi];
-  const int local = wg - grp.tile_start[pi];
-  const int tn = (P.N + kGT - 1) / kGT;
-  const int m0 = (local / tn) * kGT, n0 = (local % tn) * kGT;
+  int m0, n0;
+  tile_origin(P, wg - grp.tile_start[pi], grp.ndesc, m0, n0);
   const float* src = partial + (size_t)wg * parts * 16384 + slice * 1024;
   float sum[4];
 #pragma unroll
@@ -422,6 +436,7 @@ inline int launch_gemm_group(GemmGroup& g, float alpha, float beta, int kloFromM
           ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 15) == 0;
   }
   g.tile_start[g.count] = t;
+  g.ndesc = (khiFromN && !upperOnly) ? 1 : 0;
   if (t > 0) {
     if (vec)
       gemm_f32_kernel<A_KMAJOR, EPI, true><<<t, 256, 0, s>>>(g, alpha, beta, kloFromM, khiFromN,
@@ -449,6 +464,7 @@ inline void launch_gemm_group_splitk(GemmGroup& g, int parts, float alpha, float
           ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 15) == 0;
   }
   g.tile_start[g.count] = t;
+  g.ndesc = khiFromN ? 1 : 0;
   if (t == 0) return;
   double* pp = reinterpret_cast<double*>(partial);
   if (vec)
