@@ -316,24 +316,36 @@ constexpr int kST = 64;            // small tile edge
 constexpr int kSP = kST + 4;       // LDS pitch (floats)
 
 template <bool A_KMAJOR, bool VEC>
-__global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmProblem P, float alpha, float beta,
-                                                             int upperOnly) {
+__global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmGroup grp, float alpha, float beta,
+                                                             int kloFromM, int khiFromN, int upperOnly) {
   __shared__ __attribute__((aligned(16))) float sA[kGK * kSP];
   __shared__ __attribute__((aligned(16))) float sB[kGK * kSP];
-  const int tn = (P.N + kST - 1) / kST;
+  const int wg = (int)blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < grp.count && grp.tile_start[pi + 1] <= wg) ++pi;
+  const GemmProblem P = grp.p[pi];
+  const int local = wg - grp.tile_start[pi];
+  const int tm = (P.M + kST - 1) / kST, tn = (P.N + kST - 1) / kST;
   int m0, n0;
   if (upperOnly) {
     // only the tiles of 128-blocks on or right of the diagonal are launched:
     // tile row r starts at tile column 2*(r/2)
-    int r = 0, rem = (int)blockIdx.x;
+    int r = 0, rem = local;
     while (rem >= tn - 2 * (r / 2)) { rem -= tn - 2 * (r / 2); ++r; }
     m0 = r * kST;
     n0 = (2 * (r / 2) + rem) * kST;
+  } else if (grp.ndesc) {
+    m0 = (local % tm) * kST;
+    n0 = (tn - 1 - local / tm) * kST;
   } else {
-    m0 = ((int)blockIdx.x / tn) * kST;
-    n0 = ((int)blockIdx.x % tn) * kST;
+    m0 = (local / tn) * kST;
+    n0 = (local % tn) * kST;
   }
   if (upperOnly && (n0 / kGT) < (m0 / kGT)) return;
+  // the contraction bounds of the 128x128 tile this tile lies in
+  const int klo = kloFromM ? (m0 / kGT) * kGT : 0;
+  int khi = khiFromN ? min(P.K, (n0 / kGT) * kGT + kGT) : P.K;
+  if (khi < klo) khi = klo;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   f32x16_t acc;
@@ -354,43 +366,45 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmProblem P, floa
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = k0 + (tid >> 4) + 16 * i;
-      const bool kv = k < P.K;
+      const bool kv = k < khi;
       rb[i] = kv ? load4<VEC>(P.B + (size_t)k * P.ldb + n0 + c4, P.N - n0 - c4) : make_float4(0.f, 0.f, 0.f, 0.f);
       if (A_KMAJOR)
         ra[i] = kv ? load4<VEC>(P.A + (size_t)k * P.lda + m0 + c4, P.M - m0 - c4) : make_float4(0.f, 0.f, 0.f, 0.f);
       else {
         const int m = m0 + (tid >> 4) + 16 * i, kq = k0 + c4;
-        ra[i] = (m < P.M) ? load4<VEC>(P.A + (size_t)m * P.lda + kq, P.K - kq) : make_float4(0.f, 0.f, 0.f, 0.f);
+        ra[i] = (m < P.M) ? load4<VEC>(P.A + (size_t)m * P.lda + kq, khi - kq) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
   };
-  float4 ra[4], rb[4];
-  gload(0, ra, rb);
-  for (int k0 = 0; k0 < P.K; k0 += kGK) {
-    __syncthreads();
-    {
-      const int c4 = 4 * (tid & 15);
+  if (klo < khi) {
+    float4 ra[4], rb[4];
+    gload(klo, ra, rb);
+    for (int k0 = klo; k0 < khi; k0 += kGK) {
+      __syncthreads();
+      {
+        const int c4 = 4 * (tid & 15);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kr = (tid >> 4) + 16 * i;
-        *reinterpret_cast<float4*>(sB + kr * kSP + c4) = rb[i];
-        if (A_KMAJOR) {
-          *reinterpret_cast<float4*>(sA + kr * kSP + c4) = ra[i];
-        } else {
-          sA[(c4 + 0) * kSP + kr] = ra[i].x;
-          sA[(c4 + 1) * kSP + kr] = ra[i].y;
-          sA[(c4 + 2) * kSP + kr] = ra[i].z;
-          sA[(c4 + 3) * kSP + kr] = ra[i].w;
+        for (int i = 0; i < 4; ++i) {
+          const int kr = (tid >> 4) + 16 * i;
+          *reinterpret_cast<float4*>(sB + kr * kSP + c4) = rb[i];
+          if (A_KMAJOR) {
+            *reinterpret_cast<float4*>(sA + kr * kSP + c4) = ra[i];
+          } else {
+            sA[(c4 + 0) * kSP + kr] = ra[i].x;
+            sA[(c4 + 1) * kSP + kr] = ra[i].y;
+            sA[(c4 + 2) * kSP + kr] = ra[i].z;
+            sA[(c4 + 3) * kSP + kr] = ra[i].w;
+          }
         }
       }
-    }
-    __syncthreads();
-    if (k0 + kGK < P.K) gload(k0 + kGK, ra, rb);
-    const int kn = min(kGK, P.K - k0);
+      __syncthreads();
+      if (k0 + kGK < khi) gload(k0 + kGK, ra, rb);
+      const int kn = min(kGK, khi - k0);       // zero-filled beyond khi: keep even steps
 #pragma unroll 4
-    for (int k2 = 0; k2 < kn; k2 += 2) {
-      const int row = (k2 + (lane >> 5)) * kSP + (lane & 31);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[row + wm * 32], sB[row + wn * 32], acc, 0, 0, 0);
+      for (int k2 = 0; k2 < kn; k2 += 2) {
+        const int row = (k2 + (lane >> 5)) * kSP + (lane & 31);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[row + wm * 32], sB[row + wn * 32], acc, 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -398,6 +412,38 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmProblem P, floa
     const int m = m0 + wm * 32 + mfma32_row(r, lane), n = n0 + wn * 32 + mfma32_col(lane);
     if (m < P.M && n < P.N) P.C[(size_t)m * P.ldc + n] = (beta != 0.0f) ? alpha * acc[r] + beta * cold[r] : alpha * acc[r];
   }
+}
+
+// 64x64 tiles of a problem (upperOnly: those of 128-blocks on or right of the diagonal)
+inline int gemm_small_tiles(int M, int N, int upperOnly) {
+  const int sm = (M + kST - 1) / kST, sn = (N + kST - 1) / kST;
+  if (!upperOnly) return sm * sn;
+  int t = 0;
+  for (int r = 0; r < sm; ++r) t += std::max(0, sn - 2 * (r / 2));
+  return t;
+}
+
+// Launch one group in 64x64 tiles (kStore semantics, same results as the
+// 128x128 kernel).
+template <bool A_KMAJOR>
+inline void launch_gemm_group_small(GemmGroup& g, float alpha, float beta, int kloFromM, int khiFromN,
+                                    int upperOnly, hipStream_t s) {
+  int t = 0;
+  bool vec = true;
+  for (int i = 0; i < g.count; ++i) {
+    g.tile_start[i] = t;
+    t += gemm_small_tiles(g.p[i].M, g.p[i].N, upperOnly);
+    const GemmProblem& p = g.p[i];
+    vec = vec && (p.lda % 4 == 0) && (p.ldb % 4 == 0) &&
+          ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 15) == 0;
+  }
+  g.tile_start[g.count] = t;
+  g.ndesc = (khiFromN && !upperOnly) ? 1 : 0;
+  if (t == 0) return;
+  if (vec)
+    gemm_f32_small_kernel<A_KMAJOR, true><<<t, 256, 0, s>>>(g, alpha, beta, kloFromM, khiFromN, upperOnly);
+  else
+    gemm_f32_small_kernel<A_KMAJOR, false><<<t, 256, 0, s>>>(g, alpha, beta, kloFromM, khiFromN, upperOnly);
 }
 
 inline int gemm_tiles(int M, int N) { return ((M + kGT - 1) / kGT) * ((N + kGT - 1) / kGT); }
@@ -483,26 +529,16 @@ inline void gemm_f32(const float* A, int lda, const float* B, int ldb, float* C,
   if (M <= 0 || N <= 0) return;
   // launches of few large tiles (counting only those upperOnly keeps) take 64x64
   // tiles; with a short contraction (the rank-128 updates) up to ~3.5 tiles per CU
-  if (!kloFromM && !khiFromN) {
-    const int t128 = upperOnly ? gemm_upper_tiles(M, N) : gemm_tiles(M, N);
-    if (t128 < (K <= 256 ? 448 : 192)) {
-      const GemmProblem P{A, B, C, nullptr, lda, ldb, ldc, M, N, K};
-      const int sm = (M + kST - 1) / kST, sn = (N + kST - 1) / kST;
-      unsigned grid = (unsigned)(sm * sn);
-      if (upperOnly) {
-        grid = 0;
-        for (int r = 0; r < sm; ++r) grid += (unsigned)std::max(0, sn - 2 * (r / 2));
-      }
-      const bool vec = (lda % 4 == 0) && (ldb % 4 == 0) &&
-                       ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-      if (vec) gemm_f32_small_kernel<A_KMAJOR, true><<<grid, 256, 0, s>>>(P, alpha, beta, upperOnly);
-      else gemm_f32_small_kernel<A_KMAJOR, false><<<grid, 256, 0, s>>>(P, alpha, beta, upperOnly);
-      return;
-    }
-  }
   GemmGroup g;
   g.count = 1;
   g.p[0] = GemmProblem{A, B, C, nullptr, lda, ldb, ldc, M, N, K};
+  if (!kloFromM && !khiFromN) {
+    const int t128 = upperOnly ? gemm_upper_tiles(M, N) : gemm_tiles(M, N);
+    if (t128 < (K <= 256 ? 448 : 192)) {
+      launch_gemm_group_small<A_KMAJOR>(g, alpha, beta, 0, 0, upperOnly, s);
+      return;
+    }
+  }
   launch_gemm_group<A_KMAJOR, kStore>(g, alpha, beta, kloFromM, khiFromN, upperOnly, nullptr, s);
 }
 

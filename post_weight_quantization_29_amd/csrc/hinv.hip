@@ -500,6 +500,9 @@ struct HinvLayout {
 
 struct TreeNode { int a, mid, b; };
 
+// tree launches of fewer 128x128 tiles than this run in 64x64 tiles
+constexpr int kTreeSmallTiles = 128;
+
 static void build_levels(int lo, int hi, int depth, std::vector<std::vector<TreeNode>>& lv) {
   if (hi - lo <= 1) return;
   const int mid = lo + (hi - lo) / 2;
@@ -630,7 +633,13 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
       int tiles, kmax;
       tree_launch_shape(nodes, c0, cnt, tiles, kmax);
       const int parts = splitk_parts(tiles, kmax);
-      if (parts > 1) {
+      if (tiles < kTreeSmallTiles) {
+        // the deep levels: 64x64 tiles, four workgroups per 128-tile, no split
+        launch_gemm_group_small<false>(g1, 1.0f, 0.0f, 1, 0, 0, s);
+        GPTQ_LAUNCH_CHECK();
+        launch_gemm_group_small<false>(g2, -1.0f, 0.0f, 0, 1, 0, s);
+        GPTQ_LAUNCH_CHECK();
+      } else if (parts > 1) {
         // few tiles with long contractions: split them (partials in SK)
         launch_gemm_group_splitk<false>(g1, parts, 1.0f, 0.0f, 1, 0, SK, s);
         GPTQ_LAUNCH_CHECK();
