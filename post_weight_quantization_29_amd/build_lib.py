@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libgptq.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["hessian.hip", "hinv.hip", "quantize.hip", "error.hip", "w4a16.hip", "awq.hip", "block.hip"]
+SOURCES = ["hessian.hip", "hinv.hip", "quantize.hip", "quant_step.hip", "error.hip", "w4a16.hip", "awq.hip", "block.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-result", "-Wno-inline-asm",

@@ -125,6 +125,84 @@ GPTQ_DEV void gemm_lstore(float* sA, float* sB, int tid, const float4 (&ra)[8], 
   }
 }
 
+// One 128x128 tile, four waves (2x2) of 64x64: acc += Aop[m0.., klo:khi] * Bop[klo:khi, n0..],
+// k in chunks of 64 staged through sA, sB (kGK x kGP floats each); the next
+// chunk is loaded into registers while the current one is multiplied.
+template <bool A_KMAJOR, bool VEC>
+GPTQ_DEV void gemm_tile_contract(const GemmProblem& P, int m0, int n0, int klo, int khi, float* sA, float* sB,
+                                 f32x16_t (&acc)[2][2]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (klo >= khi) return;
+  float4 ra[8], rb[8];
+  gemm_gload<A_KMAJOR, VEC>(P, m0, n0, klo, khi, tid, ra, rb);
+  for (int k0 = klo; k0 < khi; k0 += kGK) {
+    __syncthreads();                         // the previous chunk is consumed
+    gemm_lstore<A_KMAJOR>(sA, sB, tid, ra, rb);
+    __syncthreads();
+    if (k0 + kGK < khi) gemm_gload<A_KMAJOR, VEC>(P, m0, n0, k0 + kGK, khi, tid, ra, rb);
+    const int kn = min(kGK, khi - k0);       // zero-filled beyond khi: keep even steps
+#pragma unroll 4
+    for (int k2 = 0; k2 < kn; k2 += 2) {
+      const int row = (k2 + (lane >> 5)) * kGP + (lane & 31);
+      const float a0 = sA[row + wm * 64], a1 = sA[row + wm * 64 + 32];
+      const float b0 = sB[row + wn * 64], b1 = sB[row + wn * 64 + 32];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+  }
+}
+
+// The tile's old C values in the MFMA register layout (0 outside C).
+GPTQ_DEV void gemm_tile_load_c(const GemmProblem& P, int m0, int n0, float (&cold)[2][2][16]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+        const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
+        cold[i][j][r] = (m < P.M && n < P.N) ? P.C[(size_t)m * P.ldc + n] : 0.0f;
+      }
+}
+
+// C = alpha * acc + beta * cold over the tile (beta == 0: alpha * acc).
+GPTQ_DEV void gemm_tile_store(const GemmProblem& P, int m0, int n0, float alpha, float beta,
+                              f32x16_t (&acc)[2][2], const float (&cold)[2][2][16]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (beta != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = alpha * acc[i][j][r] + beta * cold[i][j][r];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] *= alpha;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+        const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
+        if (m < P.M && n < P.N) P.C[(size_t)m * P.ldc + n] = acc[i][j][r];
+      }
+}
+
 // kPartial (split-K): workgroup w takes part w % parts of tile w / parts, i.e.
 // the part's share of the tile's contraction range (cut in multiples of 64),
 // and writes its raw 128x128 sum to partial (float*) in MFMA register order,
@@ -180,40 +258,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
   // C's old values are loaded before the contraction so that their latency and
   // bandwidth overlap the MFMA work (C never aliases A or B when beta != 0)
   float cold[2][2][16];
-  if (EPI == kStore && !skip && beta != 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-          const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
-          cold[i][j][r] = (m < P.M && n < P.N) ? P.C[(size_t)m * P.ldc + n] : 0.0f;
-        }
-  }
+  if (EPI == kStore && !skip && beta != 0.0f) gemm_tile_load_c(P, m0, n0, cold);
 
-  if (!skip && klo < khi) {
-    float4 ra[8], rb[8];
-    gemm_gload<A_KMAJOR, VEC>(P, m0, n0, klo, khi, tid, ra, rb);
-    for (int k0 = klo; k0 < khi; k0 += kGK) {
-      __syncthreads();                         // the previous chunk is consumed
-      gemm_lstore<A_KMAJOR>(sA, sB, tid, ra, rb);
-      __syncthreads();
-      if (k0 + kGK < khi) gemm_gload<A_KMAJOR, VEC>(P, m0, n0, k0 + kGK, khi, tid, ra, rb);
-      const int kn = min(kGK, khi - k0);       // zero-filled beyond khi: keep even steps
-#pragma unroll 4
-      for (int k2 = 0; k2 < kn; k2 += 2) {
-        const int row = (k2 + (lane >> 5)) * kGP + (lane & 31);
-        const float a0 = sA[row + wm * 64], a1 = sA[row + wm * 64 + 32];
-        const float b0 = sB[row + wn * 64], b1 = sB[row + wn * 64 + 32];
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
-      }
-    }
-  }
+  if (!skip) gemm_tile_contract<A_KMAJOR, VEC>(P, m0, n0, klo, khi, sA, sB, acc);
 
   if (EPI == kPartial) {
     float* out = reinterpret_cast<float*>(dot_out) + ((size_t)blockIdx.x * 4 + wave) * (4 * 16 * 64);
@@ -227,31 +274,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
   }
   if (EPI == kStore) {
     if (skip) return;
-    if (beta != 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = alpha * acc[i][j][r] + beta * cold[i][j][r];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] *= alpha;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-          const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
-          if (m < P.M && n < P.N) P.C[(size_t)m * P.ldc + n] = acc[i][j][r];
-        }
+    gemm_tile_store(P, m0, n0, alpha, beta, acc, cold);
   } else {
     double s = 0.0;
 #pragma unroll

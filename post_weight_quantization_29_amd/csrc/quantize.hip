@@ -18,15 +18,13 @@
 //   trailing GEMM:  W[:, b1:] -= Err * U[b0:b1, b1:] (fp32 MFMA).
 #include "gemm_f32.h"
 #include "lookahead.h"
+#include "panel.h"
 
+#include <cstdlib>
+#include <cstring>
 #include <utility>
 
 namespace gptq {
-
-constexpr int kQB = 128;          // block width (lazy batch)
-constexpr int kQL = 16;           // lanes per row
-constexpr int kQS = kQB / kQL;    // columns (slots) per lane
-constexpr int kQRows = 16;        // rows per workgroup (4 waves x 4 rows)
 
 // ---------------------------------------------------------------- W gather
 __global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ W, gptq_dtype wt,
@@ -39,278 +37,6 @@ __global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ 
   if (blockIdx.y == 0) g_idx[src] = j / G;
   for (int r = blockIdx.y; r < d_out; r += gridDim.y)
     Wp[(size_t)r * d + j] = load_as_float(W, wt, (size_t)r * d + src);
-}
-
-// ---------------------------------------------------------------- helpers
-// DPP on 16-lane rows.  dpp control: quad_perm 0x00-0xFF, row_ror:r = 0x120+r;
-// bank k = lanes 4k..4k+3 of a row; lanes of banks left out of bank_mask keep
-// `old`.
-template <int CTRL, int BANKS>
-GPTQ_DEV int dpp_upd(int old, int src) {
-  return __builtin_amdgcn_update_dpp(old, src, CTRL, 0xF, BANKS, false);
-}
-template <int CTRL>
-GPTQ_DEV float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// every lane of a 16-lane row reads lane P of that row: broadcast inside the
-// quads, then copy bank P/4 to the opposite bank (rotate by 8) and those two
-// to the remaining two (rotate by 4); either rotation direction maps the banks
-// the same way
-template <int P>
-GPTQ_DEV float row_bcast16(float v) {
-  constexpr int p = P & 3, B0 = P >> 2;
-  int x = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), p | (p << 2) | (p << 4) | (p << 6),
-                                   0xF, 0xF, false);
-  x = dpp_upd<0x128, (1 << (B0 ^ 2))>(x, x);
-  x = dpp_upd<0x124, (1 << (B0 ^ 1)) | (1 << (B0 ^ 3))>(x, x);
-  return __builtin_bit_cast(float, x);
-}
-template <int P>
-GPTQ_DEV double row_bcast16d(double v) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = __builtin_bit_cast(uint32_t, row_bcast16<P>(__builtin_bit_cast(float, (uint32_t)b)));
-  const uint32_t hi = __builtin_bit_cast(uint32_t, row_bcast16<P>(__builtin_bit_cast(float, (uint32_t)(b >> 32))));
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-GPTQ_DEV float row_min16(float v) {
-  v = fminf(v, dpp_f<0xB1>(v));
-  v = fminf(v, dpp_f<0x4E>(v));
-  v = fminf(v, dpp_f<0x124>(v));
-  v = fminf(v, dpp_f<0x128>(v));
-  return v;
-}
-GPTQ_DEV float row_max16(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x124>(v));
-  v = fmaxf(v, dpp_f<0x128>(v));
-  return v;
-}
-
-// min-max grid of one group: scale = (max - min)/maxq, zero = rint(-min/scale);
-// a constant group a uses the range [min(a,0), max(a,0)]; all-zero -> (1, 0).
-GPTQ_DEV void grid_params(float xmin, float xmax, float maxq, float& scale, float& zero) {
-  if (xmax == xmin) {
-    xmin = fminf(xmin, 0.0f);
-    xmax = fmaxf(xmax, 0.0f);
-  }
-  if (xmax == xmin) {
-    scale = 1.0f;
-    zero = 0.0f;
-    return;
-  }
-  scale = (xmax - xmin) / maxq;
-  zero = rintf(-xmin / scale);
-}
-
-// ---------------------------------------------------------------- panel
-struct PanelArgs {
-  float* Wp;            // [d_out x d] fp32 work copy, processing order
-  const float* U;       // [d x d]
-  const int* perm;
-  uint8_t* codes;       // [d_out x d], original order
-  float* Q;             // nullable
-  float* scales;        // [d_out x ng]
-  int* zeros;
-  float* ErrT;          // [128 x d_out]
-  int d_out, d, b0, bw, G, ng;
-  int sym;
-  float maxq;
-};
-
-// 16 rows per workgroup, 16 lanes per row (lane q holds the block's columns
-// 16t+q, t = 0..7).  Every column step is instantiated separately (template
-// fold over the 128 columns), so the row slice stays in registers with
-// compile-time indices.  GT > 0: groups of GT columns inside the block (group
-// starts known at compile time); GT == 0: groups of G >= 128 columns, which
-// can only start at the block's first column.
-template <int GT>
-__global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
-  __shared__ float4 sU4[kQB][kQS / 4][kQL];   // sU4[j][t/4][q] = U[b0+j][b0+16t+q], t..t+3
-  __shared__ double sInv[kQB];
-  __shared__ int sPerm[kQB];
-
-  const int tid = threadIdx.x;
-  float* sU = reinterpret_cast<float*>(&sU4[0][0][0]);
-  // U's diagonal block, strict upper part (zero on and below the diagonal):
-  // 16 float4 loads in flight per thread
-  {
-    // 16-byte loads when every U row starts 16-byte aligned
-    const bool vec = (a.d % 4 == 0) && (reinterpret_cast<uintptr_t>(a.U) % 16 == 0);
-    float4 v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = u * 256 + tid;              // float4 index: row j, columns 4m .. 4m+3
-      const int j = e >> 5, c = 4 * (e & 31);
-      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < a.bw && c + 3 > j) {
-        const float* src = a.U + (size_t)(a.b0 + j) * a.d + a.b0 + c;
-        if (vec && c + 3 < a.bw) {
-          v[u] = *reinterpret_cast<const float4*>(src);
-        } else {
-          if (c + 3 < a.bw) v[u].w = src[3];
-          if (c + 0 < a.bw) v[u].x = src[0];
-          if (c + 1 < a.bw) v[u].y = src[1];
-          if (c + 2 < a.bw) v[u].z = src[2];
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = u * 256 + tid;
-      const int j = e >> 5, c = 4 * (e & 31);
-      const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int cc = c + k;
-        const int t = cc >> 4;
-        sU[((j * (kQS / 4) + (t >> 2)) * kQL + (cc & 15)) * 4 + (t & 3)] = (cc > j) ? vv[k] : 0.0f;
-      }
-    }
-  }
-  for (int j = tid; j < kQB; j += 256) {
-    sInv[j] = (j < a.bw) ? 1.0 / (double)a.U[(size_t)(a.b0 + j) * a.d + a.b0 + j] : 0.0;
-    sPerm[j] = (j < a.bw) ? a.perm[a.b0 + j] : 0;
-  }
-  __syncthreads();
-
-  const int q = tid & 15;
-  const int row = blockIdx.x * kQRows + (tid >> 4);
-  const bool rv = row < a.d_out;
-  const int rowc = rv ? row : 0;     // clamped row for loads; stores are masked
-  const float* wrow = a.Wp + (size_t)rowc * a.d + a.b0;
-  const int bw = a.bw;
-
-  // The block's running weights are kept in fp64: its 127 in-block updates
-  // are where fp32 rounding would move near-ties to the other side.
-  double w[kQS];
-#pragma unroll
-  for (int t = 0; t < kQS; ++t) w[t] = (kQL * t + q < bw) ? (double)wrow[kQL * t + q] : 0.0;
-
-  float scale = 1.0f, zero = 0.0f, rscale = 1.0f;
-  if (GT == 0 && a.b0 % a.G != 0) {
-    // a group wider than the block started in an earlier block: continue with
-    // the parameters that launch stored
-    scale = a.scales[(size_t)rowc * a.ng + a.b0 / a.G];
-    zero = (float)a.zeros[(size_t)rowc * a.ng + a.b0 / a.G];
-    rscale = 1.0f / scale;
-  }
-  // results of the lane's own columns, stored once at the end
-  float eown[kQS], qown[kQS];
-  uint32_t cown[kQS / 4];
-#pragma unroll
-  for (int t = 0; t < kQS / 4; ++t) cown[t] = 0u;
-
-  auto group_start = [&]<int J>() {
-    constexpr int I = J / kQL;
-    float mn = INFINITY, mx = -INFINITY;
-    if constexpr (GT >= kQL) {
-      // slots I .. I + GT/16 - 1 hold the group's columns J .. J + GT - 1
-#pragma unroll
-      for (int t = I; t < I + GT / kQL; ++t) {
-        if (kQL * t + q < bw) {
-          mn = fminf(mn, (float)w[t]);
-          mx = fmaxf(mx, (float)w[t]);
-        }
-      }
-    } else if constexpr (GT > 0) {
-      // a group inside one slot: lanes J%16 .. J%16 + GT - 1
-      constexpr int L0 = J % kQL;
-      if (q >= L0 && q < L0 + GT && J + (q - L0) < bw) {
-        mn = (float)w[I];
-        mx = (float)w[I];
-      }
-    } else {
-      // J == 0: the whole block (columns < bw), then the rest of the group
-      // from the work copy, which holds every earlier block's lazy update
-#pragma unroll
-      for (int t = 0; t < kQS; ++t) {
-        if (kQL * t + q < bw) {
-          mn = fminf(mn, (float)w[t]);
-          mx = fmaxf(mx, (float)w[t]);
-        }
-      }
-      const int gend = min(a.b0 + a.G, a.d);
-      const float* wr = a.Wp + (size_t)rowc * a.d;
-      for (int cg = a.b0 + bw + q; cg < gend; cg += kQL) {
-        const float v = wr[cg];
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
-      }
-    }
-    mn = row_min16(mn);
-    mx = row_max16(mx);
-    if (a.sym) {
-      // symmetric: [-m, m], the middle code is zero
-      const float m = fmaxf(fabsf(mn), fabsf(mx));
-      scale = (m == 0.0f) ? 1.0f : (m + m) / a.maxq;
-      zero = 0.5f * (a.maxq + 1.0f);
-    } else {
-      grid_params(mn, mx, a.maxq, scale, zero);
-    }
-    rscale = 1.0f / scale;
-    const int gi = (GT > 0) ? (a.b0 + J) / GT : a.b0 / a.G;
-    if (rv && q == 0) {
-      a.scales[(size_t)row * a.ng + gi] = scale;
-      a.zeros[(size_t)row * a.ng + gi] = (int)zero;
-    }
-  };
-
-  auto step = [&]<int J>() {
-    constexpr int I = J / kQL, P = J % kQL;
-    if (J >= bw) return;
-    if constexpr (GT > 0) {
-      if constexpr (J % GT == 0) group_start.template operator()<J>();
-    } else {
-      if constexpr (J == 0) {
-        if (a.b0 % a.G == 0) group_start.template operator()<0>();
-      }
-    }
-    const double wj = row_bcast16d<P>(w[I]);
-    // the code is decided in fp32: correctly rounded fp32(wj)/scale from the
-    // reciprocal (one residual correction)
-    const float wf = (float)wj;
-    const float t0 = wf * rscale;
-    const float res = fmaf(-t0, scale, wf);
-    const float tq = fmaf(res, rscale, t0);
-    const float c = fminf(fmaxf(rintf(tq) + zero, 0.0f), a.maxq);
-    const double qv = (double)scale * (double)(c - zero);    // exact
-    const double e = (wj - qv) * sInv[J];
-    if (q == P) {
-      eown[I] = (float)e;
-      qown[I] = (float)qv;
-      cown[I >> 2] |= (uint32_t)c << (8 * (I & 3));
-    }
-    // w[t] -= e * U[J][16t+q] for the later columns of the block (slots t >= I;
-    // entries at columns <= J are retired, and U is zero there)
-#pragma unroll
-    for (int t = (I & ~3); t < kQS; t += 4) {
-      const float4 u4 = sU4[J][t >> 2][q];
-      if (t + 0 >= I) w[t + 0] = fma(-e, (double)u4.x, w[t + 0]);
-      if (t + 1 >= I) w[t + 1] = fma(-e, (double)u4.y, w[t + 1]);
-      if (t + 2 >= I) w[t + 2] = fma(-e, (double)u4.z, w[t + 2]);
-      if (t + 3 >= I) w[t + 3] = fma(-e, (double)u4.w, w[t + 3]);
-    }
-  };
-  [&]<int... Js>(std::integer_sequence<int, Js...>) {
-    (step.template operator()<Js>(), ...);
-  }(std::make_integer_sequence<int, kQB>{});
-
-  if (!rv) return;
-  uint8_t* crow = a.codes + (size_t)row * a.d;
-  float* qrow = a.Q ? a.Q + (size_t)row * a.d : nullptr;
-#pragma unroll
-  for (int t = 0; t < kQS; ++t) {
-    const int j = kQL * t + q;
-    if (j < bw) {
-      const int oc = sPerm[j];
-      crow[oc] = (uint8_t)(cown[t >> 2] >> (8 * (t & 3)));
-      if (qrow) qrow[oc] = qown[t];
-      a.ErrT[(size_t)j * a.d_out + row] = eown[t];
-    }
-  }
 }
 
 // ---------------------------------------------------------------- pack
@@ -449,6 +175,47 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   const int nrow_blocks = (d_out + kQRows - 1) / kQRows;
   // in-block group sizes are compile-time; wider groups (or one per row) use 0
   const int gt = (G <= kQB && kQB % G == 0 && G % 4 == 0) ? G : 0;
+
+  // Fused block steps (groups inside the block, operands the 16-byte loads
+  // take): block 0's column loop, then one launch per later block holding its
+  // column loop (which first applies the previous block's update to its own
+  // rows) beside the previous block's trailing update of the columns after
+  // it.  Same operations, same results as the per-block launches below.
+  static const bool fused_on = [] {
+    const char* env = std::getenv("GPTQ_FUSED_STEP");
+    return !(env && std::strcmp(env, "0") == 0);
+  }();
+  if (fused_on && quant_step_applies(d_out, d, U, gt)) {
+    pa.b0 = 0;
+    pa.bw = std::min(kQB, d);
+    pa.ErrT = ErrT;
+    switch (gt) {
+      case 4: panel_kernel<4><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      case 8: panel_kernel<8><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      case 16: panel_kernel<16><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      case 32: panel_kernel<32><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      case 64: panel_kernel<64><<<nrow_blocks, 256, 0, s>>>(pa); break;
+      default: panel_kernel<128><<<nrow_blocks, 256, 0, s>>>(pa); break;
+    }
+    GPTQ_LAUNCH_CHECK();
+    for (int b0 = 0, blk = 0; b0 + kQB < d; b0 += kQB, ++blk) {
+      const int b1 = b0 + kQB, bw1 = std::min(kQB, d - b1);
+      StepArgs st;
+      st.pa = pa;
+      st.pa.b0 = b1;
+      st.pa.bw = bw1;
+      st.pa.ErrT = ErrT + (size_t)((blk + 1) & 1) * kQB * d_out;
+      st.Eprev = ErrT + (size_t)(blk & 1) * kQB * d_out;
+      st.Uprev = U + (size_t)b0 * d + b1;
+      st.Wrest = Wp + b1 + bw1;
+      st.Urest = U + (size_t)b0 * d + b1 + bw1;
+      st.rest = d - b1 - bw1;
+      st.kprev = kQB;
+      launch_quant_step(st, gt, s);
+      GPTQ_LAUNCH_CHECK();
+    }
+    return GPTQ_OK;
+  }
   // Lookahead: block b's update of the next block's columns runs on the
   // caller's stream, the rest of the trailing columns on the side stream, so
   // panel b+1 overlaps it.  Panels alternate between two ErrT buffers; an
