@@ -181,10 +181,8 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   // column loop (which first applies the previous block's update to its own
   // rows) beside the previous block's trailing update of the columns after
   // it.  Same operations, same results as the per-block launches below.
-  static const bool fused_on = [] {
-    const char* env = std::getenv("GPTQ_FUSED_STEP");
-    return !(env && std::strcmp(env, "0") == 0);
-  }();
+  const char* fused_env = std::getenv("GPTQ_FUSED_STEP");
+  const bool fused_on = !(fused_env && std::strcmp(fused_env, "0") == 0);
   if (fused_on && quant_step_applies(d_out, d, U, gt)) {
     pa.b0 = 0;
     pa.bw = std::min(kQB, d);
