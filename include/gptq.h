@@ -23,12 +23,16 @@
  *    per device, one extra stream and two events, created on first use.
  *  - All work is ordered on stream s: it starts after the work already on s
  *    and is complete, as seen from s, before anything enqueued on s later.
- *    gptq_quantize_layer, for layers of 2^25 weights or more, puts part of
- *    its blocked loop on the device's extra stream (a trailing update
- *    overlapping the next block's panel), ordered against s with events and
- *    joined back to s before it returns; the results are the same bit for
- *    bit as on one stream (GPTQ_LOOKAHEAD=0 in the environment keeps
- *    everything on s).
+ *    gptq_quantize_layer with groups wider than the 128-column block, for
+ *    layers of 2^25 weights or more, puts part of its blocked loop on the
+ *    device's extra stream (a trailing update overlapping the next block's
+ *    panel), ordered against s with events and joined back to s before it
+ *    returns; the results are the same bit for bit as on one stream
+ *    (GPTQ_LOOKAHEAD=0 in the environment keeps everything on s).  With
+ *    groups inside the block it stays on s, running each block's column loop
+ *    in the same launch as the previous block's trailing update, also with
+ *    the same results bit for bit (GPTQ_FUSED_STEP=0 selects one launch per
+ *    step).
  *    The enqueue of such a call holds a per-device lock.  Only
  *    gptq_prepare_hinv and gptq_layer_error synchronize s (to read one
  *    device flag or scalar).
