@@ -88,7 +88,8 @@ constexpr int kK16 = 32;           // tokens per stage (2 k-slices of 16)
 constexpr int kSlots16 = 4;        // LDS ring slots
 constexpr int kRow16 = kT16;       // LDS row pitch in elements (512 bytes)
 constexpr int kStage16 = kK16 * kRow16;
-constexpr int kDiagRows = 8;       // x^2 rows per thread per stage issued up front
+constexpr int kDiagRows = 4;       // x^2 rows (16-byte chunks) per thread per stage, at most
+constexpr int kChunks = kT16 / 8;  // 16-byte chunks per panel row
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -175,12 +176,15 @@ GPTQ_DEV void wait_vm() {
 GPTQ_DEV void wait_vm0() { wait_vm<0>(); }
 
 // Every tile also sums x^2 in fp64 for a slice of the channels of its two
-// panels (the squares of 16-bit values are exact): tile (I, J) takes slice J
-// of panel I and, off the diagonal, slice I of panel J, where slice q of a
-// panel is channels [256q/nt, 256(q+1)/nt).  Each (panel, slice) pair occurs
-// in exactly one tile, so every channel is summed once per split, and every
-// tile carries the same small share of this work.  These sums are the keys of
-// the descending-diagonal column order, so that order does not hinge on fp32
+// panels (the squares of 16-bit values are exact), in 16-byte chunks of 8
+// channels read with one ds_read_b128: tile (I, J) takes slice J of panel I
+// and, off the diagonal, slice I of panel J, where slice q of a panel is
+// chunks [32q/nt, 32(q+1)/nt).  Each (panel, slice) pair occurs in exactly
+// one tile, so every channel is summed once per split, and every tile carries
+// a small share of this work.  (Measured: one 16-byte read and 8 squares per
+// row in the first waves is faster than spreading 4-channel pieces over all
+// four waves.)  These sums are the keys of the
+// descending-diagonal column order, so that order does not hinge on fp32
 // accumulation rounding.
 //
 // Partial layout (floats): [work item][wave 4][block 16 = mb*4+nb][reg 16][lane 64]
@@ -191,7 +195,6 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
                                                          double* __restrict__ pdiag) {
   __shared__ __attribute__((aligned(16))) T sA[kSlots16][kStage16];
   __shared__ __attribute__((aligned(16))) T sB[kSlots16][kStage16];
-  __shared__ double sD[kT16];
   constexpr uint32_t kSlotBytes = kStage16 * 2;    // 24 KB
   constexpr uint32_t kSliceBytes = 16 * kRow16 * 2; // 16 token rows
   constexpr int NI = kK16 / 8;                     // copies per panel per lane per stage
@@ -270,17 +273,19 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
                  : "memory", "m0");
   };
 
-  // fp64 x^2 slices: C channels over P row phases
-  const int lo0 = (J * kT16) / nt, hi0 = ((J + 1) * kT16) / nt;
-  const int lo1 = (I * kT16) / nt, hi1 = ((I + 1) * kT16) / nt;
-  const int n0 = hi0 - lo0, n1 = (I != J) ? hi1 - lo1 : 0;
-  const int C = n0 + n1, P = kT16 / C;
-  const int dq = tid % C, dph = tid / C;
-  const bool dact = dph < P;
-  const bool dB = dq >= n0;                        // slice of panel J (in sB)
-  const int dch = dB ? lo1 + (dq - n0) : lo0 + dq;
-  const int dM = dact ? (kK16 - dph + P - 1) / P : 0;   // rows dph, dph+P, ... < kK16
-  double dsum = 0.0;
+  // fp64 x^2 slices: Cc chunks over P row phases (Cc <= 32, so P >= 8 and a
+  // thread takes at most kDiagRows = 4 of a stage's 32 rows)
+  const int cA0 = (kChunks * J) / nt, nA = (kChunks * (J + 1)) / nt - cA0;
+  const int cB0 = (kChunks * I) / nt, nB = (I != J) ? (kChunks * (I + 1)) / nt - cB0 : 0;
+  const int Cc = nA + nB;
+  const int P = (Cc > 0) ? kT16 / Cc : 1;
+  const int dci = (Cc > 0) ? tid % Cc : 0, dph = (Cc > 0) ? tid / Cc : P;
+  const bool dB = dci >= nA;                       // a chunk of panel J (in sB)
+  const int dchunk = dB ? cB0 + (dci - nA) : cA0 + dci;
+  const int dM = (dph < P) ? (kK16 - dph + P - 1) / P : 0;   // rows dph, dph+P, ... < kK16
+  double dsum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dsum[e] = 0.0;
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -325,14 +330,12 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
       const int dslot = (slot == 0) ? kSlots16 - 1 : slot - 1;
       const uint32_t bA = ldsA + (uint32_t)slot * kSlotBytes, bB = ldsB + (uint32_t)slot * kSlotBytes;
       const uint32_t nA = ldsA + (uint32_t)nslot * kSlotBytes, nB = ldsB + (uint32_t)nslot * kSlotBytes;
-      // this thread's x^2 rows of the stage (up to kDiagRows; the rest loop below)
+      // this thread's x^2 rows of the stage: one 16-byte chunk each
       const T* dst_ = dB ? sB[slot] : sA[slot];
-      uint16_t dv[kDiagRows];
+      uint4 dv[kDiagRows];
 #pragma unroll
-      for (int u = 0; u < kDiagRows; ++u) {
-        const int r = (u < dM) ? dph + P * u : 0;
-        dv[u] = *reinterpret_cast<const uint16_t*>(dst_ + swz16(r, dch));
-      }
+      for (int u = 0; u < kDiagRows; ++u)
+        if (u < dM) dv[u] = *reinterpret_cast<const uint4*>(dst_ + swz16(dph + P * u, 8 * dchunk));
       i32x4_t rn;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -365,17 +368,18 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
         if (ks == 0) {
 #pragma unroll
           for (int u = 0; u < kDiagRows; ++u) {
-            const double v = (u < dM) ? (double)Op16<T>::to_f32(dv[u]) : 0.0;
-            dsum = fma(v, v, dsum);
+            if (u < dM) {
+              const uint32_t wv[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint16_t hv = (uint16_t)((e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xFFFFu));
+                const double v = (double)Op16<T>::to_f32(hv);
+                dsum[e] = fma(v, v, dsum[e]);
+              }
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      // slices wider than kDiagRows * P rows per stage (only when nt is small)
-      for (int u = kDiagRows; u < dM; ++u) {
-        const uint16_t hv = *reinterpret_cast<const uint16_t*>(dst_ + swz16(dph + P * u, dch));
-        const double v = (double)Op16<T>::to_f32(hv);
-        dsum = fma(v, v, dsum);
       }
       slot = nslot;
     }
@@ -389,13 +393,24 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
 #pragma unroll
       for (int r = 0; r < 16; ++r) out[((i * 4 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
 
-  sD[tid] = dsum;
+  // per-phase sums through the first stage slot (copies past the item's end
+  // still land in the slots, so wait for them first), added in phase order
+  wait_vm0();
   __syncthreads();
-  if (tid < C) {
+  double* sD = reinterpret_cast<double*>(&sA[0][0]);   // [phase][chunk][8]: P * Cc * 8 <= 2048
+  if (dph < P) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sD[(dph * Cc + dci) * 8 + e] = dsum[e];
+  }
+  __syncthreads();
+  if (tid < 8 * Cc) {
+    const int ci = tid >> 3, e = tid & 7;
     double t = 0.0;
-    for (int ph = 0; ph < P; ++ph) t += sD[ph * C + tid];
-    const int pan = dB ? J : I;
-    pdiag[((size_t)s * nt + pan) * kT16 + dch] = t;
+    for (int ph = 0; ph < P; ++ph) t += sD[(ph * Cc + ci) * 8 + e];
+    const bool inB = ci >= nA;
+    const int pan = inB ? J : I;
+    const int ch = 8 * (inB ? cB0 + (ci - nA) : cA0 + ci) + e;
+    pdiag[((size_t)s * nt + pan) * kT16 + ch] = t;
   }
   }
 }
