@@ -297,7 +297,7 @@ def block_measure(P, torch, Xg, n_tokens=32768, seq_len=2048):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "single-GPU implementation: --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -61,7 +61,7 @@ typedef enum {
   GPTQ_ERR_NOT_PD = -2,      /* damped Hessian not positive definite: raise damp_percent */
   GPTQ_ERR_HIP = -3,
   GPTQ_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query returns */
-  GPTQ_ERR_UNSUPPORTED = -5  /* a valid option this build does not implement */
+  GPTQ_ERR_UNSUPPORTED = -5  /* a valid option this library does not implement */
 } gptq_status;
 
 /* The quantizer's options, as the pages' config objects name them
@@ -71,7 +71,7 @@ typedef enum {
  *                order); -1 = one group per row.  Must divide block_size, or
  *                be a multiple of it, or be -1; in-block groups must be a
  *                multiple of 4.
- *  block_size    lazy-batch width; this build supports 128 only.
+ *  block_size    lazy-batch width; this library supports 128 only.
  *  damp_percent  lambda = damp_percent * mean(diag H) is added to diag(H).
  *  desc_act      0/1: process columns by descending diag(H).
  *  sym           0 = asymmetric min-max grid: scale = (max - min)/maxq,

@@ -91,7 +91,7 @@ extern "C" const char* gptq_status_string(int status) {
     case GPTQ_ERR_NOT_PD: return "damped Hessian is not positive definite (raise damp_percent)";
     case GPTQ_ERR_HIP: return "HIP runtime error";
     case GPTQ_ERR_WORKSPACE: return "workspace missing or too small";
-    case GPTQ_ERR_UNSUPPORTED: return "option not supported by this build";
+    case GPTQ_ERR_UNSUPPORTED: return "option not supported by this library";
     default: return "unknown status";
   }
 }

@@ -1,4 +1,4 @@
-"""Convenience driver: allocate outputs and chain the C-ABI calls for one layer.
+"""Convenience wrapper: allocate outputs and chain the C-ABI calls for one layer.
 
 Only allocation and call sequencing live here; the arithmetic is in libgptq.so.
 """
