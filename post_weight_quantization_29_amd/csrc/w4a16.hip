@@ -6,8 +6,8 @@
 // RPW output rows per wave (1 for one or two activation rows, where the
 // weight stream alone sets the pace, else 4): each lane streams 16-byte groups
 // of the rows' packed codes (8 codes per word, the gptq_pack_int4 layout), forms each weight
-// as the fp32 product scale * (code - zero) (the code made an exact float by
-// OR-ing it into the mantissa of 2^23), rounds pairs of them to the
+// as the fp32 product scale * (code - zero) (the codes made exact floats with
+// one byte conversion each), rounds pairs of them to the
 // activation's 16-bit type with one packed conversion, and multiplies them
 // with up to 8 activation rows at a time with the 2-term dot instruction
 // (fp32 accumulation); a wave reduction finishes each dot product.  Each
@@ -25,13 +25,14 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 // even) into the type's packed pair, and the 2-term dot product with fp32
 // accumulation.
 template <typename T> struct Act;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 template <> struct Act<__bf16> {
   typedef bf16x2_t v2;
   static GPTQ_DEV v2 pack(float a, float b) {
-    v2 r;
-    r[0] = (__bf16)a;
-    r[1] = (__bf16)b;
-    return r;
+    // one v_cvt_pk_bf16_f32 (round to nearest even) for the pair
+    const f32x2_t f = {a, b};
+    return __builtin_convertvector(f, v2);
   }
   static GPTQ_DEV float dot2(uint32_t x, v2 w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2, x), w, acc, false);
@@ -55,25 +56,37 @@ template <> GPTQ_DEV float out_cast<float>(float v) { return v; }
 template <> GPTQ_DEV __bf16 out_cast<__bf16>(float v) { return (__bf16)v; }
 template <> GPTQ_DEV _Float16 out_cast<_Float16>(float v) { return (_Float16)v; }
 
-// code k of word p as an exact float: 2^23 + code is 0x4B000000 | code, and
-// subtracting 2^23 + zero leaves code - zero exactly
-GPTQ_DEV float code_minus_zero(uint32_t p, int k, float zb) {
-  return __builtin_bit_cast(float, ((p >> (4 * k)) & 15u) | 0x4B000000u) - zb;
+// The eight codes of word p as exact floats: the even codes sit in the bytes
+// of p & 0x0F0F0F0F and the odd ones in those of (p >> 4) & 0x0F0F0F0F, and
+// each byte converts with one v_cvt_f32_ubyteN (the masked words are kept
+// opaque so that the compiler does not fold the masks back into per-code
+// bit-field extracts).
+GPTQ_DEV void word_codes(uint32_t p, float (&c)[8]) {
+  uint32_t lo = p & 0x0F0F0F0Fu, hi = (p >> 4) & 0x0F0F0F0Fu;
+  asm volatile("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    c[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
+    c[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+  }
 }
 
-// The eight weights of word p, in packed pairs.  NATURAL: one group for the
-// word (scale s, zb = 2^23 + zero); otherwise a group per code from g_idx.
+// The eight weights of word p, in packed pairs: RN(scale * (code - zero)) in
+// fp32 (code - zero is exact), then rounded to the 16-bit type.  NATURAL: one
+// group for the word (scale s, zero zf as a float); otherwise a group per code
+// from g_idx.
 template <typename T, bool NATURAL>
-GPTQ_DEV void dequant_word(uint32_t p, int c0, float s, float zb, const float* srow, const int32_t* zrow,
+GPTQ_DEV void dequant_word(uint32_t p, int c0, float s, float zf, const float* srow, const int32_t* zrow,
                            const int32_t* g_idx, int ng, typename Act<T>::v2 (&w)[4]) {
-  float v[8];
+  float c[8], v[8];
+  word_codes(p, c);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     if (NATURAL) {
-      v[k] = s * code_minus_zero(p, k, zb);
+      v[k] = s * (c[k] - zf);
     } else {
       const int g = min(max(g_idx[c0 + k], 0), ng - 1);
-      v[k] = srow[g] * code_minus_zero(p, k, 8388608.0f + (float)zrow[g]);
+      v[k] = srow[g] * (c[k] - (float)zrow[g]);
     }
   }
 #pragma unroll
@@ -99,6 +112,7 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
   if (r0 >= d_out) return;
   const int nw = d_in >> 3;
   const float invG = 1.0f / (float)G;
+  const bool gshared = (G % (8 * WPL)) == 0;
   for (int64_t m0 = 0; m0 < m; m0 += kWRows) {
     const int mc = (int)min<int64_t>(kWRows, m - m0);
     const uint16_t* xb = X + m0 * d_in;
@@ -122,18 +136,20 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
         }
         const float* srow = scales + (size_t)r * ng;
         const int32_t* zrow = zeros + (size_t)r * ng;
+        float sc = 0.0f, zf = 0.0f;
 #pragma unroll
         for (int u = 0; u < WPL; ++u) {
           const int c0 = (q + u) * 8;
-          float sc = 0.0f, zb = 0.0f;
-          if (NATURAL) {
+          // the WPL words of a step are 8*WPL consecutive columns from a
+          // multiple of 8*WPL, so they share a group when G is a multiple of it
+          if (NATURAL && (u == 0 || !gshared)) {
             int g = (int)((float)c0 * invG);      // exact quotient after one correction
             if (g * G > c0) --g;
             if ((g + 1) * G <= c0) ++g;
             sc = srow[g];
-            zb = 8388608.0f + (float)zrow[g];
+            zf = (float)zrow[g];
           }
-          dequant_word<T, NATURAL>(pw[u], c0, sc, zb, srow, zrow, g_idx, ng, w[j][u]);
+          dequant_word<T, NATURAL>(pw[u], c0, sc, zf, srow, zrow, g_idx, ng, w[j][u]);
         }
       }
 #pragma unroll
@@ -260,15 +276,15 @@ __global__ __launch_bounds__(256) void w4a16_mfma_kernel(const uint16_t* __restr
         v2 w[4];
         const int c0 = (q0 + u) * 8;
         if (q0 + u < nw) {
-          float sc = 0.0f, zb = 0.0f;
+          float sc = 0.0f, zf = 0.0f;
           if (NATURAL) {
             int g = (int)((float)c0 * invG);
             if (g * G > c0) --g;
             if ((g + 1) * G <= c0) ++g;
             sc = srow[g];
-            zb = 8388608.0f + (float)zrow[g];
+            zf = (float)zrow[g];
           }
-          dequant_word<T, NATURAL>(pw[u], c0, sc, zb, srow, zrow, g_idx, ng, w);
+          dequant_word<T, NATURAL>(pw[u], c0, sc, zf, srow, zrow, g_idx, ng, w);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = Act<T>::pack(0.0f, 0.0f);
