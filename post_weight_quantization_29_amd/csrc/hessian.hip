@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
                                                          double* __restrict__ pdiag) {
   __shared__ __attribute__((aligned(16))) T sA[kSlots16][kStage16];
   __shared__ __attribute__((aligned(16))) T sB[kSlots16][kStage16];
-  constexpr uint32_t kSlotBytes = kStage16 * 2;    // 24 KB
+  constexpr uint32_t kSlotBytes = kStage16 * 2;    // 16 KB
   constexpr uint32_t kSliceBytes = 16 * kRow16 * 2; // 16 token rows
   constexpr int NI = kK16 / 8;                     // copies per panel per lane per stage
   constexpr int NKS = kK16 / 16;                   // k-slices per stage
@@ -324,14 +324,15 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         op[0][f][h] = tr_at<T>((f < 4 ? ldsA + offA[f] : ldsB + offB[f - 4]) + h * 2048u);
-    int slot = 0;                                  // (kk - ks0) % kSlots16
-    for (int kk = ks0; kk < ks1; ++kk) {
-      const int nslot = (slot + 1 == kSlots16) ? 0 : slot + 1;
-      const int dslot = (slot == 0) ? kSlots16 - 1 : slot - 1;
-      const uint32_t bA = ldsA + (uint32_t)slot * kSlotBytes, bB = ldsB + (uint32_t)slot * kSlotBytes;
-      const uint32_t nA = ldsA + (uint32_t)nslot * kSlotBytes, nB = ldsB + (uint32_t)nslot * kSlotBytes;
+    // Stages run in groups of kSlots16 with the ring slot a compile-time
+    // constant, so every LDS address is a lane offset plus a constant that
+    // folds into the instruction (no per-stage address arithmetic).
+    auto stage = [&]<int SLOT>(int kk) {
+      constexpr int NSLOT = (SLOT + 1) % kSlots16, DSLOT = (SLOT + kSlots16 - 1) % kSlots16;
+      const uint32_t bA = ldsA + (uint32_t)SLOT * kSlotBytes, bB = ldsB + (uint32_t)SLOT * kSlotBytes;
+      const uint32_t nA = ldsA + (uint32_t)NSLOT * kSlotBytes, nB = ldsB + (uint32_t)NSLOT * kSlotBytes;
       // this thread's x^2 rows of the stage: one 16-byte chunk each
-      const T* dst_ = dB ? sB[slot] : sA[slot];
+      const T* dst_ = dB ? sB[SLOT] : sA[SLOT];
       uint4 dv[kDiagRows];
 #pragma unroll
       for (int u = 0; u < kDiagRows; ++u)
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
                                      (uint32_t)(ks + 1) * kSliceBytes + h * 2048u);
           else
             op[nxt][f][h] = tr_at<T>((f < 4 ? nA + offA[f] : nB + offB[f - 4]) + h * 2048u);
-          if (last && n < 2 * NI) dma(rn, dslot, n);
+          if (last && n < 2 * NI) dma(rn, DSLOT, n);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (ks == 0) {
@@ -381,8 +382,18 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      slot = nslot;
+    };
+    static_assert(kSlots16 == 4, "stage groups of four");
+    int kk = ks0;                                  // stage kk uses slot (kk - ks0) % kSlots16
+    for (; kk + 4 <= ks1; kk += 4) {
+      stage.template operator()<0>(kk);
+      stage.template operator()<1>(kk + 1);
+      stage.template operator()<2>(kk + 2);
+      stage.template operator()<3>(kk + 3);
     }
+    if (kk < ks1) stage.template operator()<0>(kk++);
+    if (kk < ks1) stage.template operator()<1>(kk++);
+    if (kk < ks1) stage.template operator()<2>(kk++);
   }
 
   float* out = partial + ((size_t)w * 4 + wave) * (16 * 16 * 64);
