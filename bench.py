@@ -336,7 +336,9 @@ def main():
     G = d if q.group_size == -1 else q.group_size
     ng = (d + G - 1) // G
     H = torch.zeros((d, d), dtype=torch.float32, device=dev)
-    hdiag = torch.zeros((d,), dtype=torch.float64, device=dev)
+    # fp64 diagonal keys only where the column order needs them (desc_act);
+    # without them damping takes mean(diag H) from H itself
+    hdiag = torch.zeros((d,), dtype=torch.float64, device=dev) if q.desc_act else None
     U = torch.empty((d, d), dtype=torch.float32, device=dev)
     perm = torch.empty((d,), dtype=torch.int32, device=dev)
     codes = torch.empty((d_out, d), dtype=torch.uint8, device=dev)
@@ -356,7 +358,8 @@ def main():
     def step(ev=None):
         rec(ev, 0)
         H.zero_()
-        hdiag.zero_()
+        if hdiag is not None:
+            hdiag.zero_()
         rec(ev, 1)
         P.gptq_hessian_accumulate(H, Xg, hdiag, ws_h)
         rec(ev, 2)
@@ -426,8 +429,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved_tf, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "kernel": ("gptq_hessian_accumulate: syrk16_kernel<bf16> + syrk_reduce_kernel<4, 512> "
-                                "+ diag_reduce_kernel"),
+                     "kernel": ("gptq_hessian_accumulate: syrk16_kernel<bf16> + syrk_reduce_kernel<4, 512>"
+                                + (" + diag_reduce_kernel (fp64 diagonal keys)" if q.desc_act else "")),
                      "work_per_launch": f"N*d*(d+1) = {h_flops:.4g} flop"},
     }
     if not args.no_extras:

@@ -187,8 +187,10 @@ GPTQ_DEV void wait_vm0() { wait_vm<0>(); }
 // descending-diagonal column order, so that order does not hinge on fp32
 // accumulation rounding.
 //
+// DIAG = false (no diagonal requested) leaves all of this out.
+//
 // Partial layout (floats): [work item][wave 4][block 16 = mb*4+nb][reg 16][lane 64]
-template <typename T>
+template <typename T, bool DIAG>
 __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X, int64_t n_tokens,
                                                          int d, int nt, int ntiles, int splits,
                                                          int nk, float* __restrict__ partial,
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
       uint4 dv[kDiagRows];
 #pragma unroll
       for (int u = 0; u < kDiagRows; ++u)
-        if (u < dM) dv[u] = *reinterpret_cast<const uint4*>(dst_ + swz16(dph + P * u, 8 * dchunk));
+        if (DIAG && u < dM) dv[u] = *reinterpret_cast<const uint4*>(dst_ + swz16(dph + P * u, 8 * dchunk));
       i32x4_t rn;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
           if (last && n < 2 * NI) dma(rn, DSLOT, n);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (ks == 0) {
+        if (DIAG && ks == 0) {
 #pragma unroll
           for (int u = 0; u < kDiagRows; ++u) {
             if (u < dM) {
@@ -406,6 +408,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
 
   // per-phase sums through the first stage slot (copies past the item's end
   // still land in the slots, so wait for them first), added in phase order
+  if (!DIAG) continue;
   wait_vm0();
   __syncthreads();
   double* sD = reinterpret_cast<double*>(&sA[0][0]);   // [phase][chunk][8]: P * Cc * 8 <= 2048
@@ -694,12 +697,16 @@ extern "C" int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, g
   // 16-bit path: one resident workgroup per CU (256 CUs), persistent over items
   const unsigned pgrid = std::min<unsigned>(256u, items);
   const unsigned pg = (pgrid + kXCD - 1) / kXCD * kXCD;
+  // the fp64 diagonal only when it is asked for (the 16-bit kernels then do
+  // no diagonal work at all; H is the same either way)
   if (x_dtype == GPTQ_BF16) {
-    syrk16_kernel<__bf16><<<pg, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in,
-                                                 p.nt, p.ntiles, p.splits, (int)p.nk, partial, pdiag);
+    auto k = hdiag ? syrk16_kernel<__bf16, true> : syrk16_kernel<__bf16, false>;
+    k<<<pg, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
+                         (int)p.nk, partial, pdiag);
   } else if (x_dtype == GPTQ_F16) {
-    syrk16_kernel<_Float16><<<pg, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in,
-                                                   p.nt, p.ntiles, p.splits, (int)p.nk, partial, pdiag);
+    auto k = hdiag ? syrk16_kernel<_Float16, true> : syrk16_kernel<_Float16, false>;
+    k<<<pg, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
+                         (int)p.nk, partial, pdiag);
   } else {
     syrk32_kernel<<<items, 256, 0, s>>>(static_cast<const float*>(X), n_tokens, d_in, p.nt, p.ntiles,
                                         p.splits, p.nk, partial, pdiag);

@@ -49,6 +49,18 @@ def test_hessian_parity(x_dtype, d, n):
     assert off.max() <= 1e-4, off.max()
 
 
+@pytest.mark.parametrize("x_dtype,d,n", [("bf16", 1240, 5000), ("f16", 520, 3000), ("bf16", 4096, 6000)])
+def test_hessian_without_keys_same_h(x_dtype, d, n):
+    # without the fp64 diagonal the kernels leave its work out; H must not change
+    say(f"[hessian/no keys] dtype={x_dtype} d={d} n={n}")
+    c = gi.random_case(2, d, n, seed=300 + d, x_dtype=x_dtype, dist="t", outlier_frac=0.01,
+                       outlier_factor=20.0)
+    k = n // 3
+    Ha = gpu_hessian([c.X[:k], c.X[k:]], x_dtype, d)
+    Hb = gpu_hessian([c.X[:k], c.X[k:]], x_dtype, d, keys=False)
+    assert bool(torch.equal(Ha, Hb))
+
+
 def test_hessian_zero_tokens_leaves_h():
     import post_weight_quantization_29_amd as P
     H = torch.full((64, 64), 3.0, device="cuda")
@@ -182,6 +194,31 @@ def test_gptq_layer_parity(case):
     if res.packed is not None:
         pk = res.packed.cpu().numpy().view(np.uint32)
         assert np.array_equal(pk, o.pack_int4(codes))
+
+
+@pytest.mark.parametrize("case", [CASES[1], CASES[4]], ids=["100x384_t", "96x640_g256_t"])
+def test_gptq_layer_parity_without_keys(case):
+    # desc_act = 0 needs no fp64 diagonal: damping then takes mean(diag H) from H
+    import post_weight_quantization_29_amd as P
+    d_out, d_in, n, w_dtype, x_dtype, bits, G, desc, kind = case
+    assert desc == 0
+    say(f"[gptq/no keys] {case}")
+    W, X = _case(d_out, d_in, n, w_dtype, x_dtype, kind, seed=1000 + d_in + d_out)
+    W64 = gi.to_float64(W, w_dtype)
+    H64 = o.hessian([gi.to_float64(X, x_dtype)], d_in)
+    ref = o.gptq(W64, H64, bits=bits, group_size=G, block_size=128, damp_percent=0.01, desc_act=False)
+    Hg = gpu_hessian([X], x_dtype, d_in, keys=False)
+    cfg = P.make_config(bits=bits, group_size=G, block_size=128, damp_percent=0.01, desc_act=0)
+    res = P.quantize_layer_outputs(to_dev(W, w_dtype), Hg, cfg)
+    torch.cuda.synchronize()
+    codes = res.codes.cpu().numpy()
+    par = compare_quant(ref, W64, H64, codes, res.scales.cpu().numpy(), res.zeros.cpu().numpy(),
+                        res.Q.cpu().numpy(), d_in if G == -1 else G)
+    say(f"  {par}")
+    assert np.array_equal(res.perm.cpu().numpy(), ref.perm)
+    assert par.agree >= 0.999 and par.first_not_tie == 0
+    assert par.scale_rel <= 1e-3 and par.zero_mismatch == 0 and par.q_bad == 0
+    assert par.obj_rel <= 1e-3
 
 
 VARIANTS = [
