@@ -97,6 +97,7 @@ typedef struct {
  *           (the squares of bf16/fp16 values are exact).  gptq_prepare_hinv
  *           orders columns by these keys when given, so the desc_act order is
  *           the exact one and does not depend on fp32 accumulation rounding.
+ *           NULL: the 16-bit kernels do none of this work (H is the same).
  *  X        [n_tokens x d_in], token-major, of x_dtype (bf16/fp16 multiply
  *           exactly in fp32 on MFMA; fp32 inputs use the fp32 MFMA).
  *  d_in     1..65536, multiple of 8.  n_tokens >= 0 (0 leaves H unchanged).
