@@ -347,8 +347,35 @@ GPTQ_DEV void leaf_inverse(float* Vb, float (*ring)[64], float (*rs)[4], const i
   for (int r = 0; r < 16; ++r) Vb[(16 * h + r) * kVP + i] = y[r];
 }
 
+// Trailing workgroups of the factor launch for block k: workgroup `local` of
+// block k-1's update of the rows after row block k (the upper 128 x 128 tiles
+// of A[(k+1)*128:, (k+1)*128:], row by row), with the same tile contraction as
+// a separate trailing-update launch.  They run on the CUs the factor leaves
+// idle and stage their operands in its LDS arrays.
+GPTQ_DEV void trail_tile(float* A, int np, int k, int local, float* sA, float* sB) {
+  const int c0 = (k + 1) * kNB, rest = np - c0;
+  const float* Arow = A + (size_t)(k - 1) * kNB * np + c0;
+  const GemmProblem P{Arow, Arow, A + (size_t)c0 * np + c0, nullptr, np, np, np, rest, rest, kNB};
+  const int tn = rest / kGT;
+  int r = 0, rem = local;
+  while (rem >= tn - r) { rem -= tn - r; ++r; }
+  const int m0 = r * kGT, n0 = (r + rem) * kGT;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  float cold[2][2][16];
+  gemm_tile_load_c(P, m0, n0, cold);
+  gemm_tile_contract<true, true>(P, m0, n0, 0, kNB, sA, sB, acc);
+  gemm_tile_store(P, m0, n0, -1.0f, 1.0f, acc, cold);
+}
+
 __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A, int np, int k,
-                                                         float* __restrict__ Dinv, int* __restrict__ flag) {
+                                                         float* __restrict__ Dinv, int* __restrict__ flag,
+                                                         int ntrail) {
   __shared__ __attribute__((aligned(16))) float M[kNB * kLP];
   __shared__ __attribute__((aligned(16))) float T[kNB * kLP];
   __shared__ __attribute__((aligned(16))) float V[4][32 * kVP];
@@ -357,6 +384,10 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A, 
   __shared__ __attribute__((aligned(16))) float yx[64];
   __shared__ int flags[kLeafSteps];
 
+  if ((int)blockIdx.x >= (int)gridDim.x - ntrail) {
+    trail_tile(A, np, k, (int)blockIdx.x - ((int)gridDim.x - ntrail), M, T);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;                     // 0: identity, t >= 1: column block k + t
   const float* Akk = A + (size_t)k * kNB * np + (size_t)k * kNB;
@@ -592,18 +623,25 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
   GPTQ_LAUNCH_CHECK();
 
   // 4. Cholesky A = R^T R: per block, diagonal factor + panel in one launch,
-  //    then the trailing update; R_kk^-1 goes to Dinv (in Z's space, which the
-  //    triangular inverse only uses later) and then onto A's diagonal blocks
+  //    then the trailing update, split so that only its first row block sits
+  //    between two factors (lookahead); R_kk^-1 goes to Dinv (in Z's space,
+  //    which the triangular inverse only uses later) and then onto A's
+  //    diagonal blocks
   float* Dinv = Z;
   for (int k = 0; k < nb; ++k) {
     const int rest = np - (k + 1) * kNB;
-    chol_panel_kernel<<<1 + rest / kNB, 256, 0, s>>>(A, np, k, Dinv, flag);
+    // block k-1's update of the row blocks after block k rides along with
+    // block k's factor (other CUs; it touches neither row block k nor Dinv) ...
+    const int ntr = (k >= 1 && rest > 0) ? gemm_upper_tiles(rest, rest) : 0;
+    chol_panel_kernel<<<1 + rest / kNB + ntr, 256, 0, s>>>(A, np, k, Dinv, flag, ntr);
     GPTQ_LAUNCH_CHECK();
     if (rest <= 0) continue;
     float* Arow = A + (size_t)k * kNB * np + (size_t)(k + 1) * kNB;   // R_k,rest
     float* Atrail = A + (size_t)(k + 1) * kNB * np + (size_t)(k + 1) * kNB;
-    // A_rest -= R_k,rest^T R_k,rest (upper tiles)
-    gemm_f32<true>(Arow, np, Arow, np, Atrail, np, rest, rest, kNB, -1.0f, 1.0f, 0, 0, 1, s);
+    // ... and block k's update of row block k + 1 alone runs before block k+1's
+    // factor: A[k+1, k+1:] -= R_k,k+1^T R_k,rest.  Every element gets the
+    // same tile contraction as one upper-tile update of A_rest would give.
+    gemm_f32<true>(Arow, np, Arow, np, Atrail, np, kNB, rest, kNB, -1.0f, 1.0f, 0, 0, 0, s);
     GPTQ_LAUNCH_CHECK();
   }
   dinv_scatter_kernel<<<nb, 256, 0, s>>>(Dinv, A, np);
