@@ -72,7 +72,10 @@ def test_hessian_zero_tokens_leaves_h():
 
 # ------------------------------------------------------------------ factor
 
-@pytest.mark.parametrize("d,desc", [(256, 0), (256, 1), (384, 1), (200, 0), (1000, 1), (2048, 1)])
+# 8: one block (no trailing update); 129: a second block with one real column;
+# 300: three blocks, the last ragged (the lookahead's smallest cases)
+@pytest.mark.parametrize("d,desc", [(256, 0), (256, 1), (384, 1), (200, 0), (1000, 1), (2048, 1),
+                                    (8, 0), (129, 1), (300, 0)])
 def test_prepare_hinv_parity(d, desc):
     say(f"[hinv] d={d} desc_act={desc}")
     import post_weight_quantization_29_amd as P
