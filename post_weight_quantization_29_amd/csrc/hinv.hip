@@ -628,11 +628,12 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
   //    which the triangular inverse only uses later) and then onto A's
   //    diagonal blocks
   float* Dinv = Z;
+  bool ride = false;   // block k-1's update of the rows after row block k rides with factor k
   for (int k = 0; k < nb; ++k) {
     const int rest = np - (k + 1) * kNB;
     // block k-1's update of the row blocks after block k rides along with
     // block k's factor (other CUs; it touches neither row block k nor Dinv) ...
-    const int ntr = (k >= 1 && rest > 0) ? gemm_upper_tiles(rest, rest) : 0;
+    const int ntr = (ride && rest > 0) ? gemm_upper_tiles(rest, rest) : 0;
     chol_panel_kernel<<<1 + rest / kNB + ntr, 256, 0, s>>>(A, np, k, Dinv, flag, ntr);
     GPTQ_LAUNCH_CHECK();
     if (rest <= 0) continue;
@@ -641,7 +642,14 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
     // ... and block k's update of row block k + 1 alone runs before block k+1's
     // factor: A[k+1, k+1:] -= R_k,k+1^T R_k,rest.  Every element gets the
     // same tile contraction as one upper-tile update of A_rest would give.
-    gemm_f32<true>(Arow, np, Arow, np, Atrail, np, kNB, rest, kNB, -1.0f, 1.0f, 0, 0, 0, s);
+    // Riding tiles run one workgroup per CU (the factor's LDS); when they
+    // would need more than two rounds of the CUs the next factor leaves free,
+    // the whole update runs on its own instead (two workgroups per CU).
+    const int next_tiles = gemm_upper_tiles(rest - kNB, rest - kNB);
+    const int free_cus = 256 - (1 + (rest - kNB) / kNB);
+    ride = next_tiles <= 2 * free_cus;
+    gemm_f32<true>(Arow, np, Arow, np, Atrail, np, ride ? kNB : rest, rest, kNB, -1.0f, 1.0f, 0, 0,
+                   ride ? 0 : 1, s);
     GPTQ_LAUNCH_CHECK();
   }
   dinv_scatter_kernel<<<nb, 256, 0, s>>>(Dinv, A, np);
