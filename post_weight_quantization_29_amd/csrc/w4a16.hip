@@ -3,8 +3,9 @@
 // and then multiplied; what the 4 bits save is the bytes moved, so at small
 // batch this product is bound by HBM).
 //
-// RPW output rows per wave (1 for one or two activation rows, where the
-// weight stream alone sets the pace, else 4): each lane streams 16-byte groups
+// RPW output rows per wave (1 for one or two activation rows, else 4; long
+// rows with one or two activation rows take w4a16_shared_x_kernel below, which
+// loads each activation chunk once per workgroup): each lane streams 16-byte groups
 // of the rows' packed codes (8 codes per word, the gptq_pack_int4 layout), forms each weight
 // as the fp32 product scale * (code - zero) (the codes made exact floats with
 // one byte conversion each), rounds pairs of them to the
@@ -183,6 +184,87 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
   }
 }
 
+// One or two activation rows over long rows (natural groups): the four waves
+// of a workgroup (four output rows) walk the same columns, so each step's
+// activation chunk (256 words = 2048 columns per activation row) is loaded
+// once per workgroup into LDS (double buffered, one barrier per step) instead
+// of once per wave; the weights are formed and dotted exactly as above.
+template <typename T, typename TY>
+__global__ __launch_bounds__(256) void w4a16_shared_x_kernel(const uint16_t* __restrict__ X, int m, int d_in,
+                                                             const uint32_t* __restrict__ packed,
+                                                             const float* __restrict__ scales,
+                                                             const int32_t* __restrict__ zeros, int G,
+                                                             int ng, int d_out, TY* __restrict__ Y) {
+  typedef typename Act<T>::v2 v2;
+  __shared__ uint4 sX[2][2][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = blockIdx.x * 4 + wave;
+  const int r = min(r0, d_out - 1);            // rows past the end: computed, not stored
+  const int nw = d_in >> 3;
+  const float invG = 1.0f / (float)G;
+  const bool gshared = (G % 32) == 0;
+  const uint32_t* prow = packed + (size_t)r * nw;
+  const float* srow = scales + (size_t)r * ng;
+  const int32_t* zrow = zeros + (size_t)r * ng;
+  float acc[2] = {0.0f, 0.0f};
+  int buf = 0;
+  for (int q0 = 0; q0 < nw; q0 += 256) {
+    const int q = q0 + 4 * lane;
+    uint4 p4 = make_uint4(0u, 0u, 0u, 0u);
+    if (q < nw) p4 = *reinterpret_cast<const uint4*>(prow + q);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i < m) {
+        const int qx = q0 + tid;
+        sX[buf][i][tid] = (qx < nw) ? *reinterpret_cast<const uint4*>(X + (size_t)i * d_in + (size_t)qx * 8)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    // also orders this buffer's writes after the reads two steps back
+    __syncthreads();
+    if (q < nw) {
+      const uint32_t pw[4] = {p4.x, p4.y, p4.z, p4.w};
+      v2 w[4][4];
+      float sc = 0.0f, zf = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c0 = (q + u) * 8;
+        if (u == 0 || !gshared) {
+          int g = (int)((float)c0 * invG);      // exact quotient after one correction
+          if (g * G > c0) --g;
+          if ((g + 1) * G <= c0) ++g;
+          sc = srow[g];
+          zf = (float)zrow[g];
+        }
+        dequant_word<T, true>(pw[u], c0, sc, zf, srow, zrow, nullptr, ng, w[u]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (i < m) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint4 xv = sX[buf][i][4 * lane + u];
+            float a = acc[i];
+            a = Act<T>::dot2(xv.x, w[u][0], a);
+            a = Act<T>::dot2(xv.y, w[u][1], a);
+            a = Act<T>::dot2(xv.z, w[u][2], a);
+            a = Act<T>::dot2(xv.w, w[u][3], a);
+            acc[i] = a;
+          }
+        }
+      }
+    }
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float v = acc[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0 && i < m && r0 < d_out) Y[(size_t)i * d_out + r0] = out_cast<TY>(v);
+  }
+}
+
 // ---------------------------------------------------------------- many activation rows
 // The same product as a tiled MFMA GEMM, for batches of activation rows where
 // the weights are worth dequantizing once per 128 rows of X: a workgroup
@@ -329,6 +411,8 @@ __global__ __launch_bounds__(256) void w4a16_mfma_kernel(const uint16_t* __restr
 
 // activation rows from which the tiled MFMA product is used
 constexpr int64_t kMfmaMinRows = 64;
+// columns from which one or two activation rows are shared through LDS
+constexpr int kSharedXMinCols = 8192;
 
 template <typename T, typename TY, int RPW>
 static void launch_w4a16_rpw(const uint16_t* x, int64_t m, int d_in, const uint32_t* packed, const float* scales,
@@ -363,6 +447,16 @@ static void launch_w4a16(const void* X, int64_t m, int d_in, const uint32_t* pac
       else w4a16_mfma_kernel<T, TY, true, false><<<grid, 256, 0, s>>>(x, m, d_in, packed, scales, zeros, nullptr, G, ng, d_out, y);
     }
   } else if (m <= 2) {
+    // long rows with natural groups: one activation load per workgroup
+    // (measured at 8192 x 28672: one row 46.8 -> 44.4 us, two rows 76 -> 58 us;
+    // at 4096 columns the extra barrier does not pay)
+    const bool shared_x = !g_idx && d_in >= kSharedXMinCols && (d_in % 32) == 0 &&
+                          ((reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(x)) & 15) == 0;
+    if (shared_x) {
+      w4a16_shared_x_kernel<T, TY><<<(unsigned)((d_out + 3) / 4), 256, 0, s>>>(x, (int)m, d_in, packed, scales,
+                                                                               zeros, G, ng, d_out, y);
+      return;
+    }
     launch_w4a16_rpw<T, TY, 1>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y, s);
   } else {
     launch_w4a16_rpw<T, TY, 4>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y, s);

@@ -60,6 +60,10 @@ CASES = [
     (13, 100, 512, -1, 0, "bf16", "f16"),
     (5, 70, 4104, 8, 1, "f16", "f16"),
     (2, 33, 96, 32, 0, "f16", "bf16"),
+    # long rows, one or two activation rows: the activations shared through LDS
+    # (d_out not a multiple of 4: the last workgroup's extra rows are not stored)
+    (1, 130, 9216, 128, 0, "bf16", "f32"),
+    (2, 70, 8192, 64, 0, "f16", "bf16"),
     # 32 or more activation rows: the tiled MFMA product
     (200, 300, 1024, 64, 1, "f16", "f32"),
     (128, 4096, 4096, 128, 0, "bf16", "bf16"),
