@@ -36,9 +36,11 @@ Readings of open points (each also listed in the design notes):
     (max == min == a) uses the range [min(a,0), max(a,0)]; a == 0 gives
     scale 1, zero 0.
   * Round half to even for both roundings; true division.
-  * Integer decisions (the zero point and each code) are taken in the same
-    precision as the GPU kernel: float32 (``decision="f32"``, the default).
-    Every other quantity is float64.  ``decision="f64"`` takes them in float64.
+  * Every quantity is float64, the integer decisions (each zero point and each
+    code) included: rint(-min/scale) and rint(w/scale) of float64 values with
+    true float64 division.  ``decision="f32"`` (float32 operands for those two
+    roundings only) is kept for a pin showing that the page's worked example
+    does not depend on that precision; nothing else uses it.
 """
 from __future__ import annotations
 
@@ -78,8 +80,13 @@ def hessian(chunks: Iterable[np.ndarray], d_in: int) -> np.ndarray:
         else:  # pragma: no cover
             H += 2.0 * (xc.T @ xc)
     if _dsyrk is not None:
-        low = np.tril(H)
-        H = low + np.tril(H, -1).T
+        # dsyrk filled the lower triangle: copy it to the upper one, a band of
+        # columns at a time (no full-size temporaries at large d)
+        for c0 in range(0, d_in, 1024):
+            c1 = min(d_in, c0 + 1024)
+            H[c0:c1, c1:] = H[c1:, c0:c1].T
+            blk = H[c0:c1, c0:c1]
+            blk[np.triu_indices(c1 - c0, 1)] = blk.T[np.triu_indices(c1 - c0, 1)]
     return np.ascontiguousarray(H)
 
 
@@ -137,7 +144,7 @@ def _f(x, decision):
     return np.asarray(x, dtype=np.float32 if decision == "f32" else np.float64)
 
 
-def group_params(seg: np.ndarray, maxq: int, decision: str = "f32", sym: bool = False):
+def group_params(seg: np.ndarray, maxq: int, decision: str = "f64", sym: bool = False):
     """Per row of seg [rows, g]: scale = (max - min)/maxq, zero = rint(-min/scale).
     Returns (scale, zero) with scale in the decision precision and zero an
     integer-valued array of the same type.
@@ -164,7 +171,7 @@ def group_params(seg: np.ndarray, maxq: int, decision: str = "f32", sym: bool = 
     return scale.astype(xmin.dtype), (zero + zero_t).astype(xmin.dtype)
 
 
-def quantize(w: np.ndarray, scale, zero, maxq: int, decision: str = "f32"):
+def quantize(w: np.ndarray, scale, zero, maxq: int, decision: str = "f64"):
     """code = clamp(rint(w/scale) + zero, 0, maxq) taken in the decision
     precision; q = scale*(code - zero) returned in float64."""
     t = _f(w, decision) / _f(scale, decision)
@@ -210,14 +217,13 @@ def prepare(H: np.ndarray, damp_percent: float = 0.01, desc_act: bool = False) -
     """Order ([P5] 2.2 "first"), damp ([P5] 3.3), then the factor of the damped,
     permuted H's inverse ([P5] 2.2 "third")."""
     perm = act_order(H, desc_act)
-    Hp = H[np.ix_(perm, perm)]
-    Hd, lam = damp(Hp, damp_percent)
+    Hd, lam = damp(H[np.ix_(perm, perm)], damp_percent)
     return Prepared(perm=perm, lam=lam, U=hinv_factor(Hd))
 
 
 def gptq(W: np.ndarray, H: np.ndarray, *, bits: int = 4, group_size: int = 128,
          block_size: int = 128, damp_percent: float = 0.01, desc_act: bool = False,
-         decision: str = "f32", prepared: Optional[Prepared] = None,
+         decision: str = "f64", prepared: Optional[Prepared] = None,
          sym: bool = False) -> GPTQResult:
     """The column loop.  ``prepared`` (from ``prepare(H, damp_percent,
     desc_act)``) lets several quantizer settings share one H's order and
@@ -271,7 +277,7 @@ def gptq(W: np.ndarray, H: np.ndarray, *, bits: int = 4, group_size: int = 128,
 
 
 def rtn(W: np.ndarray, *, bits: int = 4, group_size: int = 128,
-        perm: Optional[np.ndarray] = None, decision: str = "f32", sym: bool = False):
+        perm: Optional[np.ndarray] = None, decision: str = "f64", sym: bool = False):
     """Round-to-nearest baseline ([P2] section 二, the naive min-max grid; [P5]
     2.3 compares GPTQ against it): same grid and grouping, no compensation.
     Returns (codes, Q) in original column order."""
@@ -299,11 +305,18 @@ def rtn(W: np.ndarray, *, bits: int = 4, group_size: int = 128,
 # 6. objective and packing
 # ----------------------------------------------------------------------------
 
+def objective_rows(W: np.ndarray, Q: np.ndarray, H: np.ndarray) -> np.ndarray:
+    """Per output row r: ||(W_r - Q_r) X^T||^2 = 1/2 D_r H D_r^T with D = W - Q
+    and the undamped H = 2 X^T X (rows are independent, so the layer's error is
+    their sum)."""
+    D = np.asarray(W, np.float64) - np.asarray(Q, np.float64)
+    return 0.5 * np.sum((D @ H) * D, axis=1)
+
+
 def objective(W: np.ndarray, Q: np.ndarray, H: np.ndarray) -> float:
     """Layer reconstruction error ||(W - Q) X^T||_F^2 = 1/2 tr(D H D^T) with
     D = W - Q and the undamped H = 2 X^T X."""
-    D = np.asarray(W, np.float64) - np.asarray(Q, np.float64)
-    return 0.5 * float(np.sum((D @ H) * D))
+    return float(np.sum(objective_rows(W, Q, H)))
 
 
 def pack_int4(codes: np.ndarray) -> np.ndarray:

@@ -56,7 +56,9 @@ def test_factor_one_is_rtn(G):
     rng = np.random.default_rng(1)
     W = (rng.standard_normal((6, 64)) * 0.02).astype(np.float16).astype(np.float64)
     q = a.quantize_scaled(W, np.ones(64, np.float32), bits=4, group_size=G)
-    codes, Q = g.rtn(W, bits=4, group_size=G)
+    # AWQ's grid is taken on the fp32 products W*s, so with s = 1 it is the
+    # round-to-nearest grid with its decisions in float32
+    codes, Q = g.rtn(W, bits=4, group_size=G, decision="f32")
     assert np.array_equal(q.codes, codes) and np.array_equal(q.Qhat, Q)
 
 
