@@ -19,23 +19,13 @@
  *    gptq_layer_error, which is host memory.  The library allocates no device
  *    memory; scratch memory comes in through ws/ws_bytes, sized by the
  *    matching *_workspace_size query.  Workspaces need 256-byte alignment
- *    (any hipMalloc / torch allocation satisfies this).  Its only state is,
- *    per device, one extra stream and two events, created on first use.
- *  - All work is ordered on stream s: it starts after the work already on s
- *    and is complete, as seen from s, before anything enqueued on s later.
- *    gptq_quantize_layer with groups wider than the 128-column block, for
- *    layers of 2^25 weights or more, puts part of its blocked loop on the
- *    device's extra stream (a trailing update overlapping the next block's
- *    panel), ordered against s with events and joined back to s before it
- *    returns; the results are the same bit for bit as on one stream
- *    (GPTQ_LOOKAHEAD=0 in the environment keeps everything on s).  With
- *    groups inside the block it stays on s, running each block's column loop
- *    in the same launch as the previous block's trailing update, also with
- *    the same results bit for bit (GPTQ_FUSED_STEP=0 selects one launch per
- *    step).
- *    The enqueue of such a call holds a per-device lock.  Only
- *    gptq_prepare_hinv and gptq_layer_error synchronize s (to read one
- *    device flag or scalar).
+ *    (any hipMalloc / torch allocation satisfies this).
+ *  - The library keeps no state between calls (no handles, no globals) and
+ *    reads no environment variables: every option is an argument.
+ *  - All work is enqueued on stream s, in stream order: it starts after the
+ *    work already on s and is complete, as seen from s, before anything
+ *    enqueued on s later.  Only gptq_prepare_hinv and gptq_layer_error
+ *    synchronize s (to read one device flag or scalar).
  *  - Argument errors return GPTQ_ERR_INVALID_ARG (or GPTQ_ERR_WORKSPACE)
  *    before anything is enqueued.  HIP failures return GPTQ_ERR_HIP.
  *  - Layouts are row-major.  Columns of W are input channels.  X is
@@ -78,7 +68,12 @@ typedef enum {
  *                zero = rint(-min/scale).  1 = symmetric grid (the ms-swift
  *                review page's sym=True; no formula is given, the plainest
  *                reading is used): m = max(|min|, |max|), scale = 2m/maxq,
- *                zero = (maxq + 1)/2 (scale 1 for an all-zero group). */
+ *                zero = (maxq + 1)/2 (scale 1 for an all-zero group).
+ *  per_block_steps  0 (default): with groups inside the block, each block's
+ *                column loop runs in the same launch as the previous block's
+ *                lazy update of the later columns.  1: one launch per step
+ *                (column loop, then lazy update).  The results are the same
+ *                bit for bit; 1 exists to show that. */
 typedef struct {
   int32_t bits;
   int32_t group_size;
@@ -86,6 +81,7 @@ typedef struct {
   float damp_percent;
   int32_t desc_act;
   int32_t sym;
+  int32_t per_block_steps;
 } gptq_config;
 
 /* ---------------------------------------------------------------- Hessian
@@ -99,7 +95,8 @@ typedef struct {
  *           the exact one and does not depend on fp32 accumulation rounding.
  *           NULL: the 16-bit kernels do none of this work (H is the same).
  *  X        [n_tokens x d_in], token-major, of x_dtype (bf16/fp16 multiply
- *           exactly in fp32 on MFMA; fp32 inputs use the fp32 MFMA).
+ *           exactly in fp32 on MFMA; fp32 inputs use the fp32 MFMA), 16-byte
+ *           aligned (the kernels load 16 bytes at a time; INVALID_ARG else).
  *  d_in     1..65536, multiple of 8.  n_tokens >= 0 (0 leaves H unchanged).
  *  ws       scratch of gptq_hessian_workspace_size(n_tokens, d_in) bytes
  *           (partial sums of the split token range; the result does not
@@ -137,7 +134,10 @@ int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_in, float d
  * clamp(rint(w/scale) + zero, 0, maxq); q = scale*(code - zero);
  * e = (w - q)/U[k][k]; the later columns of the 128-column block take
  * w -= e * U[k][.] at once, the columns after the block take one lazy update
- * W -= Err * U[block rows][after] at the block's end.
+ * W -= Err * U[block rows][after] at the block's end.  The block's running
+ * weights, the grid and every integer decision (zero point, code) are fp64;
+ * the work copy of W, U and the lazy update are fp32.  scales are the fp64
+ * scales rounded to fp32.
  *  W       [d_out x d_in] of w_dtype, original column order, unchanged.
  *  U, perm as produced by gptq_prepare_hinv (processing order).
  *  codes   [d_out x d_in] uint8 output, original column order.

@@ -35,7 +35,8 @@ class NotPositiveDefinite(GPTQError):
 class gptq_config(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("damp_percent", ctypes.c_float),
-                ("desc_act", ctypes.c_int32), ("sym", ctypes.c_int32)]
+                ("desc_act", ctypes.c_int32), ("sym", ctypes.c_int32),
+                ("per_block_steps", ctypes.c_int32)]
 
 
 _lib = None
@@ -127,15 +128,24 @@ def _dev(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def _ws(nbytes: int, ws: Optional[torch.Tensor], device) -> torch.Tensor:
+def _ws(nbytes: int, ws: Optional[torch.Tensor], device, stream=None) -> torch.Tensor:
+    """The caller's workspace, or a fresh one from torch's caching allocator.
+    A fresh one is allocated on the stream the call's work goes to, so that
+    the allocator reuses its memory only after that work (the call may return
+    before its kernels have run)."""
     if ws is not None:
         return ws
-    return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
+    if stream is None:
+        return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
 
 
 def make_config(bits: int = 4, group_size: int = 128, block_size: int = 128,
-                damp_percent: float = 0.01, desc_act: int = 0, sym: int = 0) -> gptq_config:
-    return gptq_config(bits, group_size, block_size, damp_percent, int(desc_act), int(sym))
+                damp_percent: float = 0.01, desc_act: int = 0, sym: int = 0,
+                per_block_steps: int = 0) -> gptq_config:
+    return gptq_config(bits, group_size, block_size, damp_percent, int(desc_act), int(sym),
+                       int(per_block_steps))
 
 
 # ---------------------------------------------------------------- C-ABI calls
@@ -155,7 +165,7 @@ def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, hdiag: Optional[to
         _dev(hdiag, "hdiag")
         assert hdiag.dtype == torch.float64 and hdiag.numel() == d
     need = gptq_hessian_workspace_size(n, d)
-    ws = _ws(need, ws, X.device)
+    ws = _ws(need, ws, X.device, stream)
     _check(lib().gptq_hessian_accumulate(_ptr(H), _ptr(hdiag), _ptr(X), _DTYPE[X.dtype], n, d,
                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "gptq_hessian_accumulate")
@@ -174,7 +184,7 @@ def gptq_prepare_hinv(H: torch.Tensor, damp_percent: float, desc_act: int, U: to
     if hdiag is not None:
         _dev(hdiag, "hdiag")
         assert hdiag.dtype == torch.float64 and hdiag.numel() == d
-    ws = _ws(gptq_prepare_hinv_workspace_size(d), ws, H.device)
+    ws = _ws(gptq_prepare_hinv_workspace_size(d), ws, H.device, stream)
     _check(lib().gptq_prepare_hinv(_ptr(H), _ptr(hdiag), d, float(damp_percent), int(desc_act),
                                    _ptr(U), _ptr(perm), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "gptq_prepare_hinv")
@@ -196,7 +206,7 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, cf
     d_out, d_in = W.shape
     assert codes.dtype == torch.uint8 and scales.dtype == torch.float32
     assert zeros.dtype == torch.int32 and g_idx.dtype == torch.int32
-    ws = _ws(gptq_quantize_workspace_size(d_out, d_in, cfg), ws, W.device)
+    ws = _ws(gptq_quantize_workspace_size(d_out, d_in, cfg), ws, W.device, stream)
     _check(lib().gptq_quantize_layer(_ptr(W), _DTYPE[W.dtype], d_out, d_in, _ptr(U), _ptr(perm),
                                      ctypes.byref(cfg), _ptr(codes), _ptr(scales), _ptr(zeros),
                                      _ptr(g_idx), _ptr(Q), _ptr(ws), ws.numel() * ws.element_size(),
@@ -247,7 +257,7 @@ def gptq_awq_act_sumsq(a: torch.Tensor, X: torch.Tensor, ws: Optional[torch.Tens
     _dev(a, "a"); _dev(X, "X")
     n, d_in = X.shape
     assert a.dtype == torch.float64 and a.shape == (d_in,)
-    ws = _ws(gptq_awq_sumsq_workspace_size(n, d_in), ws, X.device)
+    ws = _ws(gptq_awq_sumsq_workspace_size(n, d_in), ws, X.device, stream)
     _check(lib().gptq_awq_act_sumsq(_ptr(a), _ptr(X), _DTYPE[X.dtype], n, d_in, _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)),
            "gptq_awq_act_sumsq")
@@ -265,7 +275,7 @@ def gptq_awq_search(W: torch.Tensor, a: torch.Tensor, s_out: torch.Tensor, score
         _dev(t, n)
     d_out, d_in = W.shape
     g = (ctypes.c_float * len(grid))(*[float(v) for v in grid])
-    ws = _ws(gptq_awq_search_workspace_size(d_out, d_in, group_size), ws, W.device)
+    ws = _ws(gptq_awq_search_workspace_size(d_out, d_in, group_size), ws, W.device, stream)
     _check(lib().gptq_awq_search(_ptr(W), _DTYPE[W.dtype], d_out, d_in, _ptr(a), bits, group_size,
                                  float(top_frac), g, len(grid), _ptr(s_out), _ptr(scores), _ptr(best),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
@@ -303,7 +313,7 @@ def gptq_linear(X: torch.Tensor, W: torch.Tensor, Y: torch.Tensor, R: Optional[t
     d_out = W.shape[0]
     assert W.shape == (d_out, d_in) and Y.shape == (n, d_out)
     assert X.dtype == W.dtype == Y.dtype == torch.float32
-    ws = _ws(gptq_linear_workspace_size(d_out, d_in), ws, X.device)
+    ws = _ws(gptq_linear_workspace_size(d_out, d_in), ws, X.device, stream)
     _check(lib().gptq_linear(_ptr(X), n, d_in, _ptr(W), d_out, _ptr(R), _ptr(Y), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "gptq_linear")
 
@@ -318,7 +328,7 @@ def gptq_block_attention(x1: torch.Tensor, Wq: torch.Tensor, Wk: torch.Tensor, W
     for t, n in ((x1, "x1"), (Wq, "Wq"), (Wk, "Wk"), (Wv, "Wv"), (out, "out")):
         _dev(t, n)
     T, d = x1.shape
-    ws = _ws(gptq_block_attention_workspace_size(T, d, n_heads, seq_len), ws, x1.device)
+    ws = _ws(gptq_block_attention_workspace_size(T, d, n_heads, seq_len), ws, x1.device, stream)
     _check(lib().gptq_block_attention(_ptr(x1), T, d, n_heads, seq_len, _ptr(Wq), _ptr(Wk), _ptr(Wv),
                                       float(rope_base), _ptr(out), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)),
@@ -339,7 +349,7 @@ def gptq_layer_error(H: torch.Tensor, W: torch.Tensor, Q: torch.Tensor,
                      ws: Optional[torch.Tensor] = None, stream=None) -> float:
     _dev(H, "H"); _dev(W, "W"); _dev(Q, "Q")
     d_out, d_in = W.shape
-    ws = _ws(gptq_layer_error_workspace_size(d_out, d_in), ws, W.device)
+    ws = _ws(gptq_layer_error_workspace_size(d_out, d_in), ws, W.device, stream)
     out = ctypes.c_double(0.0)
     _check(lib().gptq_layer_error(_ptr(H), _ptr(W), _DTYPE[W.dtype], _ptr(Q), d_out, d_in,
                                   ctypes.byref(out), _ptr(ws), ws.numel() * ws.element_size(),

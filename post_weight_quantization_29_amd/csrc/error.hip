@@ -96,4 +96,4 @@ extern "C" const char* gptq_status_string(int status) {
   }
 }
 
-extern "C" int gptq_abi_version(void) { return 1; }
+extern "C" int gptq_abi_version(void) { return 2; }

@@ -686,7 +686,7 @@ extern "C" int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, g
   if (!H || d_in <= 0 || d_in > 65536 || (d_in % 8) != 0 || n_tokens < 0) return GPTQ_ERR_INVALID_ARG;
   if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_F16 && x_dtype != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
   if (n_tokens == 0) return GPTQ_OK;
-  if (!X) return GPTQ_ERR_INVALID_ARG;
+  if (!X || (reinterpret_cast<uintptr_t>(X) & 15)) return GPTQ_ERR_INVALID_ARG;
   const bool f32 = (x_dtype == GPTQ_F32);
   SyrkPlan p = syrk_plan(n_tokens, d_in, f32);
   if (!ws || ws_bytes < p.ws || ws_bytes < gptq_hessian_workspace_size(n_tokens, d_in))

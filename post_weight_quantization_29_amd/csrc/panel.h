@@ -24,10 +24,6 @@ template <int CTRL, int BANKS>
 GPTQ_DEV int dpp_upd(int old, int src) {
   return __builtin_amdgcn_update_dpp(old, src, CTRL, 0xF, BANKS, false);
 }
-template <int CTRL>
-GPTQ_DEV float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
 
 // every lane of a 16-lane row reads lane P of that row: broadcast inside the
 // quads, then copy bank P/4 to the opposite bank (rotate by 8) and those two
@@ -49,35 +45,46 @@ GPTQ_DEV double row_bcast16d(double v) {
   const uint32_t hi = __builtin_bit_cast(uint32_t, row_bcast16<P>(__builtin_bit_cast(float, (uint32_t)(b >> 32))));
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
-GPTQ_DEV float row_min16(float v) {
-  v = fminf(v, dpp_f<0xB1>(v));
-  v = fminf(v, dpp_f<0x4E>(v));
-  v = fminf(v, dpp_f<0x124>(v));
-  v = fminf(v, dpp_f<0x128>(v));
+// the same DPP pattern applied to both halves of a double
+template <int CTRL>
+GPTQ_DEV double dpp_d(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// min / max over the 16 lanes of a row (butterfly: swap pairs, swap halves of
+// quads, then rotate the row by 4 and by 8)
+GPTQ_DEV double row_min16d(double v) {
+  v = fmin(v, dpp_d<0xB1>(v));
+  v = fmin(v, dpp_d<0x4E>(v));
+  v = fmin(v, dpp_d<0x124>(v));
+  v = fmin(v, dpp_d<0x128>(v));
   return v;
 }
-GPTQ_DEV float row_max16(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x124>(v));
-  v = fmaxf(v, dpp_f<0x128>(v));
+GPTQ_DEV double row_max16d(double v) {
+  v = fmax(v, dpp_d<0xB1>(v));
+  v = fmax(v, dpp_d<0x4E>(v));
+  v = fmax(v, dpp_d<0x124>(v));
+  v = fmax(v, dpp_d<0x128>(v));
   return v;
 }
 
-// min-max grid of one group: scale = (max - min)/maxq, zero = rint(-min/scale);
-// a constant group a uses the range [min(a,0), max(a,0)]; all-zero -> (1, 0).
-GPTQ_DEV void grid_params(float xmin, float xmax, float maxq, float& scale, float& zero) {
+// min-max grid of one group, in fp64 with IEEE division: scale =
+// (max - min)/maxq, zero = rint(-min/scale); a constant group a uses the range
+// [min(a,0), max(a,0)]; all-zero -> (1, 0).
+GPTQ_DEV void grid_params(double xmin, double xmax, double maxq, double& scale, double& zero) {
   if (xmax == xmin) {
-    xmin = fminf(xmin, 0.0f);
-    xmax = fmaxf(xmax, 0.0f);
+    xmin = fmin(xmin, 0.0);
+    xmax = fmax(xmax, 0.0);
   }
   if (xmax == xmin) {
-    scale = 1.0f;
-    zero = 0.0f;
+    scale = 1.0;
+    zero = 0.0;
     return;
   }
   scale = (xmax - xmin) / maxq;
-  zero = rintf(-xmin / scale);
+  zero = rint(-xmin / scale);
 }
 
 // ---------------------------------------------------------------- panel
@@ -90,6 +97,7 @@ struct PanelArgs {
   float* scales;        // [d_out x ng]
   int* zeros;
   float* ErrT;          // [128 x d_out]
+  double* gscale;       // [d_out] fp64 scale of the group in progress (groups wider than the block)
   int d_out, d, b0, bw, G, ng;
   int sym;
   float maxq;
@@ -171,13 +179,15 @@ GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4 (*sU4)[kQS / 4][kQL]
     w[t] = (double)v;
   }
 
-  float scale = 1.0f, zero = 0.0f, rscale = 1.0f;
+  // the grid and every integer decision are taken in fp64, like the rest of
+  // the column loop
+  double scale = 1.0, zero = 0.0, rscale = 1.0;
   if (GT == 0 && a.b0 % a.G != 0) {
     // a group wider than the block started in an earlier block: continue with
-    // the parameters that launch stored
-    scale = a.scales[(size_t)rowc * a.ng + a.b0 / a.G];
-    zero = (float)a.zeros[(size_t)rowc * a.ng + a.b0 / a.G];
-    rscale = 1.0f / scale;
+    // the parameters that launch kept (the fp64 scale, the integer zero point)
+    scale = a.gscale[rowc];
+    zero = (double)a.zeros[(size_t)rowc * a.ng + a.b0 / a.G];
+    rscale = 1.0 / scale;
   }
   // results of the lane's own columns, stored once at the end
   float eown[kQS], qown[kQS];
@@ -187,22 +197,22 @@ GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4 (*sU4)[kQS / 4][kQL]
 
   auto group_start = [&]<int J>() {
     constexpr int I = J / kQL;
-    float mn = INFINITY, mx = -INFINITY;
+    double mn = INFINITY, mx = -INFINITY;
     if constexpr (GT >= kQL) {
       // slots I .. I + GT/16 - 1 hold the group's columns J .. J + GT - 1
 #pragma unroll
       for (int t = I; t < I + GT / kQL; ++t) {
         if (kQL * t + q < bw) {
-          mn = fminf(mn, (float)w[t]);
-          mx = fmaxf(mx, (float)w[t]);
+          mn = fmin(mn, w[t]);
+          mx = fmax(mx, w[t]);
         }
       }
     } else if constexpr (GT > 0) {
       // a group inside one slot: lanes J%16 .. J%16 + GT - 1
       constexpr int L0 = J % kQL;
       if (q >= L0 && q < L0 + GT && J + (q - L0) < bw) {
-        mn = (float)w[I];
-        mx = (float)w[I];
+        mn = w[I];
+        mx = w[I];
       }
     } else {
       // J == 0: the whole block (columns < bw), then the rest of the group
@@ -210,33 +220,34 @@ GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4 (*sU4)[kQS / 4][kQL]
 #pragma unroll
       for (int t = 0; t < kQS; ++t) {
         if (kQL * t + q < bw) {
-          mn = fminf(mn, (float)w[t]);
-          mx = fmaxf(mx, (float)w[t]);
+          mn = fmin(mn, w[t]);
+          mx = fmax(mx, w[t]);
         }
       }
       const int gend = min(a.b0 + a.G, a.d);
       const float* wr = a.Wp + (size_t)rowc * a.d;
       for (int cg = a.b0 + bw + q; cg < gend; cg += kQL) {
-        const float v = wr[cg];
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+        const double v = (double)wr[cg];
+        mn = fmin(mn, v);
+        mx = fmax(mx, v);
       }
     }
-    mn = row_min16(mn);
-    mx = row_max16(mx);
+    mn = row_min16d(mn);
+    mx = row_max16d(mx);
     if (a.sym) {
       // symmetric: [-m, m], the middle code is zero
-      const float m = fmaxf(fabsf(mn), fabsf(mx));
-      scale = (m == 0.0f) ? 1.0f : (m + m) / a.maxq;
-      zero = 0.5f * (a.maxq + 1.0f);
+      const double m = fmax(fabs(mn), fabs(mx));
+      scale = (m == 0.0) ? 1.0 : (m + m) / (double)a.maxq;
+      zero = 0.5 * ((double)a.maxq + 1.0);
     } else {
-      grid_params(mn, mx, a.maxq, scale, zero);
+      grid_params(mn, mx, (double)a.maxq, scale, zero);
     }
-    rscale = 1.0f / scale;
+    rscale = 1.0 / scale;
     const int gi = (GT > 0) ? (a.b0 + J) / GT : a.b0 / a.G;
     if (rv && q == 0) {
-      a.scales[(size_t)row * a.ng + gi] = scale;
+      a.scales[(size_t)row * a.ng + gi] = (float)scale;
       a.zeros[(size_t)row * a.ng + gi] = (int)zero;
+      if constexpr (GT == 0) a.gscale[row] = scale;
     }
   };
 
@@ -251,14 +262,14 @@ GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4 (*sU4)[kQS / 4][kQL]
       }
     }
     const double wj = row_bcast16d<P>(w[I]);
-    // the code is decided in fp32: correctly rounded fp32(wj)/scale from the
-    // reciprocal (one residual correction)
-    const float wf = (float)wj;
-    const float t0 = wf * rscale;
-    const float res = fmaf(-t0, scale, wf);
-    const float tq = fmaf(res, rscale, t0);
-    const float c = fminf(fmaxf(rintf(tq) + zero, 0.0f), a.maxq);
-    const double qv = (double)scale * (double)(c - zero);    // exact
+    // code = clamp(rint(wj/scale) + zero, 0, maxq) with the quotient formed from
+    // the reciprocal plus one residual correction (the correctly rounded
+    // quotient for every divisor whose significand is not all ones)
+    const double t0 = wj * rscale;
+    const double res = fma(-t0, scale, wj);
+    const double tq = fma(res, rscale, t0);
+    const double c = fmin(fmax(rint(tq) + zero, 0.0), (double)a.maxq);
+    const double qv = scale * (c - zero);
     const double e = (wj - qv) * sInv[J];
     if (q == P) {
       eown[I] = (float)e;

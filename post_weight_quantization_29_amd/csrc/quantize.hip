@@ -17,11 +17,8 @@
 //                   and kept in ErrT.
 //   trailing GEMM:  W[:, b1:] -= Err * U[b0:b1, b1:] (fp32 MFMA).
 #include "gemm_f32.h"
-#include "lookahead.h"
 #include "panel.h"
 
-#include <cstdlib>
-#include <cstring>
 #include <utility>
 
 namespace gptq {
@@ -98,7 +95,7 @@ __global__ __launch_bounds__(256) void pack_dense_kernel(const uint8_t* __restri
 
 // ---------------------------------------------------------------- planning
 struct QuantLayout {
-  size_t off_wp, off_err, total;
+  size_t off_wp, off_err, off_gscale, total;
 };
 
 static QuantLayout quant_layout(int d_out, int d) {
@@ -106,8 +103,10 @@ static QuantLayout quant_layout(int d_out, int d) {
   size_t off = 0;
   L.off_wp = off;
   off = align_up(off + (size_t)d_out * d * sizeof(float));
-  L.off_err = off;   // two buffers: panel b+1 writes one while block b's update reads the other
+  L.off_err = off;   // two buffers: block b+1's column loop writes one while block b's update reads the other
   off = align_up(off + 2 * (size_t)kQB * d_out * sizeof(float));
+  L.off_gscale = off;   // fp64 scale of each row's group in progress (groups wider than the block)
+  off = align_up(off + (size_t)d_out * sizeof(double));
   L.total = off;
   return L;
 }
@@ -117,6 +116,7 @@ static int check_config(const gptq_config* c, int d) {
   if (c->bits < 2 || c->bits > 8) return GPTQ_ERR_INVALID_ARG;
   if (c->desc_act != 0 && c->desc_act != 1) return GPTQ_ERR_INVALID_ARG;
   if (c->block_size <= 0 || c->sym < 0 || c->sym > 1) return GPTQ_ERR_INVALID_ARG;
+  if (c->per_block_steps != 0 && c->per_block_steps != 1) return GPTQ_ERR_INVALID_ARG;
   const int G = c->group_size;
   if (G != -1 && G <= 0) return GPTQ_ERR_INVALID_ARG;
   if (c->block_size != kQB) return GPTQ_ERR_UNSUPPORTED;
@@ -158,6 +158,7 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   char* base = static_cast<char*>(ws);
   float* Wp = reinterpret_cast<float*>(base + L.off_wp);
   float* ErrT = reinterpret_cast<float*>(base + L.off_err);
+  double* gscale = reinterpret_cast<double*>(base + L.off_gscale);
   const int d = d_in;
   const int G = (cfg->group_size == -1) ? d : cfg->group_size;
   const int ng = (d + G - 1) / G;
@@ -168,7 +169,7 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
 
   PanelArgs pa;
   pa.Wp = Wp; pa.U = U; pa.perm = perm; pa.codes = codes; pa.Q = Q;
-  pa.scales = scales; pa.zeros = zeros; pa.ErrT = ErrT;
+  pa.scales = scales; pa.zeros = zeros; pa.ErrT = ErrT; pa.gscale = gscale;
   pa.d_out = d_out; pa.d = d; pa.G = G; pa.ng = ng;
   pa.maxq = (float)((1 << cfg->bits) - 1);
   pa.sym = cfg->sym;
@@ -180,10 +181,9 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   // take): block 0's column loop, then one launch per later block holding its
   // column loop (which first applies the previous block's update to its own
   // rows) beside the previous block's trailing update of the columns after
-  // it.  Same operations, same results as the per-block launches below.
-  const char* fused_env = std::getenv("GPTQ_FUSED_STEP");
-  const bool fused_on = !(fused_env && std::strcmp(fused_env, "0") == 0);
-  if (fused_on && quant_step_applies(d_out, d, U, gt)) {
+  // it.  Same operations, same results as the per-block launches below
+  // (cfg->per_block_steps = 1 selects those).
+  if (!cfg->per_block_steps && quant_step_applies(d_out, d, U, gt)) {
     pa.b0 = 0;
     pa.bw = std::min(kQB, d);
     pa.ErrT = ErrT;
@@ -214,31 +214,13 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
     }
     return GPTQ_OK;
   }
-  // Lookahead: block b's update of the next block's columns runs on the
-  // caller's stream, the rest of the trailing columns on the side stream, so
-  // panel b+1 overlaps it.  Panels alternate between two ErrT buffers; an
-  // update of columns c waits for the side stream's previous update, which
-  // also wrote columns c.  Each element gets the same tile, contraction and
-  // order of updates as with one stream.  Each cross-stream wait costs a few
-  // microseconds, so only layers of 2^25 weights or more (where the trailing
-  // updates are long) take this path: measured 3-8 % faster there, 11 %
-  // slower at 4096 x 4096.
-  Lookahead* la = ((int64_t)d_out * d >= (int64_t(1) << 25)) ? lookahead_for_current_device() : nullptr;
-  std::unique_lock<std::mutex> lk;
-  if (la) lk = std::unique_lock<std::mutex>(la->mu);
-  bool side_pending = false;
-  for (int b0 = 0, blk = 0; b0 < d; b0 += kQB, ++blk) {
+  // One launch per step: block b's column loop, then its lazy update of every
+  // later column, W[:, b1:] -= Err * U[b0:b1, b1:] with Aop(m, k) = ErrT[k][m].
+  for (int b0 = 0; b0 < d; b0 += kQB) {
     const int bw = std::min(kQB, d - b0);
-    float* Eb = ErrT + (size_t)(blk & 1) * kQB * d_out;
     pa.b0 = b0;
     pa.bw = bw;
-    pa.ErrT = Eb;
-    // a group wider than the block takes its grid at its first column from
-    // every column of the group, so its panel waits for the side stream too
-    if (side_pending && gt == 0 && b0 % G == 0 && b0 + bw < d) {
-      GPTQ_HIP_TRY(hipStreamWaitEvent(s, la->trail_done, 0));
-      side_pending = false;
-    }
+    pa.ErrT = ErrT;
     switch (gt) {
       case 4: panel_kernel<4><<<nrow_blocks, 256, 0, s>>>(pa); break;
       case 8: panel_kernel<8><<<nrow_blocks, 256, 0, s>>>(pa); break;
@@ -250,30 +232,11 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
     }
     GPTQ_LAUNCH_CHECK();
     const int b1 = b0 + bw;
-    if (b1 >= d) continue;
-    const int rest = d - b1;
-    // W[:, b1:] -= Err * U[b0:b1, b1:]  with Aop(m, k) = ErrT[k][m]
-    if (!la || rest <= kQB) {
-      if (side_pending) GPTQ_HIP_TRY(hipStreamWaitEvent(s, la->trail_done, 0));
-      side_pending = false;
-      gemm_f32<true>(Eb, d_out, U + (size_t)b0 * d + b1, d, Wp + b1, d, d_out, rest, bw, -1.0f, 1.0f,
-                     0, 0, 0, s);
-      GPTQ_LAUNCH_CHECK();
-      continue;
-    }
-    GPTQ_HIP_TRY(hipEventRecord(la->panel_done, s));
-    if (side_pending) GPTQ_HIP_TRY(hipStreamWaitEvent(s, la->trail_done, 0));
-    gemm_f32<true>(Eb, d_out, U + (size_t)b0 * d + b1, d, Wp + b1, d, d_out, kQB, bw, -1.0f, 1.0f, 0,
-                   0, 0, s);
+    if (b1 >= d) break;
+    gemm_f32<true>(ErrT, d_out, U + (size_t)b0 * d + b1, d, Wp + b1, d, d_out, d - b1, bw, -1.0f, 1.0f,
+                   0, 0, 0, s);
     GPTQ_LAUNCH_CHECK();
-    GPTQ_HIP_TRY(hipStreamWaitEvent(la->side, la->panel_done, 0));
-    gemm_f32<true>(Eb, d_out, U + (size_t)b0 * d + b1 + kQB, d, Wp + b1 + kQB, d, d_out, rest - kQB, bw,
-                   -1.0f, 1.0f, 0, 0, 0, la->side);
-    GPTQ_LAUNCH_CHECK();
-    GPTQ_HIP_TRY(hipEventRecord(la->trail_done, la->side));
-    side_pending = true;
   }
-  if (side_pending) GPTQ_HIP_TRY(hipStreamWaitEvent(s, la->trail_done, 0));
   return GPTQ_OK;
 }
 
