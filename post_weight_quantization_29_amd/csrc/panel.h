@@ -316,18 +316,19 @@ __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
 
 // ---------------------------------------------------------------- fused block step
 // One launch per block b >= 0 (b + 1 < blocks): the column loop of block b + 1,
-// whose workgroups first apply block b's update to their own 16 rows of block
-// b + 1's columns (the products kept in LDS, never stored), beside the
-// trailing update of the columns after block b + 1.  The two parts share no
-// data, so they run side by side without waiting on each other.
+// whose workgroups first apply the update block b + 1 still owes (block b's,
+// or at a super-block's end the whole super-block's) to their own 16 rows of
+// its columns (the products kept in LDS, never stored), beside the trailing
+// update of later columns by the same Err rows.  The two parts share no data,
+// so they run side by side without waiting on each other.
 struct StepArgs {
   PanelArgs pa;          // column loop of block b + 1 (pa.b0, pa.bw, pa.ErrT: its Err buffer)
-  const float* Eprev;    // Err of block b, [kQB x d_out]
-  const float* Uprev;    // U rows of block b from block b + 1's first column (row pitch d)
-  float* Wrest;          // work copy from the column after block b + 1 (row pitch d)
-  const float* Urest;    // U rows of block b from that column (row pitch d)
-  int rest;              // columns after block b + 1
-  int kprev;             // width of block b (the contraction length, kQB)
+  const float* Eprev;    // Err rows owed, [kprev x d_out]
+  const float* Uprev;    // the matching U rows from block b + 1's first column (row pitch d)
+  float* Wrest;          // work copy from the first column of the trailing update (row pitch d)
+  const float* Urest;    // the same U rows from that column (row pitch d)
+  int rest;              // columns of the trailing update
+  int kprev;             // the contraction length (a multiple of kQB)
 };
 
 // Whether the fused steps apply: groups of gt columns inside the block (gt > 0),

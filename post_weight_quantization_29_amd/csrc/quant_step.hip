@@ -2,17 +2,25 @@
 // section 2.2 "second": a block of columns is quantized, then everything after
 // it is updated with one matrix product).
 //
-// The per-block order is: column loop of block b, then W[:, after b] -= Err_b *
-// U[b, after b], then the column loop of block b + 1.  Block b + 1's loop only
-// needs block b's update of its own columns, and each row needs only its own
-// part of it, so one launch holds two kinds of workgroups:
-//   * column-loop workgroups (16 rows each): the 16 x 128 product
-//     Err_b[rows] * U[b, b+1] with v_mfma_f32_32x32x2f32 (rows 16..31 of the
+// Blocks are grouped into super-blocks of gb consecutive blocks.  The
+// per-block order is: column loop of block b, then its lazy update of the
+// later columns of its super-block, W[:, b+1 .. end of S] -= Err_b U[b, ...];
+// at the super-block's end, one update of every column after it by the whole
+// super-block, W[:, after S] -= Err_S U[S, after S] (K = 128 gb).  Deferring
+// the far columns' updates to one product of K = 128 gb is exact in exact
+// arithmetic (the sums are only regrouped) and reads and writes the work copy
+// gb times less often.  Block b + 1's loop only needs the update it still
+// owes (block b's, or at a super-block's end the whole super-block's) for its
+// own columns, and each row needs only its own part of it, so one launch
+// holds two kinds of workgroups:
+//   * column-loop workgroups (16 rows each): the 16 x 128 product of the owed
+//     Err rows and U rows with v_mfma_f32_32x32x2f32 (rows 16..31 of the
 //     32-row operand are zero), the same MFMA steps in the same k order as the
 //     trailing GEMM's tile, kept in LDS; then the column loop of block b + 1
 //     starting from the work copy minus that product;
-//   * trailing-GEMM workgroups: W[:, after b + 1] -= Err_b * U[b, after b + 1],
-//     128 x 128 tiles.
+//   * trailing-GEMM workgroups: the same Err rows' update of the columns after
+//     block b + 1 (to the super-block's end, or to the last column), 128 x 128
+//     tiles.
 // Neither reads what the other writes, so there are no waits between them, and
 // every value equals what the per-block launches compute.
 #include "gemm_f32.h"
@@ -30,54 +38,60 @@ static_assert((size_t)kQB * kQRows * 4 <= (size_t)kQRows * kPreP * 4, "Err rows 
 static_assert(kStepLds >= 2 * (size_t)kGK * kGP * 4, "the GEMM tile's staging fits");
 static_assert(2 * kStepLds <= 160 * 1024, "two workgroups per CU");
 
-// products P[r][c] = sum_k Err_b[k][row0 + r] * U[b0 + k][b1 + c], r < 16, c < 128
+// products P[r][c] = sum_k Eprev[k][row0 + r] * Uprev[k][c], r < 16, c < 128,
+// k < kprev (128 per block whose update is still owed), in chunks of 128 k
+// staged through LDS; the k order is the trailing GEMM tile's
 GPTQ_DEV void step_products(const StepArgs& f, int row0, char* lds) {
   const PanelArgs& a = f.pa;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* sE = reinterpret_cast<float*>(lds + kStepE);      // [k][16]
   float* sUb = reinterpret_cast<float*>(lds);              // [k][kQB]
-  // Err rows: k = tid/16 + 16u, row row0 + tid%16 (16 consecutive floats per k)
-  {
-    const int i = tid & 15, r = row0 + i;
-    float e[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = (tid >> 4) + 16 * u;
-      e[u] = (r < a.d_out) ? f.Eprev[(size_t)k * a.d_out + r] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) sE[((tid >> 4) + 16 * u) * kQRows + i] = e[u];
-  }
-  // U tile: rows k of block b, columns c < bw of block b + 1 (zero beyond)
-  {
-    float4 v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = u * 256 + tid, k = e >> 5, c = 4 * (e & 31);
-      v[u] = (c + 3 < a.bw) ? *reinterpret_cast<const float4*>(f.Uprev + (size_t)k * a.d + c)
-                            : make_float4(c + 0 < a.bw ? f.Uprev[(size_t)k * a.d + c + 0] : 0.0f,
-                                          c + 1 < a.bw ? f.Uprev[(size_t)k * a.d + c + 1] : 0.0f,
-                                          c + 2 < a.bw ? f.Uprev[(size_t)k * a.d + c + 2] : 0.0f, 0.0f);
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = u * 256 + tid;
-      reinterpret_cast<float4*>(sUb)[e] = v[u];
-    }
-  }
-  __syncthreads();
-  // wave w: rows 0..31 (16..31 zero) x columns 32w .. 32w+31, k in pairs
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
   const int m = lane & 31, kh = lane >> 5;
+  for (int kc = 0; kc < f.kprev; kc += kQB) {
+    const float* E = f.Eprev + (size_t)kc * a.d_out;
+    const float* Ub = f.Uprev + (size_t)kc * a.d;
+    // Err rows: k = tid/16 + 16u, row row0 + tid%16 (16 consecutive floats per k)
+    {
+      const int i = tid & 15, r = row0 + i;
+      float e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = (tid >> 4) + 16 * u;
+        e[u] = (r < a.d_out) ? E[(size_t)k * a.d_out + r] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sE[((tid >> 4) + 16 * u) * kQRows + i] = e[u];
+    }
+    // U tile: rows kc + k of the owed blocks, columns c < bw of this block (zero beyond)
+    {
+      float4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = u * 256 + tid, k = e >> 5, c = 4 * (e & 31);
+        v[u] = (c + 3 < a.bw) ? *reinterpret_cast<const float4*>(Ub + (size_t)k * a.d + c)
+                              : make_float4(c + 0 < a.bw ? Ub[(size_t)k * a.d + c + 0] : 0.0f,
+                                            c + 1 < a.bw ? Ub[(size_t)k * a.d + c + 1] : 0.0f,
+                                            c + 2 < a.bw ? Ub[(size_t)k * a.d + c + 2] : 0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = u * 256 + tid;
+        reinterpret_cast<float4*>(sUb)[e] = v[u];
+      }
+    }
+    __syncthreads();
+    // wave w: rows 0..31 (16..31 zero) x columns 32w .. 32w+31, k in pairs
 #pragma unroll 8
-  for (int k2 = 0; k2 < kQB; k2 += 2) {
-    const float av = (m < kQRows) ? sE[(k2 + kh) * kQRows + m] : 0.0f;
-    const float bv = sUb[(k2 + kh) * kQB + 32 * wave + m];
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    for (int k2 = 0; k2 < kQB; k2 += 2) {
+      const float av = (m < kQRows) ? sE[(k2 + kh) * kQRows + m] : 0.0f;
+      const float bv = sUb[(k2 + kh) * kQB + 32 * wave + m];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+    __syncthreads();                                       // sE and sUb are read
   }
-  __syncthreads();                                         // sE and sUb are read
   float* sPre = reinterpret_cast<float*>(lds + kStepE);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -99,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void quant_step_kernel(StepArgs f) {
                          reinterpret_cast<const float*>(lds + kStepE));
     return;
   }
-  // trailing tile: rows 128*(t / tn), columns 128*(t % tn) of the columns after block b + 1
+  // trailing tile: rows 128*(t / tn), columns 128*(t % tn) of the update's columns
   const GemmProblem P{f.Eprev, f.Urest, f.Wrest, nullptr, f.pa.d_out, f.pa.d, f.pa.d, f.pa.d_out, f.rest, f.kprev};
   int m0, n0;
   tile_origin(P, wg - npanel, 0, m0, n0);

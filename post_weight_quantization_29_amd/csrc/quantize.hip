@@ -98,13 +98,28 @@ struct QuantLayout {
   size_t off_wp, off_err, off_gscale, total;
 };
 
-static QuantLayout quant_layout(int d_out, int d) {
+// Blocks per super-block (the lazy updates of the columns after a super-block
+// are one product of K = 128 * gb).  Layers whose fp32 work copy exceeds the
+// 256 MB last-level cache take 4: their per-block updates are bound by the
+// copy's read-modify-write from HBM.  Groups wider than the block read the
+// rest of the group from the work copy at its first column, so they keep 1.
+constexpr size_t kSuperMinBytes = size_t(256) << 20;
+static int super_blocks(int d_out, int d, int gt) {
+  if (gt == 0) return 1;
+  return ((size_t)d_out * d * sizeof(float) > kSuperMinBytes) ? 4 : 1;
+}
+
+static int in_block_group(int G) { return (G <= kQB && kQB % G == 0 && G % 4 == 0) ? G : 0; }
+
+static QuantLayout quant_layout(int d_out, int d, int gb) {
   QuantLayout L;
   size_t off = 0;
   L.off_wp = off;
   off = align_up(off + (size_t)d_out * d * sizeof(float));
-  L.off_err = off;   // two buffers: block b+1's column loop writes one while block b's update reads the other
-  off = align_up(off + 2 * (size_t)kQB * d_out * sizeof(float));
+  // Err rows of two super-blocks: the next block's column loop writes one
+  // while the current super-block's update reads the other
+  L.off_err = off;
+  off = align_up(off + 2 * (size_t)gb * kQB * d_out * sizeof(float));
   L.off_gscale = off;   // fp64 scale of each row's group in progress (groups wider than the block)
   off = align_up(off + (size_t)d_out * sizeof(double));
   L.total = off;
@@ -138,10 +153,15 @@ static int check_config(const gptq_config* c, int d) {
 
 using namespace gptq;
 
+static int config_super_blocks(int d_out, int d, const gptq_config* cfg) {
+  if (!cfg) return 4;   // the largest layout
+  const int G = (cfg->group_size == -1) ? d : cfg->group_size;
+  return super_blocks(d_out, d, G > 0 ? in_block_group(G) : 0);
+}
+
 extern "C" size_t gptq_quantize_workspace_size(int32_t d_out, int32_t d_in, const gptq_config* cfg) {
-  (void)cfg;
   if (d_out <= 0 || d_in <= 0) return 0;
-  return quant_layout(d_out, d_in).total;
+  return quant_layout(d_out, d_in, config_super_blocks(d_out, d_in, cfg)).total;
 }
 
 extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in,
@@ -153,15 +173,18 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   if (w_dtype != GPTQ_F32 && w_dtype != GPTQ_F16 && w_dtype != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
   const int st = check_config(cfg, d_in);
   if (st != GPTQ_OK) return st;
-  const QuantLayout L = quant_layout(d_out, d_in);
+  const int d = d_in;
+  const int G = (cfg->group_size == -1) ? d : cfg->group_size;
+  const int ng = (d + G - 1) / G;
+  // in-block group sizes are compile-time; wider groups (or one per row) use 0
+  const int gt = in_block_group(G);
+  const int gb = super_blocks(d_out, d, gt);
+  const QuantLayout L = quant_layout(d_out, d_in, gb);
   if (!ws || ws_bytes < L.total) return GPTQ_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
   float* Wp = reinterpret_cast<float*>(base + L.off_wp);
   float* ErrT = reinterpret_cast<float*>(base + L.off_err);
   double* gscale = reinterpret_cast<double*>(base + L.off_gscale);
-  const int d = d_in;
-  const int G = (cfg->group_size == -1) ? d : cfg->group_size;
-  const int ng = (d + G - 1) / G;
 
   gather_w_kernel<<<dim3((d + 255) / 256, std::min(d_out, 1024)), 256, 0, s>>>(W, w_dtype, d_out, d,
                                                                               perm, G, Wp, g_idx);
@@ -174,8 +197,11 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   pa.maxq = (float)((1 << cfg->bits) - 1);
   pa.sym = cfg->sym;
   const int nrow_blocks = (d_out + kQRows - 1) / kQRows;
-  // in-block group sizes are compile-time; wider groups (or one per row) use 0
-  const int gt = (G <= kQB && kQB % G == 0 && G % 4 == 0) ? G : 0;
+  const int nb = (d + kQB - 1) / kQB;
+  // Err rows of block b: super-block b / gb's buffer, slot b % gb
+  auto err_of = [&](int b) { return ErrT + ((size_t)((b / gb) & 1) * gb + b % gb) * kQB * d_out; };
+  // first column after block b's super-block
+  auto super_end = [&](int b) { return std::min(d, (b / gb + 1) * gb * kQB); };
 
   // Fused block steps (groups inside the block, operands the 16-byte loads
   // take): block 0's column loop, then one launch per later block holding its
@@ -186,7 +212,7 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   if (!cfg->per_block_steps && quant_step_applies(d_out, d, U, gt)) {
     pa.b0 = 0;
     pa.bw = std::min(kQB, d);
-    pa.ErrT = ErrT;
+    pa.ErrT = err_of(0);
     switch (gt) {
       case 4: panel_kernel<4><<<nrow_blocks, 256, 0, s>>>(pa); break;
       case 8: panel_kernel<8><<<nrow_blocks, 256, 0, s>>>(pa); break;
@@ -196,31 +222,37 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
       default: panel_kernel<128><<<nrow_blocks, 256, 0, s>>>(pa); break;
     }
     GPTQ_LAUNCH_CHECK();
-    for (int b0 = 0, blk = 0; b0 + kQB < d; b0 += kQB, ++blk) {
-      const int b1 = b0 + kQB, bw1 = std::min(kQB, d - b1);
+    for (int b = 0; b + 1 < nb; ++b) {
+      const int b0 = b * kQB, b1 = b0 + kQB, bw1 = std::min(kQB, d - b1);
+      // the Err rows block b + 1 still owes: block b's inside a super-block,
+      // the whole super-block's at its end (then every later column takes them)
+      const bool s_end = (b + 1) % gb == 0;
+      const int k0 = s_end ? (b / gb) * gb * kQB : b0;
       StepArgs st;
       st.pa = pa;
       st.pa.b0 = b1;
       st.pa.bw = bw1;
-      st.pa.ErrT = ErrT + (size_t)((blk + 1) & 1) * kQB * d_out;
-      st.Eprev = ErrT + (size_t)(blk & 1) * kQB * d_out;
-      st.Uprev = U + (size_t)b0 * d + b1;
+      st.pa.ErrT = err_of(b + 1);
+      st.Eprev = s_end ? err_of(b - b % gb) : err_of(b);
+      st.kprev = b1 - k0;
+      st.Uprev = U + (size_t)k0 * d + b1;
       st.Wrest = Wp + b1 + bw1;
-      st.Urest = U + (size_t)b0 * d + b1 + bw1;
-      st.rest = d - b1 - bw1;
-      st.kprev = kQB;
+      st.Urest = U + (size_t)k0 * d + b1 + bw1;
+      st.rest = std::max(0, (s_end ? d : super_end(b)) - (b1 + bw1));
       launch_quant_step(st, gt, s);
       GPTQ_LAUNCH_CHECK();
     }
     return GPTQ_OK;
   }
-  // One launch per step: block b's column loop, then its lazy update of every
-  // later column, W[:, b1:] -= Err * U[b0:b1, b1:] with Aop(m, k) = ErrT[k][m].
-  for (int b0 = 0; b0 < d; b0 += kQB) {
-    const int bw = std::min(kQB, d - b0);
+  // One launch per step: block b's column loop, then its lazy update: of the
+  // later columns of its super-block, or, at the super-block's end, the whole
+  // super-block's update of every later column; W[:, c] -= Err * U[rows, c]
+  // with Aop(m, k) = ErrT[k][m].
+  for (int b = 0; b < nb; ++b) {
+    const int b0 = b * kQB, bw = std::min(kQB, d - b0);
     pa.b0 = b0;
     pa.bw = bw;
-    pa.ErrT = ErrT;
+    pa.ErrT = err_of(b);
     switch (gt) {
       case 4: panel_kernel<4><<<nrow_blocks, 256, 0, s>>>(pa); break;
       case 8: panel_kernel<8><<<nrow_blocks, 256, 0, s>>>(pa); break;
@@ -233,8 +265,11 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
     GPTQ_LAUNCH_CHECK();
     const int b1 = b0 + bw;
     if (b1 >= d) break;
-    gemm_f32<true>(ErrT, d_out, U + (size_t)b0 * d + b1, d, Wp + b1, d, d_out, d - b1, bw, -1.0f, 1.0f,
-                   0, 0, 0, s);
+    const bool s_end = (b + 1) % gb == 0;
+    const int k0 = s_end ? (b / gb) * gb * kQB : b0;
+    const int c1 = s_end ? d : super_end(b);
+    gemm_f32<true>(s_end ? err_of(b - b % gb) : err_of(b), d_out, U + (size_t)k0 * d + b1, d, Wp + b1, d,
+                   d_out, c1 - b1, b1 - k0, -1.0f, 1.0f, 0, 0, 0, s);
     GPTQ_LAUNCH_CHECK();
   }
   return GPTQ_OK;
