@@ -347,15 +347,26 @@ GPTQ_DEV void leaf_inverse(float* Vb, float (*ring)[64], float (*rs)[4], const i
   for (int r = 0; r < 16; ++r) Vb[(16 * h + r) * kVP + i] = y[r];
 }
 
+// The part of an update that rides with the factor of row block k: factor
+// rows [k0, k0 + K) (already factored R row blocks) times themselves over the
+// columns after row block k, subtracted from rows [(k + 1)*128, + rows) and
+// every column after row block k (upper tiles only).
+struct TrailArgs {
+  int k0;     // first factor row of the contraction
+  int K;      // contraction length (128 per factored block)
+  int rows;   // rows of A updated, from row (k + 1) * 128
+};
+
 // Trailing workgroups of the factor launch for block k: workgroup `local` of
-// block k-1's update of the rows after row block k (the upper 128 x 128 tiles
-// of A[(k+1)*128:, (k+1)*128:], row by row), with the same tile contraction as
-// a separate trailing-update launch.  They run on the CUs the factor leaves
-// idle and stage their operands in its LDS arrays.
-GPTQ_DEV void trail_tile(float* A, int np, int k, int local, float* sA, float* sB) {
+// the update owed by the rows after row block k (set up by the previous
+// factor; the upper 128 x 128 tiles of A[(k+1)*128 : (k+1)*128 + t.rows,
+// (k+1)*128 :], row by row), with the same tile contraction as a separate
+// trailing-update launch.  They run on the CUs the factor leaves idle and
+// stage their operands in its LDS arrays.
+GPTQ_DEV void trail_tile(float* A, int np, int k, const TrailArgs& t, int local, float* sA, float* sB) {
   const int c0 = (k + 1) * kNB, rest = np - c0;
-  const float* Arow = A + (size_t)(k - 1) * kNB * np + c0;
-  const GemmProblem P{Arow, Arow, A + (size_t)c0 * np + c0, nullptr, np, np, np, rest, rest, kNB};
+  const float* Arow = A + (size_t)t.k0 * np + c0;
+  const GemmProblem P{Arow, Arow, A + (size_t)c0 * np + c0, nullptr, np, np, np, t.rows, rest, t.K};
   const int tn = rest / kGT;
   int r = 0, rem = local;
   while (rem >= tn - r) { rem -= tn - r; ++r; }
@@ -369,13 +380,13 @@ GPTQ_DEV void trail_tile(float* A, int np, int k, int local, float* sA, float* s
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   float cold[2][2][16];
   gemm_tile_load_c(P, m0, n0, cold);
-  gemm_tile_contract<true, true>(P, m0, n0, 0, kNB, sA, sB, acc);
+  gemm_tile_contract<true, true>(P, m0, n0, 0, t.K, sA, sB, acc);
   gemm_tile_store(P, m0, n0, -1.0f, 1.0f, acc, cold);
 }
 
 __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A, int np, int k,
                                                          float* __restrict__ Dinv, int* __restrict__ flag,
-                                                         int ntrail) {
+                                                         int ntrail, TrailArgs trail) {
   __shared__ __attribute__((aligned(16))) float M[kNB * kLP];
   __shared__ __attribute__((aligned(16))) float T[kNB * kLP];
   __shared__ __attribute__((aligned(16))) float V[4][32 * kVP];
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A, 
   __shared__ int flags[kLeafSteps];
 
   if ((int)blockIdx.x >= (int)gridDim.x - ntrail) {
-    trail_tile(A, np, k, (int)blockIdx.x - ((int)gridDim.x - ntrail), M, T);
+    trail_tile(A, np, k, trail, (int)blockIdx.x - ((int)gridDim.x - ntrail), M, T);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -555,6 +566,13 @@ static void tree_launch_shape(const std::vector<TreeNode>& nodes, size_t c0, int
   }
 }
 
+// Blocks per super-block of the factor's trailing updates: 4 once the padded
+// matrix exceeds the 256 MB last-level cache (the rank-128 updates are then
+// bound by its read-modify-write from HBM), else 1.
+static int hinv_super_blocks(int np) {
+  return ((size_t)np * np * sizeof(float) > (size_t(256) << 20)) ? 4 : 1;
+}
+
 static HinvLayout hinv_layout(int n) {
   HinvLayout L;
   L.n = n;
@@ -626,29 +644,44 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
   //    then the trailing update, split so that only its first row block sits
   //    between two factors (lookahead); R_kk^-1 goes to Dinv (in Z's space,
   //    which the triangular inverse only uses later) and then onto A's
-  //    diagonal blocks
+  //    diagonal blocks.  Blocks form super-blocks of gb: inside a super-block
+  //    a factored row block updates only the rows of the super-block's later
+  //    blocks; at its end the whole super-block's rows update every later row
+  //    in one product of K = 128 gb (the same sums regrouped; the trailing
+  //    matrix is read and written gb times less often).
+  const int gb = hinv_super_blocks(np);
   float* Dinv = Z;
-  bool ride = false;   // block k-1's update of the rows after row block k rides with factor k
+  bool ride = false;   // the previous update's rows after row block k ride with factor k
+  TrailArgs trail{0, 0, 0};
   for (int k = 0; k < nb; ++k) {
     const int rest = np - (k + 1) * kNB;
-    // block k-1's update of the row blocks after block k rides along with
-    // block k's factor (other CUs; it touches neither row block k nor Dinv) ...
-    const int ntr = (ride && rest > 0) ? gemm_upper_tiles(rest, rest) : 0;
-    chol_panel_kernel<<<1 + rest / kNB + ntr, 256, 0, s>>>(A, np, k, Dinv, flag, ntr);
+    // the previous update's rows after row block k ride along with block k's
+    // factor (other CUs; they touch neither row block k nor Dinv) ...
+    const int ntr = (ride && rest > 0 && trail.rows > 0) ? gemm_upper_tiles(trail.rows, rest) : 0;
+    chol_panel_kernel<<<1 + rest / kNB + ntr, 256, 0, s>>>(A, np, k, Dinv, flag, ntr, trail);
     GPTQ_LAUNCH_CHECK();
     if (rest <= 0) continue;
-    float* Arow = A + (size_t)k * kNB * np + (size_t)(k + 1) * kNB;   // R_k,rest
+    // the update this factor owes: factor rows [k0, (k+1)*128) subtracted
+    // from rows [(k+1)*128, row_end) and every column after row block k
+    const bool s_end = (k + 1) % gb == 0;
+    const int k0 = (s_end ? (k / gb) * gb : k) * kNB;
+    const int Kk = (k + 1) * kNB - k0;
+    const int row_end = s_end ? np : std::min(np, (k / gb + 1) * gb * kNB);
+    const int urows = row_end - (k + 1) * kNB;
+    float* Arow = A + (size_t)k0 * np + (size_t)(k + 1) * kNB;
     float* Atrail = A + (size_t)(k + 1) * kNB * np + (size_t)(k + 1) * kNB;
-    // ... and block k's update of row block k + 1 alone runs before block k+1's
-    // factor: A[k+1, k+1:] -= R_k,k+1^T R_k,rest.  Every element gets the
-    // same tile contraction as one upper-tile update of A_rest would give.
-    // Riding tiles run one workgroup per CU (the factor's LDS); when they
-    // would need more than two rounds of the CUs the next factor leaves free,
-    // the whole update runs on its own instead (two workgroups per CU).
-    const int next_tiles = gemm_upper_tiles(rest - kNB, rest - kNB);
+    // ... and the update of row block k + 1 alone runs before block k+1's
+    // factor.  Every element gets the same tile contraction as one upper-tile
+    // update of those rows would give.  Riding tiles run one workgroup per CU
+    // (the factor's LDS); when they would need more than two rounds of the CUs
+    // the next factor leaves free, the whole update runs on its own instead
+    // (two workgroups per CU).
+    const int ride_rows = urows - kNB;
+    const int next_tiles = ride_rows > 0 ? gemm_upper_tiles(ride_rows, rest - kNB) : 0;
     const int free_cus = 256 - (1 + (rest - kNB) / kNB);
     ride = next_tiles <= 2 * free_cus;
-    gemm_f32<true>(Arow, np, Arow, np, Atrail, np, ride ? kNB : rest, rest, kNB, -1.0f, 1.0f, 0, 0,
+    trail = TrailArgs{k0, Kk, ride ? std::max(0, ride_rows) : 0};
+    gemm_f32<true>(Arow, np, Arow, np, Atrail, np, ride ? kNB : urows, rest, Kk, -1.0f, 1.0f, 0, 0,
                    ride ? 0 : 1, s);
     GPTQ_LAUNCH_CHECK();
   }
