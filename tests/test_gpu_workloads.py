@@ -1,23 +1,27 @@
-"""Parity at the workloads' full layer shapes (GPU, through the C ABI).
+"""Parity at the workloads' full sizes (GPU, through the C ABI).
 
 The workloads are the five synthetic layer configurations of gptq_inputs.
 Every expected value comes from the float64 oracle run on the same input bytes:
 
 * Hessian of the q_proj workload over all 262,144 calibration tokens, in one
   call (the benchmark's launch) and streamed as eight 32,768-token calls:
-  sampled entries and the whole fp64 diagonal.
-* Every layer at its full (d_out, d_in): both sides build H from the
-  workload's first 32,768-token chunk (the GPU with the SYRK kernel, the
-  oracle in float64); H is compared entry by entry, the factor as a whole,
-  and the column loop on sampled rows (rows are independent given H), for
-  every quantizer setting of the workload.
-* The 70B down_proj (d_in = 28,672) is beyond a float64 factor in test time:
-  sampled Hessian entries and the whole diagonal, the order, the factor's
-  defining property U^T U H_d = I on sampled columns (H_d from the H the
-  factor was given), and on sampled rows the codes' range,
-  Q = scale * (code - zero), the packing, and GPTQ <= round-to-nearest.
+  sampled entries (oracle computed here) and the whole fp64 diagonal.
+* Every layer of the Llama-7B q_proj, the Llama-7B MLP, the 13B desc_act
+  layers and the 70B down_proj at its full (d_out, d_in) with H over all
+  262,144 calibration tokens, in the benchmark's launch configuration (one
+  Hessian call over every token, then prepare_hinv, quantize_layer, pack):
+  against tests/golden/workloads/<key>.npz, which
+  tests/golden/make_workload_goldens.py writes from the oracle alone (its
+  float64 Hessian of the 70B down_proj is 2.2e14 flop, too long to repeat in
+  a test).  Compared: the Hessian's diagonal and a sampled 64 x 64 block, the
+  order, the factor's diagonal and a sampled block element by element, and
+  on sampled rows (rows are independent given H) codes, scales, zero points,
+  Q, packing and the layer objective, for every quantizer setting.
 """
 from __future__ import annotations
+
+import hashlib
+import os
 
 import numpy as np
 import pytest
@@ -25,7 +29,7 @@ import pytest
 import gptq_inputs as gi
 from oracle import gptq_ref as o
 
-from gpu_helpers import compare_quant, gpu_hessian, say, to_dev
+from gpu_helpers import compare_golden, compare_quant, gpu_hessian, say, to_dev
 
 torch = pytest.importorskip("torch")
 
@@ -94,154 +98,129 @@ def test_q_proj_hessian_full_tokens():
     _check_h_sampled(H2, idx, cols64, hd2, diag_ref)
 
 
-LAYERS = [("c2_llama7b_q_proj", 0), ("c3_llama7b_mlp", 0), ("c3_llama7b_mlp", 2),
-          ("c4_13b_desc_act", 0), ("c4_13b_desc_act", 1)]
-
-# Code agreement bar.  North star: >= 99.9 %, disagreements only at rounding
-# ties.  GPTQ's error feedback makes a row's codes after its first tie flip
-# diverge (the two sides then compensate different errors), so agreement is
-# (rows with a flip) x (length of the divergence).  The kernels keep the
-# column loop's running weights in fp64 like the oracle (with the oracle's
-# own factor given to the GPU loop, no row flips at the 13B down_proj shape);
-# what remains is H's fp32 accumulation (about 1e-6 relative after 2048
-# accumulation steps), and in the oracle a 1e-6 relative perturbation of H
-# alone moves 61 % of that layer's rows.  At d_in = 13824 with 4-bit groups of
-# 64 this leaves 99.8-99.9 %; that one layer is held to 99.8 %, with every row's
-# first disagreement at a tie and the objective within 1e-3 like the others.
-AGREE = {("c4_13b_desc_act", 1): 0.998}
+GOLD_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "workloads")
+FULL = [("c2_llama7b_q_proj", 0), ("c3_llama7b_mlp", 0), ("c3_llama7b_mlp", 1),
+        ("c4_13b_desc_act", 0), ("c4_13b_desc_act", 1), ("c5_70b_down_proj", 0)]
 
 
-@pytest.mark.parametrize("key,li", LAYERS, ids=[f"{k.split('_')[0]}-{gi.workload(k).layers[i].name}"
-                                                for k, i in LAYERS])
-def test_workload_layer(key, li):
+def _gold(key):
+    path = os.path.join(GOLD_DIR, key + ".npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing {path}: run tests/golden/make_workload_goldens.py {key}")
+    return np.load(path, allow_pickle=False)
+
+
+def _sha(a):
+    return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()
+
+
+def _upload_calib(cal, config):
+    """All calibration tokens on the device, generated chunk by chunk."""
+    X = torch.empty((cal.n_tokens, cal.d_in), dtype=torch.bfloat16, device="cuda")
+    for c in range(gi.n_chunks(cal)):
+        r0 = c * gi.CHUNK_TOKENS
+        xc = gi.x_chunk(cal, config, c)
+        X[r0:r0 + xc.shape[0]].copy_(to_dev(xc, cal.dtype))
+        del xc
+    return X
+
+
+@pytest.mark.parametrize("key,ci", FULL, ids=[f"{k.split('_')[0]}-d{gi.workload(k).calib[c].d_in}"
+                                              for k, c in FULL])
+def test_workload_full_tokens(key, ci):
     import post_weight_quantization_29_amd as P
     wl = gi.workload(key)
-    layer = wl.layers[li]
-    cal = wl.calib_for(layer.d_in)
-    d, d_out = layer.d_in, layer.d_out
-    say(f"[workload] {key} {layer.name}: W {d_out}x{d}, H from {CHUNK} tokens, "
-        f"{len(wl.quant)} quantizer setting(s)")
-    x0 = gi.x_chunk(cal, wl.config, 0)
-    W = gi.weight(layer, wl.config)
-    W64 = gi.to_float64(W, layer.dtype)
-    Hg, hd = gpu_hessian([x0], cal.dtype, d, with_diag=True)
-    H64 = o.hessian([gi.to_float64(x0, cal.dtype)], d)
-    # H entry by entry (fp32 accumulation of exact products)
-    Hn = Hg.cpu().numpy().astype(np.float64)
-    dg = np.sqrt(np.diag(H64))
-    err = float((np.abs(Hn - H64) / np.outer(dg, dg)).max())
-    say(f"  H: max |dH|/sqrt(Hii Hjj) = {err:.2e}")
-    assert err <= 1e-4 and np.array_equal(Hn, Hn.T)
-    assert np.max(np.abs(hd.cpu().numpy() - np.diag(H64)) / np.diag(H64)) <= 1e-12
-    del Hn
+    cal = wl.calib[ci]
+    d = cal.d_in
+    z = _gold(key)
+    pre = f"d{d}_"
+    assert str(z["numpy_version"]) == np.__version__, "inputs are drawn with another numpy"
+    assert int(z["n_tokens"]) == cal.n_tokens
+    assert str(z[pre + "x0_sha256"]) == _sha(gi.x_chunk(cal, wl.config, 0))
+    say(f"[workload] {key} d_in={d}: H over {cal.n_tokens} tokens (one call)")
+    X = _upload_calib(cal, wl.config)
+    Hg = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    hd = torch.zeros((d,), dtype=torch.float64, device="cuda")
+    P.gptq_hessian_accumulate(Hg, X, hd)
+    torch.cuda.synchronize()
+    del X
+    torch.cuda.empty_cache()
+    # Hessian: the fp64 diagonal, and a sampled block element by element
+    hdiag = z[pre + "hdiag"]
+    rel = float(np.max(np.abs(hd.cpu().numpy() - hdiag) / hdiag))
+    idx = z[pre + "h_idx"]
+    ti = torch.as_tensor(idx, device="cuda")
+    Hs = Hg.index_select(0, ti).index_select(1, ti).cpu().numpy().astype(np.float64)
+    ref = z[pre + "h_sub"]
+    dg = np.sqrt(np.diag(ref))
+    herr = float((np.abs(Hs - ref) / np.outer(dg, dg)).max())
+    say(f"  fp64 diagonal max rel {rel:.2e}; sampled H max |dH|/sqrt(Hii Hjj) {herr:.2e}")
+    assert rel <= 1e-12 and herr <= 1e-5
+    assert bool(torch.equal(Hg, Hg.t()))
 
-    q0 = wl.quant[0]
-    prep = o.prepare(H64, q0.damp_percent, bool(q0.desc_act))
+    desc = wl.quant[0].desc_act
+    damp = wl.quant[0].damp_percent
+    p2 = f"{pre}desc{desc}_"
     U = torch.empty((d, d), dtype=torch.float32, device="cuda")
     perm = torch.empty((d,), dtype=torch.int32, device="cuda")
-    P.gptq_prepare_hinv(Hg, q0.damp_percent, q0.desc_act, U, perm, hd)
-    assert np.array_equal(perm.cpu().numpy(), prep.perm)
-    Un = U.cpu().numpy().astype(np.float64)
-    rel = np.linalg.norm(Un - prep.U) / np.linalg.norm(prep.U)
-    say(f"  U: rel Frobenius = {rel:.2e}")
-    assert rel <= 1e-3 and np.all(np.tril(Un, -1) == 0)
-    del Un
+    P.gptq_prepare_hinv(Hg, damp, desc, U, perm, hd if desc else None)
+    pn = perm.cpu().numpy()
+    assert np.array_equal(pn, z[p2 + "perm"])
+    # the factor, element by element: diagonal relative, a sampled block
+    # relative to sqrt(U_ii U_jj)
+    ud = torch.diagonal(U).cpu().numpy().astype(np.float64)
+    uref = z[p2 + "u_diag"]
+    udrel = float(np.max(np.abs(ud - uref) / uref))
+    uidx = z[p2 + "u_idx"]
+    tu = torch.as_tensor(uidx, device="cuda")
+    Us = U.index_select(0, tu).index_select(1, tu).cpu().numpy().astype(np.float64)
+    us_ref = z[p2 + "u_sub"]
+    nd = np.sqrt(np.outer(np.diag(us_ref), np.diag(us_ref)))
+    uerr = float((np.abs(Us - us_ref) / nd).max())
+    say(f"  U: diagonal max rel {udrel:.2e}; sampled block max |dU|/sqrt(Uii Ujj) {uerr:.2e}")
+    assert udrel <= 1e-4 and uerr <= 1e-4
+    assert bool((torch.tril(U, -1) == 0).all())
 
-    rows = _sample(d_out, 62, 5, must=(0, d_out - 1))
-    Wg = to_dev(W, layer.dtype)
-    tr = torch.as_tensor(rows, device="cuda")
-    bar = AGREE.get((key, li), 0.999)
     failures = []
-    for q in wl.quant:
-        assert q.damp_percent == q0.damp_percent and q.desc_act == q0.desc_act
-        cfg = P.make_config(bits=q.bits, group_size=q.group_size, block_size=q.block_size,
-                            damp_percent=q.damp_percent, desc_act=q.desc_act)
-        res = P.quantize_layer_outputs(Wg, Hg, cfg, with_q=True, pack=True, U=U, perm=perm, hdiag=hd)
-        ref = o.gptq(W64[rows], H64, bits=q.bits, group_size=q.group_size,
-                     block_size=q.block_size, damp_percent=q.damp_percent,
-                     desc_act=bool(q.desc_act), prepared=prep)
-        G = d if q.group_size == -1 else q.group_size
-        codes = res.codes.index_select(0, tr).cpu().numpy()
-        par = compare_quant(ref, W64[rows], H64, codes, res.scales.index_select(0, tr).cpu().numpy(),
-                            res.zeros.index_select(0, tr).cpu().numpy(),
-                            res.Q.index_select(0, tr).cpu().numpy(), G)
-        say(f"  {q.bits}-bit G{q.group_size}: {par}")
-        ok = (np.array_equal(res.g_idx.cpu().numpy(), ref.g_idx)
-              and codes.min() >= 0 and codes.max() <= (1 << q.bits) - 1
-              and par.agree >= bar and par.first_not_tie == 0
-              and par.scale_rel <= 1e-3 and par.zero_mismatch == 0 and par.q_bad == 0
-              and par.obj_rel <= 1e-3)
-        if res.packed is not None:
+    for layer in wl.layers:
+        if layer.d_in != d:
+            continue
+        W = gi.weight(layer, wl.config)
+        assert str(z[f"{layer.name}_w_sha256"]) == _sha(W)
+        Wg = to_dev(W, layer.dtype)
+        W64 = gi.to_float64(W, layer.dtype)
+        for q in wl.quant:
+            k3 = f"{layer.name}_b{q.bits}_g{q.group_size}_"
+            rows = z[k3 + "rows"]
+            tr = torch.as_tensor(rows, device="cuda")
+            cfg = P.make_config(bits=q.bits, group_size=q.group_size, block_size=q.block_size,
+                                damp_percent=q.damp_percent, desc_act=q.desc_act)
+            res = P.quantize_layer_outputs(Wg, Hg, cfg, with_q=True, pack=True, U=U, perm=perm)
+            G = d if q.group_size == -1 else q.group_size
+            codes = res.codes.index_select(0, tr).cpu().numpy()
+            Qr = res.Q.index_select(0, tr)
+            par = compare_golden(z, k3, d, pn, codes, res.scales.index_select(0, tr).cpu().numpy(),
+                                 res.zeros.index_select(0, tr).cpu().numpy(), Qr.cpu().numpy(), G)
+            obj_gpu = P.gptq_layer_error(Hg, Wg.index_select(0, tr).contiguous(), Qr.contiguous())
+            obj_o = float(z[k3 + "obj_rows"].sum())
+            obj_rtn = float(z[k3 + "rtn_obj_rows"].sum())
+            obj_rel = abs(obj_gpu - obj_o) / obj_o
+            say(f"  {layer.name} {q.bits}-bit G{q.group_size}: {par}; objective gpu {obj_gpu:.6g} "
+                f"oracle {obj_o:.6g} (rel {obj_rel:.1e}), RTN {obj_rtn:.6g}")
+            ok = (np.array_equal(res.g_idx.cpu().numpy()[pn], np.arange(d) // G)
+                  and codes.min() >= 0 and codes.max() <= (1 << q.bits) - 1
+                  and par.agree >= 0.999 and par.first_not_tie == 0
+                  and par.scale_rel <= 1e-3 and par.zero_mismatch == 0 and par.q_bad == 0
+                  and obj_rel <= 1e-3 and obj_gpu <= obj_rtn)
             pk = res.packed.index_select(0, tr).cpu().numpy().view(np.uint32)
             ok = ok and np.array_equal(pk, o.pack_int4(codes))
-        if not ok:
-            failures.append((q.bits, q.group_size))
-        del res
+            if not ok:
+                failures.append((layer.name, q.bits, q.group_size))
+            del res
+        del Wg
+    del Hg, U
+    torch.cuda.empty_cache()
     assert not failures, failures
-
-
-def test_70b_down_proj_properties():
-    import post_weight_quantization_29_amd as P
-    wl = gi.workload("c5_70b_down_proj")
-    layer, q = wl.layers[0], wl.quant[0]
-    cal = wl.calib_for(layer.d_in)
-    d, d_out = layer.d_in, layer.d_out
-    say(f"[workload] c5 down_proj: W {d_out}x{d}, H from {CHUNK} tokens")
-    x0 = gi.x_chunk(cal, wl.config, 0)
-    Hg, hd = gpu_hessian([x0], cal.dtype, d, with_diag=True)
-    idx = _sample(d, 48, 17)
-    diag_ref = _diag_ref([x0], cal.dtype, d)
-    _check_h_sampled(Hg, idx, gi.to_float64(x0[:, idx], cal.dtype), hd, diag_ref)
-    del x0
-
-    U = torch.empty((d, d), dtype=torch.float32, device="cuda")
-    perm = torch.empty((d,), dtype=torch.int32, device="cuda")
-    P.gptq_prepare_hinv(Hg, q.damp_percent, q.desc_act, U, perm, hd)
-    pn = perm.cpu().numpy()
-    assert np.array_equal(pn, o.order_from_keys(diag_ref, bool(q.desc_act)))
-    # U^T U H_d = I on sampled columns of H_d = H[perm][:, perm] + lambda I
-    lam = q.damp_percent * float(np.mean(diag_ref))
-    S = _sample(d, 16, 23, must=(0, d - 1))
-    tp = perm.long()
-    HdS = Hg.index_select(0, tp).index_select(1, tp[torch.as_tensor(S, device="cuda")]).double()
-    HdS[torch.as_tensor(S, device="cuda"), torch.arange(len(S), device="cuda")] += lam
-    U64 = U.double()
-    Z = (U64.t() @ (U64 @ HdS)).cpu().numpy()
-    E = np.zeros_like(Z)
-    E[S, np.arange(len(S))] = 1.0
-    say(f"  U^T U H_d - I on {len(S)} columns: max {np.abs(Z - E).max():.2e}")
-    assert np.abs(Z - E).max() <= 1e-2
-    assert bool((torch.tril(U, -1) == 0).all()) and bool((torch.diagonal(U) > 0).all())
-    del U64, HdS
-
-    W = gi.weight(layer, wl.config)
-    W64 = gi.to_float64(W, layer.dtype)
-    cfg = P.make_config(bits=q.bits, group_size=q.group_size, block_size=q.block_size,
-                        damp_percent=q.damp_percent, desc_act=q.desc_act)
-    res = P.quantize_layer_outputs(to_dev(W, layer.dtype), Hg, cfg, with_q=True, pack=True,
-                                   U=U, perm=perm, hdiag=hd)
-    rows = _sample(d_out, 14, 29, must=(0, d_out - 1))
-    tr = torch.as_tensor(rows, device="cuda")
-    codes = res.codes.index_select(0, tr).cpu().numpy().astype(np.int64)
-    scales = res.scales.index_select(0, tr).cpu().numpy()
-    zeros = res.zeros.index_select(0, tr).cpu().numpy()
-    Qg = res.Q.index_select(0, tr).cpu().numpy()
-    g_idx = res.g_idx.cpu().numpy()
-    assert np.array_equal(g_idx[pn], np.arange(d) // q.group_size)
-    assert codes.min() >= 0 and codes.max() <= (1 << q.bits) - 1
-    # Q = scale * (code - zero) in fp32, group by g_idx
-    sc = scales[:, g_idx].astype(np.float32)
-    zc = zeros[:, g_idx].astype(np.float32)
-    assert np.array_equal(Qg, (sc * (codes.astype(np.float32) - zc)).astype(np.float32))
-    pk = res.packed.index_select(0, tr).cpu().numpy().view(np.uint32)
-    assert np.array_equal(pk, o.pack_int4(codes))
-    # GPTQ does not do worse than round-to-nearest on H's objective
-    Hn = Hg.cpu().numpy().astype(np.float64)
-    _, Qr = o.rtn(W64[rows], bits=q.bits, group_size=q.group_size, perm=pn)
-    og = o.objective(W64[rows], Qg.astype(np.float64), Hn)
-    orr = o.objective(W64[rows], Qr, Hn)
-    say(f"  objective on {len(rows)} rows: GPTQ {og:.4g}  RTN {orr:.4g}")
-    assert og <= orr
 
 
 _LARGE = {}
@@ -261,9 +240,9 @@ def _large_inputs(desc):
 
 @pytest.mark.parametrize("G,desc", [(-1, 0), (256, 1), (128, 1)])
 def test_large_layer_wide_groups(G, desc):
-    """A 4096 x 8192 layer (2^25 weights: the column loop's trailing updates
-    overlap the next panel on a second stream) with one group per row, groups
-    wider than the 128-column block, and in-block groups.  Both sides get the
+    """A 4096 x 8192 layer with one group per row, groups wider than the
+    128-column block (their fp64 scale carried from block to block), and
+    in-block groups.  Both sides get the
     same fp32 H (2 X^T X of 12,288 normal tokens, more than the 8192
     channels, so that H is well conditioned like the workloads'), so only the
     factor and the loop are compared; sampled rows."""
@@ -276,7 +255,9 @@ def test_large_layer_wide_groups(G, desc):
     cfg = P.make_config(bits=4, group_size=G, desc_act=desc)
     res = P.quantize_layer_outputs(torch.from_numpy(W).cuda(), torch.from_numpy(H32).cuda(), cfg,
                                    with_q=True)
-    rows = _sample(d_out, 16, 31, must=(0, d_out - 1))
+    # 128 sampled rows: one row's divergence after a tie flip is ~200 codes of
+    # 8192, so over 16 rows a single flip alone would be 0.15 % of the sample
+    rows = _sample(d_out, 126, 31, must=(0, d_out - 1))
     ref = o.gptq(W64[rows], H64, bits=4, group_size=G, damp_percent=0.01, desc_act=bool(desc),
                  prepared=prep)
     tr = torch.as_tensor(rows, device="cuda")
