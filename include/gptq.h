@@ -21,7 +21,9 @@
  *    matching *_workspace_size query.  Workspaces need 256-byte alignment
  *    (any hipMalloc / torch allocation satisfies this).
  *  - The library keeps no state between calls (no handles, no globals) and
- *    reads no environment variables: every option is an argument.
+ *    reads no environment variables: every option is an argument.  The one
+ *    exception is gptq_hessian_accumulate_noalloc, which keeps per device the
+ *    address of its static scratch array.
  *  - All work is enqueued on stream s, in stream order: it starts after the
  *    work already on s and is complete, as seen from s, before anything
  *    enqueued on s later.  Only gptq_prepare_hinv and gptq_layer_error
@@ -105,6 +107,24 @@ size_t gptq_hessian_workspace_size(int64_t n_tokens, int32_t d_in);
 int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, gptq_dtype x_dtype,
                             int64_t n_tokens, int32_t d_in, void* ws, size_t ws_bytes,
                             hipStream_t s);
+
+/* gptq_hessian_accumulate for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight calibration loops, harnesses that forbid
+ * hipMalloc): the same H and hdiag (same kernels; H within fp32 accumulation
+ * order of the other call, since the token range may be split differently),
+ * with the partial sums in a static device array of
+ * gptq_hessian_noalloc_scratch_bytes() = 256 MiB that each GPU the library
+ * runs on holds until the process ends.  It calls no allocator.
+ *  d_in up to 11,264 (one token split's partial tiles must fit the array);
+ *  larger d_in returns GPTQ_ERR_WORKSPACE before anything is enqueued.
+ *  The first call on a device looks up the array's device address (kept per
+ *  device).  Every call on one GPU shares its array, so calls that overlap on
+ *  one GPU (different streams, or host threads) race: order them on one
+ *  stream.  Nothing in the array needs clearing (every partial is written
+ *  before it is read). */
+size_t gptq_hessian_noalloc_scratch_bytes(void);
+int gptq_hessian_accumulate_noalloc(float* H, double* hdiag, const void* X, gptq_dtype x_dtype,
+                                    int64_t n_tokens, int32_t d_in, hipStream_t s);
 
 /* ---------------------------------------------------------------- H^-1 factor
  * From H (undamped, as accumulated): lambda = damp_percent * mean(diag H);

@@ -8,7 +8,8 @@ by layer.
 """
 from ._lib import (  # noqa: F401
     EXPORTED, GPTQError, LIB_PATH, NotPositiveDefinite, gptq_abi_version, gptq_config,
-    gptq_hessian_accumulate, gptq_hessian_workspace_size, gptq_layer_error,
+    gptq_hessian_accumulate, gptq_hessian_accumulate_noalloc, gptq_hessian_noalloc_scratch_bytes,
+    gptq_hessian_workspace_size, gptq_layer_error,
     gptq_layer_error_workspace_size, gptq_pack_dense, gptq_pack_int4, gptq_prepare_hinv,
     gptq_w4a16_gemm, AWQ_DEFAULT_GRID, gptq_awq_act_sumsq, gptq_awq_quantize, gptq_awq_search,
     gptq_awq_search_workspace_size, gptq_awq_sumsq_workspace_size, gptq_block_attention,

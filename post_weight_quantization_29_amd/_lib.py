@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         sig = {
             "gptq_hessian_workspace_size": (sz, [i64, i32]),
             "gptq_hessian_accumulate": (ctypes.c_int, [vp, vp, vp, ctypes.c_int, i64, i32, vp, sz, vp]),
+            "gptq_hessian_noalloc_scratch_bytes": (sz, []),
+            "gptq_hessian_accumulate_noalloc": (ctypes.c_int, [vp, vp, vp, ctypes.c_int, i64, i32, vp]),
             "gptq_prepare_hinv_workspace_size": (sz, [i32]),
             "gptq_prepare_hinv": (ctypes.c_int, [vp, vp, i32, ctypes.c_float, i32, vp, vp, vp, sz, vp]),
             "gptq_quantize_workspace_size": (sz, [i32, i32, ctypes.POINTER(gptq_config)]),
@@ -92,6 +94,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("gptq_hessian_workspace_size", "gptq_hessian_accumulate",
+            "gptq_hessian_noalloc_scratch_bytes", "gptq_hessian_accumulate_noalloc",
             "gptq_prepare_hinv_workspace_size", "gptq_prepare_hinv",
             "gptq_quantize_workspace_size", "gptq_quantize_layer", "gptq_pack_int4",
             "gptq_pack_dense", "gptq_w4a16_gemm", "gptq_awq_sumsq_workspace_size",
@@ -169,6 +172,24 @@ def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, hdiag: Optional[to
     _check(lib().gptq_hessian_accumulate(_ptr(H), _ptr(hdiag), _ptr(X), _DTYPE[X.dtype], n, d,
                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "gptq_hessian_accumulate")
+
+
+def gptq_hessian_noalloc_scratch_bytes() -> int:
+    return int(lib().gptq_hessian_noalloc_scratch_bytes())
+
+
+def gptq_hessian_accumulate_noalloc(H: torch.Tensor, X: torch.Tensor,
+                                    hdiag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """gptq_hessian_accumulate with the partial sums in the library's static
+    per-device scratch array (no allocation at all; d_in <= 11,264)."""
+    _dev(H, "H"); _dev(X, "X")
+    n, d = X.shape
+    assert H.dtype == torch.float32 and tuple(H.shape) == (d, d)
+    if hdiag is not None:
+        _dev(hdiag, "hdiag")
+        assert hdiag.dtype == torch.float64 and hdiag.numel() == d
+    _check(lib().gptq_hessian_accumulate_noalloc(_ptr(H), _ptr(hdiag), _ptr(X), _DTYPE[X.dtype], n, d,
+                                                 _stream(stream)), "gptq_hessian_accumulate_noalloc")
 
 
 def gptq_prepare_hinv_workspace_size(d_in: int) -> int:

@@ -11,6 +11,8 @@
 // partials in a fixed order into H and mirrors off-diagonal tiles.
 #include "common.h"
 
+#include <mutex>
+
 namespace gptq {
 
 // ---------------------------------------------------------------------------
@@ -641,7 +643,7 @@ struct SyrkPlan {
   size_t ws;      // partial buffers, bytes
 };
 
-static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32) {
+static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32, size_t max_ws = SIZE_MAX) {
   SyrkPlan p;
   p.tile = f32 ? kT32 : kT16;
   const int kst = f32 ? kK32 : kK16;
@@ -656,7 +658,11 @@ static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32) {
   const double bytes_tile = (double)p.tile * p.tile * 4.0 * 2.0;    // partial write + read
   double best = 1e300;
   int best_s = 1;
-  const int smax = (int)std::max<int64_t>(1, std::min<int64_t>(64, p.nk / 16));
+  int smax = (int)std::max<int64_t>(1, std::min<int64_t>(64, p.nk / 16));
+  // a scratch bound caps the split count (each split holds one partial per tile)
+  const size_t per_split = (size_t)p.ntiles * p.tile * p.tile * sizeof(float) +
+                           (size_t)nt * p.tile * sizeof(double) + 2 * kAlign;
+  if (max_ws != SIZE_MAX) smax = std::max(1, std::min<int>(smax, (int)(max_ws / per_split)));
   for (int s = 1; s <= smax; ++s) {
     const double items = (double)kXCD * ((p.ntiles + kXCD - 1) / kXCD) * s;
     const double rounds = std::ceil(items / 256.0);
@@ -670,27 +676,10 @@ static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32) {
   return p;
 }
 
-}  // namespace gptq
-
-using namespace gptq;
-
-extern "C" size_t gptq_hessian_workspace_size(int64_t n_tokens, int32_t d_in) {
-  if (n_tokens < 0 || d_in <= 0) return 0;
-  SyrkPlan a = syrk_plan(n_tokens, d_in, false), b = syrk_plan(n_tokens, d_in, true);
-  return std::max(a.ws, b.ws);
-}
-
-extern "C" int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, gptq_dtype x_dtype,
-                                       int64_t n_tokens, int32_t d_in, void* ws, size_t ws_bytes,
-                                       hipStream_t s) {
-  if (!H || d_in <= 0 || d_in > 65536 || (d_in % 8) != 0 || n_tokens < 0) return GPTQ_ERR_INVALID_ARG;
-  if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_F16 && x_dtype != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
-  if (n_tokens == 0) return GPTQ_OK;
-  if (!X || (reinterpret_cast<uintptr_t>(X) & 15)) return GPTQ_ERR_INVALID_ARG;
+// The calls below share one launch sequence; ws holds the plan's partials.
+static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_dtype, int64_t n_tokens,
+                          int32_t d_in, const SyrkPlan& p, void* ws, hipStream_t s) {
   const bool f32 = (x_dtype == GPTQ_F32);
-  SyrkPlan p = syrk_plan(n_tokens, d_in, f32);
-  if (!ws || ws_bytes < p.ws || ws_bytes < gptq_hessian_workspace_size(n_tokens, d_in))
-    return GPTQ_ERR_WORKSPACE;
   float* partial = static_cast<float*>(ws);
   double* pdiag = reinterpret_cast<double*>(static_cast<char*>(ws) + p.off_diag);
   const unsigned items = (unsigned)(kXCD * ((p.ntiles + kXCD - 1) / kXCD) * p.splits);
@@ -724,4 +713,74 @@ extern "C" int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, g
     GPTQ_LAUNCH_CHECK();
   }
   return GPTQ_OK;
+}
+
+static int hessian_check(float* H, const void* X, gptq_dtype x_dtype, int64_t n_tokens, int32_t d_in) {
+  if (!H || d_in <= 0 || d_in > 65536 || (d_in % 8) != 0 || n_tokens < 0) return GPTQ_ERR_INVALID_ARG;
+  if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_F16 && x_dtype != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return GPTQ_OK;
+  if (!X || (reinterpret_cast<uintptr_t>(X) & 15)) return GPTQ_ERR_INVALID_ARG;
+  return 1;
+}
+
+// ---------------------------------------------------------------------------
+// The variant that allocates nothing: its partials live in this file-scope
+// array, one copy per GPU, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in): the
+// device address is looked up once per device and kept.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(256) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GPTQ_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GPTQ_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GPTQ_OK;
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_hessian_workspace_size(int64_t n_tokens, int32_t d_in) {
+  if (n_tokens < 0 || d_in <= 0) return 0;
+  SyrkPlan a = syrk_plan(n_tokens, d_in, false), b = syrk_plan(n_tokens, d_in, true);
+  return std::max(a.ws, b.ws);
+}
+
+extern "C" int gptq_hessian_accumulate(float* H, double* hdiag, const void* X, gptq_dtype x_dtype,
+                                       int64_t n_tokens, int32_t d_in, void* ws, size_t ws_bytes,
+                                       hipStream_t s) {
+  const int c = hessian_check(H, X, x_dtype, n_tokens, d_in);
+  if (c != 1) return c;
+  const SyrkPlan p = syrk_plan(n_tokens, d_in, x_dtype == GPTQ_F32);
+  if (!ws || ws_bytes < p.ws || ws_bytes < gptq_hessian_workspace_size(n_tokens, d_in))
+    return GPTQ_ERR_WORKSPACE;
+  return hessian_launch(H, hdiag, X, x_dtype, n_tokens, d_in, p, ws, s);
+}
+
+extern "C" size_t gptq_hessian_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int gptq_hessian_accumulate_noalloc(float* H, double* hdiag, const void* X,
+                                               gptq_dtype x_dtype, int64_t n_tokens, int32_t d_in,
+                                               hipStream_t s) {
+  const int c = hessian_check(H, X, x_dtype, n_tokens, d_in);
+  if (c != 1) return c;
+  const SyrkPlan p = syrk_plan(n_tokens, d_in, x_dtype == GPTQ_F32, kScratchBytes);
+  if (p.ws > kScratchBytes) return GPTQ_ERR_WORKSPACE;   // one split's partials do not fit
+  void* ws = nullptr;
+  const int st = scratch_for_current_device(&ws);
+  if (st != GPTQ_OK) return st;
+  return hessian_launch(H, hdiag, X, x_dtype, n_tokens, d_in, p, ws, s);
 }
