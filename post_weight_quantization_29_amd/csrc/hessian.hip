@@ -192,11 +192,33 @@ GPTQ_DEV void wait_vm0() { wait_vm<0>(); }
 // DIAG = false (no diagonal requested) leaves all of this out.
 //
 // Partial layout (floats): [work item][wave 4][block 16 = mb*4+nb][reg 16][lane 64]
-template <typename T, bool DIAG>
+// Pacing.  A workgroup streams every token of its tile, so over a tile's
+// thousands of stages the co-resident workgroups of an XCD drift apart by
+// far more than the few stages of channel panels their L2 can hold for one
+// another, and each re-reads the panels it shares from memory (at 8192 x
+// 28672, 100x the activations' bytes per call).  Each workgroup therefore
+// publishes the stages it has done in its slot of its XCD's 64-slot row
+// (pace[x][c]) every four stages, and wave 0 waits while it is more than
+// kPaceLag stages ahead of the slowest workgroup of its XCD (finished ones
+// publish ~0u).  The wait is bounded (kPaceSpin polls); a workgroup whose
+// wait runs out stops pacing, so residency problems cost time, never a hang.
+// Only timing depends on it: every sum is the same.
+constexpr unsigned kPaceLag = 8;
+constexpr int kPaceSpin = 4096;
+constexpr int kPaceSlots = 64;
+
+GPTQ_DEV unsigned wave_min_u32(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o));
+  return v;
+}
+
+template <typename T, bool DIAG, bool PACE>
 __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X, int64_t n_tokens,
                                                          int d, int nt, int ntiles, int splits,
                                                          int nk, float* __restrict__ partial,
-                                                         double* __restrict__ pdiag) {
+                                                         double* __restrict__ pdiag,
+                                                         unsigned* __restrict__ pace) {
   __shared__ __attribute__((aligned(16))) T sA[kSlots16][kStage16];
   __shared__ __attribute__((aligned(16))) T sB[kSlots16][kStage16];
   constexpr uint32_t kSlotBytes = kStage16 * 2;    // 16 KB
@@ -223,9 +245,35 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   // and those sharing channel panels read the same tokens at the same time.
   const int x = blockIdx.x % kXCD, c = blockIdx.x / kXCD, nper = gridDim.x / kXCD;
   const int per_xcd = ((ntiles + kXCD - 1) / kXCD) * splits;
+  unsigned* prow = PACE ? pace + x * kPaceSlots : nullptr;
+  bool pacing = PACE && (wave == 0) && (nper <= kPaceSlots);
+  unsigned done = 0;                             // stages done (skipped items included)
+  // wave 0: publish `progress`, then wait (bounded) while more than kPaceLag
+  // stages ahead of the XCD's slowest workgroup
+  auto pace_at = [&](unsigned progress) {
+    if (!PACE || !pacing) return;
+    if (lane == 0) __hip_atomic_store(prow + c, progress, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0;; ++it) {
+      const unsigned v = (lane < nper) ? __hip_atomic_load(prow + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                       : ~0u;
+      if (wave_min_u32(v) + kPaceLag >= progress) break;
+      if (it == kPaceSpin) {
+        // stop pacing, and let no one wait on this workgroup any more
+        pacing = false;
+        if (lane == 0) __hip_atomic_store(prow + c, ~0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  };
   for (int kidx = c; kidx < per_xcd; kidx += nper) {
   int s, I, J;
-  if (!xcd_item(kidx * kXCD + x, nt, ntiles, splits, s, I, J)) continue;
+  if (!xcd_item(kidx * kXCD + x, nt, ntiles, splits, s, I, J)) {
+    // a padding item: count its stages as done so the others do not wait on it
+    const int sp = kidx / ((ntiles + kXCD - 1) / kXCD);
+    if (PACE && sp < splits) done += (unsigned)((int64_t)nk * (sp + 1) / splits - (int64_t)nk * sp / splits);
+    continue;
+  }
   s = __builtin_amdgcn_readfirstlane(s);
   I = __builtin_amdgcn_readfirstlane(I);
   J = __builtin_amdgcn_readfirstlane(J);
@@ -390,6 +438,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     static_assert(kSlots16 == 4, "stage groups of four");
     int kk = ks0;                                  // stage kk uses slot (kk - ks0) % kSlots16
     for (; kk + 4 <= ks1; kk += 4) {
+      pace_at(done + (unsigned)(kk - ks0));
       stage.template operator()<0>(kk);
       stage.template operator()<1>(kk + 1);
       stage.template operator()<2>(kk + 2);
@@ -399,6 +448,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     if (kk < ks1) stage.template operator()<1>(kk++);
     if (kk < ks1) stage.template operator()<2>(kk++);
   }
+  if (PACE) done += (unsigned)(ks1 - ks0);
 
   float* out = partial + ((size_t)w * 4 + wave) * (16 * 16 * 64);
 #pragma unroll
@@ -429,6 +479,8 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     pdiag[((size_t)s * nt + pan) * kT16 + ch] = t;
   }
   }
+  // finished: no one waits on this workgroup
+  if (PACE && wave == 0 && lane == 0) __hip_atomic_store(prow + c, ~0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -640,8 +692,13 @@ struct SyrkPlan {
   int64_t nk;     // number of token stages
   int nt;         // tile rows
   size_t off_diag;
+  size_t off_pace;  // kXCD x kPaceSlots progress slots of the 16-bit kernel
   size_t ws;      // partial buffers, bytes
 };
+
+__global__ __launch_bounds__(256) void zero_u32_kernel(unsigned* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
 
 static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32, size_t max_ws = SIZE_MAX) {
   SyrkPlan p;
@@ -661,7 +718,8 @@ static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32, size_t max_ws = SIZ
   int smax = (int)std::max<int64_t>(1, std::min<int64_t>(64, p.nk / 16));
   // a scratch bound caps the split count (each split holds one partial per tile)
   const size_t per_split = (size_t)p.ntiles * p.tile * p.tile * sizeof(float) +
-                           (size_t)nt * p.tile * sizeof(double) + 2 * kAlign;
+                           (size_t)nt * p.tile * sizeof(double) + 2 * kAlign +
+                           (size_t)kXCD * kPaceSlots * sizeof(unsigned);
   if (max_ws != SIZE_MAX) smax = std::max(1, std::min<int>(smax, (int)(max_ws / per_split)));
   for (int s = 1; s <= smax; ++s) {
     const double items = (double)kXCD * ((p.ntiles + kXCD - 1) / kXCD) * s;
@@ -672,7 +730,8 @@ static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32, size_t max_ws = SIZ
   p.splits = (p.nk == 0) ? 1 : best_s;
   const size_t per_item = (size_t)p.tile * p.tile * sizeof(float);
   p.off_diag = align_up((size_t)p.splits * p.ntiles * per_item);
-  p.ws = align_up(p.off_diag + (size_t)p.splits * nt * p.tile * sizeof(double));
+  p.off_pace = align_up(p.off_diag + (size_t)p.splits * nt * p.tile * sizeof(double));
+  p.ws = align_up(p.off_pace + (size_t)kXCD * kPaceSlots * sizeof(unsigned));
   return p;
 }
 
@@ -682,20 +741,31 @@ static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_d
   const bool f32 = (x_dtype == GPTQ_F32);
   float* partial = static_cast<float*>(ws);
   double* pdiag = reinterpret_cast<double*>(static_cast<char*>(ws) + p.off_diag);
+  unsigned* pace = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + p.off_pace);
   const unsigned items = (unsigned)(kXCD * ((p.ntiles + kXCD - 1) / kXCD) * p.splits);
   // 16-bit path: one resident workgroup per CU (256 CUs), persistent over items
   const unsigned pgrid = std::min<unsigned>(256u, items);
   const unsigned pg = (pgrid + kXCD - 1) / kXCD * kXCD;
   // the fp64 diagonal only when it is asked for (the 16-bit kernels then do
   // no diagonal work at all; H is the same either way)
+  // pacing pays where every workgroup streams all tokens of its tiles (one
+  // split: 262,144-token chains at 8192 x 28672, 4 % faster, 3.8x less
+  // traffic); with split token ranges the items are short and it does not
+  const bool pace_on = !f32 && p.splits == 1;
+  if (pace_on) {
+    zero_u32_kernel<<<1, 256, 0, s>>>(pace, kXCD * kPaceSlots);
+    GPTQ_LAUNCH_CHECK();
+  }
   if (x_dtype == GPTQ_BF16) {
-    auto k = hdiag ? syrk16_kernel<__bf16, true> : syrk16_kernel<__bf16, false>;
+    auto k = hdiag ? (pace_on ? syrk16_kernel<__bf16, true, true> : syrk16_kernel<__bf16, true, false>)
+                   : (pace_on ? syrk16_kernel<__bf16, false, true> : syrk16_kernel<__bf16, false, false>);
     k<<<pg, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
-                         (int)p.nk, partial, pdiag);
+                         (int)p.nk, partial, pdiag, pace);
   } else if (x_dtype == GPTQ_F16) {
-    auto k = hdiag ? syrk16_kernel<_Float16, true> : syrk16_kernel<_Float16, false>;
+    auto k = hdiag ? (pace_on ? syrk16_kernel<_Float16, true, true> : syrk16_kernel<_Float16, true, false>)
+                   : (pace_on ? syrk16_kernel<_Float16, false, true> : syrk16_kernel<_Float16, false, false>);
     k<<<pg, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
-                         (int)p.nk, partial, pdiag);
+                         (int)p.nk, partial, pdiag, pace);
   } else {
     syrk32_kernel<<<items, 256, 0, s>>>(static_cast<const float*>(X), n_tokens, d_in, p.nt, p.ntiles,
                                         p.splits, p.nk, partial, pdiag);
