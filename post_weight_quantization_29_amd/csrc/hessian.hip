@@ -72,12 +72,14 @@ GPTQ_DEV int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
 
 // ---------------------------------------------------------------------------
 // 16-bit inputs: bf16 / fp16, v_mfma_f32_32x32x16_{bf16,f16}
-// Workgroup tile 256x256, 4 waves (2x2) of 128x128, 48 tokens per stage.
+// Workgroup tile 256x256, 4 waves (2x2) of 128x128, 32 tokens per stage.
 //
 // Stages are copied HBM -> LDS by buffer_load ... lds (16 bytes per lane, the
 // 64 lanes of one instruction fill 1 KB of LDS in lane order) into a ring of
-// three slots: stage kk+2 streams in while stage kk is multiplied, so a copy
-// has about two stages to land, with no staging registers.  The 16 copies a wave issues per stage are interleaved one per
+// five slots (160 KB, all of a CU's LDS): stage kk+3 streams in while stage kk
+// is multiplied, so a copy has about three stages to land, with no staging
+// registers.  (Four slots, two stages of slack, cost 8 % at 8192 x 28672, where
+// the paced workgroups run at 2 GHz and the copies' latency showed.)  The 16 copies a wave issues per stage are interleaved one per
 // MFMA with the first k-slice, so the MFMA pipe keeps running while the
 // address unit takes them.  A stage row (one token, 256 channels) is 512 bytes, unpadded;
 // its 16-byte chunk c sits at slot c ^ 4*(row % 4), which keeps the
@@ -87,7 +89,7 @@ GPTQ_DEV int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
 // ---------------------------------------------------------------------------
 constexpr int kT16 = 256;          // tile edge (channels)
 constexpr int kK16 = 32;           // tokens per stage (2 k-slices of 16)
-constexpr int kSlots16 = 4;        // LDS ring slots
+constexpr int kSlots16 = 5;        // LDS ring slots
 constexpr int kRow16 = kT16;       // LDS row pitch in elements (512 bytes)
 constexpr int kStage16 = kK16 * kRow16;
 constexpr int kDiagRows = 4;       // x^2 rows (16-byte chunks) per thread per stage, at most
@@ -435,18 +437,20 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
         }
       }
     };
-    static_assert(kSlots16 == 4, "stage groups of four");
+    static_assert(kSlots16 == 5, "stage groups of five");
     int kk = ks0;                                  // stage kk uses slot (kk - ks0) % kSlots16
-    for (; kk + 4 <= ks1; kk += 4) {
+    for (; kk + 5 <= ks1; kk += 5) {
       pace_at(done + (unsigned)(kk - ks0));
       stage.template operator()<0>(kk);
       stage.template operator()<1>(kk + 1);
       stage.template operator()<2>(kk + 2);
       stage.template operator()<3>(kk + 3);
+      stage.template operator()<4>(kk + 4);
     }
     if (kk < ks1) stage.template operator()<0>(kk++);
     if (kk < ks1) stage.template operator()<1>(kk++);
     if (kk < ks1) stage.template operator()<2>(kk++);
+    if (kk < ks1) stage.template operator()<3>(kk++);
   }
   if (PACE) done += (unsigned)(ks1 - ks0);
 
