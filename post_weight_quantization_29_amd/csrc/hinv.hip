@@ -566,11 +566,11 @@ static void tree_launch_shape(const std::vector<TreeNode>& nodes, size_t c0, int
   }
 }
 
-// Blocks per super-block of the factor's trailing updates: 4 once the padded
+// Blocks per super-block of the factor's trailing updates: 8 once the padded
 // matrix exceeds the 256 MB last-level cache (the rank-128 updates are then
 // bound by its read-modify-write from HBM), else 1.
 static int hinv_super_blocks(int np) {
-  return ((size_t)np * np * sizeof(float) > (size_t(256) << 20)) ? 4 : 1;
+  return ((size_t)np * np * sizeof(float) > (size_t(256) << 20)) ? 8 : 1;
 }
 
 static HinvLayout hinv_layout(int n) {
