@@ -654,7 +654,7 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
                      "kernel": ("gptq_hessian_accumulate: syrk16_kernel<bf16> + syrk_reduce_kernel<4, 512>"
-                                + (" + diag_reduce_kernel (fp64 diagonal keys)" if q.desc_act else "")),
+                                + (" + sumsq_kernel pass (fp64 diagonal keys)" if q.desc_act else "")),
                      "work_per_launch": f"N*d*(d+1) = {h_flops:.4g} flop"},
     }
     if not args.no_extras:

@@ -92,8 +92,6 @@ constexpr int kK16 = 32;           // tokens per stage (2 k-slices of 16)
 constexpr int kSlots16 = 5;        // LDS ring slots
 constexpr int kRow16 = kT16;       // LDS row pitch in elements (512 bytes)
 constexpr int kStage16 = kK16 * kRow16;
-constexpr int kDiagRows = 4;       // x^2 rows (16-byte chunks) per thread per stage, at most
-constexpr int kChunks = kT16 / 8;  // 16-byte chunks per panel row
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -179,19 +177,8 @@ GPTQ_DEV void wait_vm() {
 }
 GPTQ_DEV void wait_vm0() { wait_vm<0>(); }
 
-// Every tile also sums x^2 in fp64 for a slice of the channels of its two
-// panels (the squares of 16-bit values are exact), in 16-byte chunks of 8
-// channels read with one ds_read_b128: tile (I, J) takes slice J of panel I
-// and, off the diagonal, slice I of panel J, where slice q of a panel is
-// chunks [32q/nt, 32(q+1)/nt).  Each (panel, slice) pair occurs in exactly
-// one tile, so every channel is summed once per split, and every tile carries
-// a small share of this work.  (Measured: one 16-byte read and 8 squares per
-// row in the first waves is faster than spreading 4-channel pieces over all
-// four waves.)  These sums are the keys of the
-// descending-diagonal column order, so that order does not hinge on fp32
-// accumulation rounding.
-//
-// DIAG = false (no diagonal requested) leaves all of this out.
+// The fp64 diagonal keys of 16-bit inputs (the desc_act order) are not summed
+// here: a separate streaming pass over X does it (see hessian_launch).
 //
 // Partial layout (floats): [work item][wave 4][block 16 = mb*4+nb][reg 16][lane 64]
 // Pacing.  A workgroup streams every token of its tile, so over a tile's
@@ -215,11 +202,10 @@ GPTQ_DEV unsigned wave_min_u32(unsigned v) {
   return v;
 }
 
-template <typename T, bool DIAG, bool PACE>
+template <typename T, bool PACE>
 __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X, int64_t n_tokens,
                                                          int d, int nt, int ntiles, int splits,
                                                          int nk, float* __restrict__ partial,
-                                                         double* __restrict__ pdiag,
                                                          unsigned* __restrict__ pace) {
   __shared__ __attribute__((aligned(16))) T sA[kSlots16][kStage16];
   __shared__ __attribute__((aligned(16))) T sB[kSlots16][kStage16];
@@ -327,19 +313,6 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
                  : "memory", "m0");
   };
 
-  // fp64 x^2 slices: Cc chunks over P row phases (Cc <= 32, so P >= 8 and a
-  // thread takes at most kDiagRows = 4 of a stage's 32 rows)
-  const int cA0 = (kChunks * J) / nt, nA = (kChunks * (J + 1)) / nt - cA0;
-  const int cB0 = (kChunks * I) / nt, nB = (I != J) ? (kChunks * (I + 1)) / nt - cB0 : 0;
-  const int Cc = nA + nB;
-  const int P = (Cc > 0) ? kT16 / Cc : 1;
-  const int dci = (Cc > 0) ? tid % Cc : 0, dph = (Cc > 0) ? tid / Cc : P;
-  const bool dB = dci >= nA;                       // a chunk of panel J (in sB)
-  const int dchunk = dB ? cB0 + (dci - nA) : cA0 + dci;
-  const int dM = (dph < P) ? (kK16 - dph + P - 1) / P : 0;   // rows dph, dph+P, ... < kK16
-  double dsum[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dsum[e] = 0.0;
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -385,12 +358,6 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
       constexpr int NSLOT = (SLOT + 1) % kSlots16, DSLOT = (SLOT + kSlots16 - 1) % kSlots16;
       const uint32_t bA = ldsA + (uint32_t)SLOT * kSlotBytes, bB = ldsB + (uint32_t)SLOT * kSlotBytes;
       const uint32_t nA = ldsA + (uint32_t)NSLOT * kSlotBytes, nB = ldsB + (uint32_t)NSLOT * kSlotBytes;
-      // this thread's x^2 rows of the stage: one 16-byte chunk each
-      const T* dst_ = dB ? sB[SLOT] : sA[SLOT];
-      uint4 dv[kDiagRows];
-#pragma unroll
-      for (int u = 0; u < kDiagRows; ++u)
-        if (DIAG && u < dM) dv[u] = *reinterpret_cast<const uint4*>(dst_ + swz16(dph + P * u, 8 * dchunk));
       i32x4_t rn;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -420,21 +387,6 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
           if (last && n < 2 * NI) dma(rn, DSLOT, n);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (DIAG && ks == 0) {
-#pragma unroll
-          for (int u = 0; u < kDiagRows; ++u) {
-            if (u < dM) {
-              const uint32_t wv[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint16_t hv = (uint16_t)((e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xFFFFu));
-                const double v = (double)Op16<T>::to_f32(hv);
-                dsum[e] = fma(v, v, dsum[e]);
-              }
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
     };
     static_assert(kSlots16 == 5, "stage groups of five");
@@ -461,27 +413,6 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) out[((i * 4 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
-
-  // per-phase sums through the first stage slot (copies past the item's end
-  // still land in the slots, so wait for them first), added in phase order
-  if (!DIAG) continue;
-  wait_vm0();
-  __syncthreads();
-  double* sD = reinterpret_cast<double*>(&sA[0][0]);   // [phase][chunk][8]: P * Cc * 8 <= 2048
-  if (dph < P) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sD[(dph * Cc + dci) * 8 + e] = dsum[e];
-  }
-  __syncthreads();
-  if (tid < 8 * Cc) {
-    const int ci = tid >> 3, e = tid & 7;
-    double t = 0.0;
-    for (int ph = 0; ph < P; ++ph) t += sD[(ph * Cc + ci) * 8 + e];
-    const bool inB = ci >= nA;
-    const int pan = inB ? J : I;
-    const int ch = 8 * (inB ? cB0 + (ci - nA) : cA0 + ci) + e;
-    pdiag[((size_t)s * nt + pan) * kT16 + ch] = t;
-  }
   }
   // finished: no one waits on this workgroup
   if (PACE && wave == 0 && lane == 0) __hip_atomic_store(prow + c, ~0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -697,11 +628,24 @@ struct SyrkPlan {
   int nt;         // tile rows
   size_t off_diag;
   size_t off_pace;  // kXCD x kPaceSlots progress slots of the 16-bit kernel
+  size_t off_sq;    // the 16-bit path's fp64 sums of squares [d] and their token-split partials
+  size_t sq_ws;
   size_t ws;      // partial buffers, bytes
 };
 
 __global__ __launch_bounds__(256) void zero_u32_kernel(unsigned* __restrict__ p, int n) {
   for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void zero_f64_kernel(double* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.0;
+}
+
+// hdiag[c] += 2 * t[c]  (t: the channels' sums of squares)
+__global__ __launch_bounds__(256) void add_twice_kernel(double* __restrict__ hdiag, const double* __restrict__ t, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) hdiag[i] += 2.0 * t[i];
 }
 
 static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32, size_t max_ws = SIZE_MAX) {
@@ -735,7 +679,9 @@ static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32, size_t max_ws = SIZ
   const size_t per_item = (size_t)p.tile * p.tile * sizeof(float);
   p.off_diag = align_up((size_t)p.splits * p.ntiles * per_item);
   p.off_pace = align_up(p.off_diag + (size_t)p.splits * nt * p.tile * sizeof(double));
-  p.ws = align_up(p.off_pace + (size_t)kXCD * kPaceSlots * sizeof(unsigned));
+  p.off_sq = align_up(p.off_pace + (size_t)kXCD * kPaceSlots * sizeof(unsigned));
+  p.sq_ws = f32 ? 0 : gptq_awq_sumsq_workspace_size(n_tokens, d);
+  p.ws = align_up(p.off_sq + (f32 ? 0 : align_up((size_t)d * sizeof(double)) + p.sq_ws));
   return p;
 }
 
@@ -746,6 +692,19 @@ static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_d
   float* partial = static_cast<float*>(ws);
   double* pdiag = reinterpret_cast<double*>(static_cast<char*>(ws) + p.off_diag);
   unsigned* pace = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + p.off_pace);
+  if (hdiag && !f32) {
+    // the 16-bit path's fp64 keys come from one streaming pass over X (exact
+    // squares summed in fp64, token splits added in a fixed order): summing
+    // them inside the SYRK tiles cost ~9 % of the call, the pass ~1.5 %
+    double* t = reinterpret_cast<double*>(static_cast<char*>(ws) + p.off_sq);
+    void* sq_ws = static_cast<char*>(ws) + p.off_sq + align_up((size_t)d_in * sizeof(double));
+    zero_f64_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(t, d_in);
+    GPTQ_LAUNCH_CHECK();
+    const int st = gptq_awq_act_sumsq(t, X, x_dtype, n_tokens, d_in, sq_ws, p.sq_ws, s);
+    if (st != GPTQ_OK) return st;
+    add_twice_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(hdiag, t, d_in);
+    GPTQ_LAUNCH_CHECK();
+  }
   const unsigned items = (unsigned)(kXCD * ((p.ntiles + kXCD - 1) / kXCD) * p.splits);
   // 16-bit path: one resident workgroup per CU (256 CUs), persistent over items
   const unsigned pgrid = std::min<unsigned>(256u, items);
@@ -761,15 +720,13 @@ static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_d
     GPTQ_LAUNCH_CHECK();
   }
   if (x_dtype == GPTQ_BF16) {
-    auto k = hdiag ? (pace_on ? syrk16_kernel<__bf16, true, true> : syrk16_kernel<__bf16, true, false>)
-                   : (pace_on ? syrk16_kernel<__bf16, false, true> : syrk16_kernel<__bf16, false, false>);
+    auto k = pace_on ? syrk16_kernel<__bf16, true> : syrk16_kernel<__bf16, false>;
     k<<<pg, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
-                         (int)p.nk, partial, pdiag, pace);
+                         (int)p.nk, partial, pace);
   } else if (x_dtype == GPTQ_F16) {
-    auto k = hdiag ? (pace_on ? syrk16_kernel<_Float16, true, true> : syrk16_kernel<_Float16, true, false>)
-                   : (pace_on ? syrk16_kernel<_Float16, false, true> : syrk16_kernel<_Float16, false, false>);
+    auto k = pace_on ? syrk16_kernel<_Float16, true> : syrk16_kernel<_Float16, false>;
     k<<<pg, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
-                         (int)p.nk, partial, pdiag, pace);
+                         (int)p.nk, partial, pace);
   } else {
     syrk32_kernel<<<items, 256, 0, s>>>(static_cast<const float*>(X), n_tokens, d_in, p.nt, p.ntiles,
                                         p.splits, p.nk, partial, pdiag);
@@ -782,7 +739,7 @@ static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_d
     // loads in flight come from more threads per workgroup
     syrk_reduce_kernel<4, 512><<<p.ntiles * 4, 512, 0, s>>>(partial, H, d_in, p.ntiles, p.splits);
   GPTQ_LAUNCH_CHECK();
-  if (hdiag) {
+  if (hdiag && f32) {
     diag_reduce_kernel<<<(d_in + 255) / 256, 256, 0, s>>>(pdiag, d_in, p.nt * p.tile, p.splits, hdiag);
     GPTQ_LAUNCH_CHECK();
   }
