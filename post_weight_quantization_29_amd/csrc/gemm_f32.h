@@ -81,6 +81,17 @@ GPTQ_DEV void gemm_gload(const GemmProblem& P, int m0, int n0, int k0, int khi, 
                          float4 (&ra)[8], float4 (&rb)[8]) {
   // B (and k-major A): row k = k0 + tid/32 + 8i, columns c = 4*(tid%32) .. +3
   const int c4 = 4 * (tid & 31);
+  if (VEC && A_KMAJOR && m0 + kGT <= P.M && n0 + kGT <= P.N && k0 + kGK <= khi) {
+    // a chunk inside every bound (the common case; the test is uniform over
+    // the workgroup): no per-lane limits, so no branches around the loads
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + (tid >> 5) + 8 * i;
+      rb[i] = *reinterpret_cast<const float4*>(P.B + (size_t)k * P.ldb + n0 + c4);
+      ra[i] = *reinterpret_cast<const float4*>(P.A + (size_t)k * P.lda + m0 + c4);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int k = k0 + (tid >> 5) + 8 * i;
@@ -255,12 +266,14 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // C's old values are loaded before the contraction so that their latency and
-  // bandwidth overlap the MFMA work (C never aliases A or B when beta != 0)
+  if (!skip) gemm_tile_contract<A_KMAJOR, VEC>(P, m0, n0, klo, khi, sA, sB, acc);
+
+  // C's old values are read after the contraction, all 64 per thread in one
+  // batch: read first, they held 64 registers through the contraction and
+  // their loads queued ahead of the first operand chunk's (the other
+  // workgroup on the CU covers this batch's latency)
   float cold[2][2][16];
   if (EPI == kStore && !skip && beta != 0.0f) gemm_tile_load_c(P, m0, n0, cold);
-
-  if (!skip) gemm_tile_contract<A_KMAJOR, VEC>(P, m0, n0, klo, khi, sA, sB, acc);
 
   if (EPI == kPartial) {
     float* out = reinterpret_cast<float*>(dot_out) + ((size_t)blockIdx.x * 4 + wave) * (4 * 16 * 64);

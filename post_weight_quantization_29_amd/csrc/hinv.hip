@@ -89,7 +89,78 @@ __global__ __launch_bounds__(256) void act_order_kernel(const float* __restrict_
   if (i < n) perm[rank] = i;
 }
 
+// The same rank, with the chip filled: a workgroup takes 64 keys i (one per
+// lane) and its 16 waves split the keys j into 16 contiguous slices; a wave
+// reads 64 keys j at a time (one per lane) and hands them to every lane with
+// v_readlane, so each comparison costs no memory access.  The 16 partial
+// counts of key i are added in slice order.
+constexpr int kRankSlices = 16;
+__global__ __launch_bounds__(1024) void act_rank_kernel(const float* __restrict__ H,
+                                                        const double* __restrict__ hdiag, int n,
+                                                        int* __restrict__ perm) {
+  __shared__ int part[kRankSlices][64];
+  const int lane = threadIdx.x & 63;
+  const int q = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int i = blockIdx.x * 64 + lane;
+  const double ki = (i < n) ? diag_key(H, hdiag, n, i) : 0.0;
+  const int j0 = (int)((int64_t)n * q / kRankSlices), j1 = (int)((int64_t)n * (q + 1) / kRankSlices);
+  int rank = 0;
+  for (int jb = j0; jb < j1; jb += 64) {
+    const int jl = jb + lane;
+    const double kl = (jl < j1) ? diag_key(H, hdiag, n, jl) : 0.0;
+    const int lo = __double2loint(kl), hi = __double2hiint(kl);
+    const int cnt = min(64, j1 - jb);
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+      if (u < cnt) {
+        const double kj = __hiloint2double(__builtin_amdgcn_readlane(hi, u), __builtin_amdgcn_readlane(lo, u));
+        rank += key_before(kj, jb + u, ki, i) ? 1 : 0;
+      }
+    }
+  }
+  part[q][lane] = rank;
+  __syncthreads();
+  if (q == 0 && i < n) {
+    int r = 0;
+#pragma unroll
+    for (int t = 0; t < kRankSlices; ++t) r += part[t][lane];
+    perm[r] = i;
+  }
+}
+
 // ---------------------------------------------------------------- 3. gather
+// Output row a reads source row perm[n-1-a] of H at the columns
+// perm[n-1-b]: the row is first copied to LDS with coalesced loads and the
+// column gather then reads LDS (a direct gather from memory touches a new
+// cache line for almost every element).  Rows up to kGatherRow floats.
+constexpr int kGatherRow = 32768;
+__global__ __launch_bounds__(1024) void gather_flip_row_kernel(const float* __restrict__ H, int n, int np,
+                                                              const int* __restrict__ perm,
+                                                              const double* __restrict__ lam,
+                                                              float* __restrict__ A) {
+  __shared__ float row[kGatherRow];
+  const int a = blockIdx.x;
+  float* out = A + (size_t)a * np;
+  if (a >= n) {                        // padding rows: identity
+    for (int b = threadIdx.x; b < np; b += 1024) out[b] = (a == b) ? 1.0f : 0.0f;
+    return;
+  }
+  const float* src = H + (size_t)perm[n - 1 - a] * n;
+  for (int c = threadIdx.x; c < n; c += 1024) row[c] = src[c];
+  __syncthreads();
+  const float l = (float)lam[0];
+  for (int b = threadIdx.x; b < np; b += 1024) {
+    float v;
+    if (b < n) {
+      v = row[perm[n - 1 - b]];
+      if (a == b) v += l;
+    } else {
+      v = (a == b) ? 1.0f : 0.0f;
+    }
+    out[b] = v;
+  }
+}
+
 __global__ __launch_bounds__(256) void gather_flip_kernel(const float* __restrict__ H, int n, int np,
                                                           const int* __restrict__ perm,
                                                           const double* __restrict__ lam,
@@ -378,9 +449,9 @@ GPTQ_DEV void trail_tile(float* A, int np, int k, const TrailArgs& t, int local,
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  gemm_tile_contract<true, true>(P, m0, n0, 0, t.K, sA, sB, acc);
   float cold[2][2][16];
   gemm_tile_load_c(P, m0, n0, cold);
-  gemm_tile_contract<true, true>(P, m0, n0, 0, t.K, sA, sB, acc);
   gemm_tile_store(P, m0, n0, -1.0f, 1.0f, acc, cold);
 }
 
@@ -635,9 +706,15 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
 
   damp_lambda_kernel<<<1, 1024, 0, s>>>(H, hdiag, n, damp_percent, lam, flag);
   GPTQ_LAUNCH_CHECK();
-  act_order_kernel<<<(n + 255) / 256, 256, 0, s>>>(H, hdiag, n, desc_act, perm);
+  if (desc_act)
+    act_rank_kernel<<<(n + 63) / 64, 1024, 0, s>>>(H, hdiag, n, perm);
+  else
+    act_order_kernel<<<(n + 255) / 256, 256, 0, s>>>(H, hdiag, n, desc_act, perm);
   GPTQ_LAUNCH_CHECK();
-  gather_flip_kernel<<<dim3((np + 255) / 256, np), 256, 0, s>>>(H, n, np, perm, lam, A);
+  if (n <= kGatherRow)
+    gather_flip_row_kernel<<<np, 1024, 0, s>>>(H, n, np, perm, lam, A);
+  else
+    gather_flip_kernel<<<dim3((np + 255) / 256, np), 256, 0, s>>>(H, n, np, perm, lam, A);
   GPTQ_LAUNCH_CHECK();
 
   // 4. Cholesky A = R^T R: per block, diagonal factor + panel in one launch,

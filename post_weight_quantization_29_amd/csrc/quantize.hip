@@ -36,6 +36,25 @@ __global__ __launch_bounds__(256) void gather_w_kernel(const void* __restrict__ 
     Wp[(size_t)r * d + j] = load_as_float(W, wt, (size_t)r * d + src);
 }
 
+// The same gather with row r staged in LDS first (coalesced loads; the
+// permuted reads then hit LDS instead of a new cache line per element); one
+// workgroup per row, rows up to kGatherW elements.
+constexpr int kGatherW = 32768;
+__global__ __launch_bounds__(1024) void gather_w_row_kernel(const void* __restrict__ W, gptq_dtype wt,
+                                                           int d_out, int d, const int* __restrict__ perm,
+                                                           int G, float* __restrict__ Wp,
+                                                           int* __restrict__ g_idx) {
+  __shared__ float row[kGatherW];
+  const int r = blockIdx.x;
+  for (int c = threadIdx.x; c < d; c += 1024) row[c] = load_as_float(W, wt, (size_t)r * d + c);
+  __syncthreads();
+  for (int j = threadIdx.x; j < d; j += 1024) {
+    const int src = perm[j];
+    if (r == 0) g_idx[src] = j / G;
+    Wp[(size_t)r * d + j] = row[src];
+  }
+}
+
 // ---------------------------------------------------------------- pack
 // packed word m = sum_k (codes[8m+k] & 15) << 4k over the flat code array
 // (cols % 8 == 0, so no word straddles two rows).
@@ -186,8 +205,11 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   float* ErrT = reinterpret_cast<float*>(base + L.off_err);
   double* gscale = reinterpret_cast<double*>(base + L.off_gscale);
 
-  gather_w_kernel<<<dim3((d + 255) / 256, std::min(d_out, 1024)), 256, 0, s>>>(W, w_dtype, d_out, d,
-                                                                              perm, G, Wp, g_idx);
+  if (d <= kGatherW)
+    gather_w_row_kernel<<<d_out, 1024, 0, s>>>(W, w_dtype, d_out, d, perm, G, Wp, g_idx);
+  else
+    gather_w_kernel<<<dim3((d + 255) / 256, std::min(d_out, 1024)), 256, 0, s>>>(W, w_dtype, d_out, d,
+                                                                                perm, G, Wp, g_idx);
   GPTQ_LAUNCH_CHECK();
 
   PanelArgs pa;
