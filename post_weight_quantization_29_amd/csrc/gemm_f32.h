@@ -6,7 +6,7 @@
 //
 // Aop(m, k) = A[k*lda + m] ("k-major", A_KMAJOR) or A[m*lda + k];
 // Bop(k, n) = B[k*ldb + n] always.  Tiles are 128x128, four waves (2x2) of
-// 64x64; k runs in chunks of 64, each loaded into registers (float4 when the
+// 64x64; k runs in chunks of 32, each loaded into registers (float4 when the
 // leading dimensions allow) while the previous chunk is multiplied out of
 // LDS, so global latency hides behind a chunk of MFMA work.  Several independent
 // problems of one shape class (a "group") run in one launch; each workgroup
@@ -24,7 +24,7 @@
 namespace gptq {
 
 constexpr int kGT = 128;          // tile edge
-constexpr int kGK = 64;           // k per chunk: loaded into registers one chunk ahead
+constexpr int kGK = 32;           // k per chunk: loaded into registers one chunk ahead
 constexpr int kGP = kGT + 4;      // LDS pitch (floats)
 constexpr int kGemmMaxGroup = 32;
 
@@ -74,18 +74,19 @@ GPTQ_DEV float4 load4(const float* p, int lim) {
   return r;
 }
 
-// One chunk of 64 k: A chunk 128 (m) x 64 (k), B chunk 64 (k) x 128 (n); each
-// thread holds 8 float4 of each.
+// One chunk of kGK = 32 k: A chunk 128 (m) x 32 (k), B chunk 32 (k) x 128 (n);
+// each thread holds 4 float4 of each.
+constexpr int kGL = kGK * kGT / 1024;   // float4 per thread per operand chunk
 template <bool A_KMAJOR, bool VEC>
 GPTQ_DEV void gemm_gload(const GemmProblem& P, int m0, int n0, int k0, int khi, int tid,
-                         float4 (&ra)[8], float4 (&rb)[8]) {
+                         float4 (&ra)[kGL], float4 (&rb)[kGL]) {
   // B (and k-major A): row k = k0 + tid/32 + 8i, columns c = 4*(tid%32) .. +3
   const int c4 = 4 * (tid & 31);
   if (VEC && A_KMAJOR && m0 + kGT <= P.M && n0 + kGT <= P.N && k0 + kGK <= khi) {
     // a chunk inside every bound (the common case; the test is uniform over
     // the workgroup): no per-lane limits, so no branches around the loads
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kGL; ++i) {
       const int k = k0 + (tid >> 5) + 8 * i;
       rb[i] = *reinterpret_cast<const float4*>(P.B + (size_t)k * P.ldb + n0 + c4);
       ra[i] = *reinterpret_cast<const float4*>(P.A + (size_t)k * P.lda + m0 + c4);
@@ -93,7 +94,7 @@ GPTQ_DEV void gemm_gload(const GemmProblem& P, int m0, int n0, int k0, int khi, 
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kGL; ++i) {
     const int k = k0 + (tid >> 5) + 8 * i;
     const bool kv = k < khi;
     rb[i] = kv ? load4<VEC>(P.B + (size_t)k * P.ldb + n0 + c4, P.N - n0 - c4)
@@ -103,11 +104,11 @@ GPTQ_DEV void gemm_gload(const GemmProblem& P, int m0, int n0, int k0, int khi, 
                  : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (!A_KMAJOR) {
-    // m-major A: row m = m0 + tid/16 + 16i, k = k0 + 4*(tid%16) .. +3
-    const int kq = k0 + 4 * (tid & 15);
+    // m-major A: row m = m0 + tid/8 + 32i, k = k0 + 4*(tid%8) .. +3
+    const int kq = k0 + 4 * (tid & 7);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + (tid >> 4) + 16 * i;
+    for (int i = 0; i < kGL; ++i) {
+      const int m = m0 + (tid >> 3) + 32 * i;
       ra[i] = (m < P.M) ? load4<VEC>(P.A + (size_t)m * P.lda + kq, khi - kq)
                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -115,19 +116,19 @@ GPTQ_DEV void gemm_gload(const GemmProblem& P, int m0, int n0, int k0, int khi, 
 }
 
 template <bool A_KMAJOR>
-GPTQ_DEV void gemm_lstore(float* sA, float* sB, int tid, const float4 (&ra)[8], const float4 (&rb)[8]) {
+GPTQ_DEV void gemm_lstore(float* sA, float* sB, int tid, const float4 (&ra)[kGL], const float4 (&rb)[kGL]) {
   const int c4 = 4 * (tid & 31);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kGL; ++i) {
     const int kr = (tid >> 5) + 8 * i;
     *reinterpret_cast<float4*>(sB + kr * kGP + c4) = rb[i];
     if (A_KMAJOR) *reinterpret_cast<float4*>(sA + kr * kGP + c4) = ra[i];
   }
   if (!A_KMAJOR) {
-    const int kq = 4 * (tid & 15);
+    const int kq = 4 * (tid & 7);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int mr = (tid >> 4) + 16 * i;
+    for (int i = 0; i < kGL; ++i) {
+      const int mr = (tid >> 3) + 32 * i;
       sA[(kq + 0) * kGP + mr] = ra[i].x;
       sA[(kq + 1) * kGP + mr] = ra[i].y;
       sA[(kq + 2) * kGP + mr] = ra[i].z;
@@ -137,7 +138,7 @@ GPTQ_DEV void gemm_lstore(float* sA, float* sB, int tid, const float4 (&ra)[8], 
 }
 
 // One 128x128 tile, four waves (2x2) of 64x64: acc += Aop[m0.., klo:khi] * Bop[klo:khi, n0..],
-// k in chunks of 64 staged through sA, sB (kGK x kGP floats each); the next
+// k in chunks of kGK staged through sA, sB (kGK x kGP floats each); the next
 // chunk is loaded into registers while the current one is multiplied.
 template <bool A_KMAJOR, bool VEC>
 GPTQ_DEV void gemm_tile_contract(const GemmProblem& P, int m0, int n0, int klo, int khi, float* sA, float* sB,
@@ -145,7 +146,7 @@ GPTQ_DEV void gemm_tile_contract(const GemmProblem& P, int m0, int n0, int klo, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   if (klo >= khi) return;
-  float4 ra[8], rb[8];
+  float4 ra[kGL], rb[kGL];
   gemm_gload<A_KMAJOR, VEC>(P, m0, n0, klo, khi, tid, ra, rb);
   for (int k0 = klo; k0 < khi; k0 += kGK) {
     __syncthreads();                         // the previous chunk is consumed
@@ -166,61 +167,48 @@ GPTQ_DEV void gemm_tile_contract(const GemmProblem& P, int m0, int n0, int klo, 
   }
 }
 
-// The tile's old C values in the MFMA register layout (0 outside C).
-GPTQ_DEV void gemm_tile_load_c(const GemmProblem& P, int m0, int n0, float (&cold)[2][2][16]) {
+// C = alpha * acc + beta * C over the tile (beta == 0: alpha * acc, C not
+// read), after the contraction: the old values of one half of a wave's
+// 64 x 64 block (32 per thread) are read in one batch, then that half is
+// written.  Holding C through the contraction cost registers (the tile runs
+// three workgroups per CU), and its loads queued ahead of the first
+// operand chunk's; the other workgroups on the CU cover this batch's latency.
+GPTQ_DEV void gemm_tile_update(const GemmProblem& P, int m0, int n0, float alpha, float beta,
+                               f32x16_t (&acc)[2][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    float cold[2][16];
+    if (beta != 0.0f) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
+          const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
+          cold[j][r] = (m < P.M && n < P.N) ? P.C[(size_t)m * P.ldc + n] : 0.0f;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
         const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
-        cold[i][j][r] = (m < P.M && n < P.N) ? P.C[(size_t)m * P.ldc + n] : 0.0f;
+        const float v = (beta != 0.0f) ? alpha * acc[i][j][r] + beta * cold[j][r] : alpha * acc[i][j][r];
+        if (m < P.M && n < P.N) P.C[(size_t)m * P.ldc + n] = v;
       }
-}
-
-// C = alpha * acc + beta * cold over the tile (beta == 0: alpha * acc).
-GPTQ_DEV void gemm_tile_store(const GemmProblem& P, int m0, int n0, float alpha, float beta,
-                              f32x16_t (&acc)[2][2], const float (&cold)[2][2][16]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  if (beta != 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = alpha * acc[i][j][r] + beta * cold[i][j][r];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] *= alpha;
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + mfma32_row(r, lane);
-        const int n = n0 + wn * 64 + j * 32 + mfma32_col(lane);
-        if (m < P.M && n < P.N) P.C[(size_t)m * P.ldc + n] = acc[i][j][r];
-      }
 }
 
 // kPartial (split-K): workgroup w takes part w % parts of tile w / parts, i.e.
-// the part's share of the tile's contraction range (cut in multiples of 64),
+// the part's share of the tile's contraction range (cut in multiples of kGK),
 // and writes its raw 128x128 sum to partial (float*) in MFMA register order,
 // [tile*parts + part][wave 4][block 4][reg 16][lane 64]; gemm_splitk_reduce
 // adds the parts in order.
 template <bool A_KMAJOR, int EPI, bool VEC>
-__global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float alpha, float beta,
+__global__ __launch_bounds__(256, 3) void gemm_f32_kernel(GemmGroup grp, float alpha, float beta,
                                                           int kloFromM, int khiFromN, int upperOnly,
                                                           double* __restrict__ dot_out, int parts = 1) {
   __shared__ __attribute__((aligned(16))) float sA[kGK * kGP];
@@ -268,13 +256,6 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
 
   if (!skip) gemm_tile_contract<A_KMAJOR, VEC>(P, m0, n0, klo, khi, sA, sB, acc);
 
-  // C's old values are read after the contraction, all 64 per thread in one
-  // batch: read first, they held 64 registers through the contraction and
-  // their loads queued ahead of the first operand chunk's (the other
-  // workgroup on the CU covers this batch's latency)
-  float cold[2][2][16];
-  if (EPI == kStore && !skip && beta != 0.0f) gemm_tile_load_c(P, m0, n0, cold);
-
   if (EPI == kPartial) {
     float* out = reinterpret_cast<float*>(dot_out) + ((size_t)blockIdx.x * 4 + wave) * (4 * 16 * 64);
 #pragma unroll
@@ -287,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmGroup grp, float a
   }
   if (EPI == kStore) {
     if (skip) return;
-    gemm_tile_store(P, m0, n0, alpha, beta, acc, cold);
+    gemm_tile_update(P, m0, n0, alpha, beta, acc);
   } else {
     double s = 0.0;
 #pragma unroll
@@ -350,12 +331,13 @@ static __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmGroup grp, 
 // (the diagonal 128-blocks are computed whole).
 constexpr int kST = 64;            // small tile edge
 constexpr int kSP = kST + 4;       // LDS pitch (floats)
+constexpr int kSK = 64;            // k per chunk
 
 template <bool A_KMAJOR, bool VEC>
 __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmGroup grp, float alpha, float beta,
                                                              int kloFromM, int khiFromN, int upperOnly) {
-  __shared__ __attribute__((aligned(16))) float sA[kGK * kSP];
-  __shared__ __attribute__((aligned(16))) float sB[kGK * kSP];
+  __shared__ __attribute__((aligned(16))) float sA[kSK * kSP];
+  __shared__ __attribute__((aligned(16))) float sB[kSK * kSP];
   const int wg = (int)blockIdx.x;
   int pi = 0;
   while (pi + 1 < grp.count && grp.tile_start[pi + 1] <= wg) ++pi;
@@ -415,7 +397,7 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmGroup grp, floa
   if (klo < khi) {
     float4 ra[4], rb[4];
     gload(klo, ra, rb);
-    for (int k0 = klo; k0 < khi; k0 += kGK) {
+    for (int k0 = klo; k0 < khi; k0 += kSK) {
       __syncthreads();
       {
         const int c4 = 4 * (tid & 15);
@@ -434,8 +416,8 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmGroup grp, floa
         }
       }
       __syncthreads();
-      if (k0 + kGK < khi) gload(k0 + kGK, ra, rb);
-      const int kn = min(kGK, khi - k0);       // zero-filled beyond khi: keep even steps
+      if (k0 + kSK < khi) gload(k0 + kSK, ra, rb);
+      const int kn = min(kSK, khi - k0);       // zero-filled beyond khi: keep even steps
 #pragma unroll 4
       for (int k2 = 0; k2 < kn; k2 += 2) {
         const int row = (k2 + (lane >> 5)) * kSP + (lane & 31);

@@ -450,9 +450,7 @@ GPTQ_DEV void trail_tile(float* A, int np, int k, const TrailArgs& t, int local,
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   gemm_tile_contract<true, true>(P, m0, n0, 0, t.K, sA, sB, acc);
-  float cold[2][2][16];
-  gemm_tile_load_c(P, m0, n0, cold);
-  gemm_tile_store(P, m0, n0, -1.0f, 1.0f, acc, cold);
+  gemm_tile_update(P, m0, n0, -1.0f, 1.0f, acc);
 }
 
 __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A, int np, int k,

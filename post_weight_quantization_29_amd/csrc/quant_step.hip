@@ -127,9 +127,7 @@ __global__ __launch_bounds__(256, 2) void quant_step_kernel(StepArgs f) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   gemm_tile_contract<true, true>(P, m0, n0, 0, P.K, sA, sB, acc);
-  float cold[2][2][16];
-  gemm_tile_load_c(P, m0, n0, cold);
-  gemm_tile_store(P, m0, n0, -1.0f, 1.0f, acc, cold);
+  gemm_tile_update(P, m0, n0, -1.0f, 1.0f, acc);
 }
 
 void launch_quant_step(const StepArgs& f, int gt, hipStream_t s) {
