@@ -261,8 +261,23 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
       st.Wrest = Wp + b1 + bw1;
       st.Urest = U + (size_t)k0 * d + b1 + bw1;
       st.rest = std::max(0, (s_end ? d : super_end(b)) - (b1 + bw1));
+      // At a super-block's end (gb > 1) the update of the columns after the
+      // next super-block is a plain GEMM of K = 128 gb: it runs as a launch of
+      // its own, four tiles per CU instead of the fused kernel's two.
+      int tail = 0;
+      if (s_end && gb > 1) {
+        const int c_split = super_end(b + 1);
+        tail = std::max(0, d - std::max(c_split, b1 + bw1));
+        st.rest -= tail;
+      }
       launch_quant_step(st, gt, s);
       GPTQ_LAUNCH_CHECK();
+      if (tail > 0) {
+        const int c = d - tail;
+        gemm_f32<true>(st.Eprev, d_out, U + (size_t)k0 * d + c, d, Wp + c, d, d_out, tail, st.kprev,
+                       -1.0f, 1.0f, 0, 0, 0, s);
+        GPTQ_LAUNCH_CHECK();
+      }
     }
     return GPTQ_OK;
   }
