@@ -137,7 +137,7 @@ constexpr int kGatherRow = 32768;
 __global__ __launch_bounds__(1024) void gather_flip_row_kernel(const float* __restrict__ H, int n, int np,
                                                               const int* __restrict__ perm,
                                                               const double* __restrict__ lam,
-                                                              float* __restrict__ A) {
+                                                              float* __restrict__ A, int vec) {
   __shared__ float row[kGatherRow];
   const int a = blockIdx.x;
   float* out = A + (size_t)a * np;
@@ -146,9 +146,41 @@ __global__ __launch_bounds__(1024) void gather_flip_row_kernel(const float* __re
     return;
   }
   const float* src = H + (size_t)perm[n - 1 - a] * n;
+  const float l = (float)lam[0];
+  if (vec) {
+    // 16-byte loads and stores, every one of a thread's loads issued at once
+    // (vec: n is a multiple of 4 and H and perm are 16-byte aligned, so every
+    // row and every group of four perm entries is; np is a multiple of 128)
+    constexpr int kU = kGatherRow / 4 / 1024;
+    float4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = 4 * (threadIdx.x + 1024 * u);
+      if (c < n) v[u] = *reinterpret_cast<const float4*>(src + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = 4 * (threadIdx.x + 1024 * u);
+      if (c < n) *reinterpret_cast<float4*>(row + c) = v[u];
+    }
+    __syncthreads();
+    for (int b = 4 * threadIdx.x; b < np; b += 4096) {
+      float4 o;
+      if (b < n) {
+        // perm[n-1-b-3 .. n-1-b]: one aligned 16-byte load, in reverse order
+        const int4 q = *reinterpret_cast<const int4*>(perm + (n - 4 - b));
+        o = make_float4(row[q.w], row[q.z], row[q.y], row[q.x]);
+        if (a >= b && a < b + 4) (&o.x)[a - b] += l;
+      } else {
+        o = make_float4(a == b ? 1.0f : 0.0f, a == b + 1 ? 1.0f : 0.0f, a == b + 2 ? 1.0f : 0.0f,
+                        a == b + 3 ? 1.0f : 0.0f);
+      }
+      *reinterpret_cast<float4*>(out + b) = o;
+    }
+    return;
+  }
   for (int c = threadIdx.x; c < n; c += 1024) row[c] = src[c];
   __syncthreads();
-  const float l = (float)lam[0];
   for (int b = threadIdx.x; b < np; b += 1024) {
     float v;
     if (b < n) {
@@ -710,7 +742,9 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
     act_order_kernel<<<(n + 255) / 256, 256, 0, s>>>(H, hdiag, n, desc_act, perm);
   GPTQ_LAUNCH_CHECK();
   if (n <= kGatherRow)
-    gather_flip_row_kernel<<<np, 1024, 0, s>>>(H, n, np, perm, lam, A);
+    gather_flip_row_kernel<<<np, 1024, 0, s>>>(H, n, np, perm, lam, A,
+                                               (n % 4 == 0) && (reinterpret_cast<uintptr_t>(H) % 16 == 0) &&
+                                                   (reinterpret_cast<uintptr_t>(perm) % 16 == 0));
   else
     gather_flip_kernel<<<dim3((np + 255) / 256, np), 256, 0, s>>>(H, n, np, perm, lam, A);
   GPTQ_LAUNCH_CHECK();

@@ -43,9 +43,68 @@ constexpr int kGatherW = 32768;
 __global__ __launch_bounds__(1024) void gather_w_row_kernel(const void* __restrict__ W, gptq_dtype wt,
                                                            int d_out, int d, const int* __restrict__ perm,
                                                            int G, float* __restrict__ Wp,
-                                                           int* __restrict__ g_idx) {
+                                                           int* __restrict__ g_idx, int vec) {
   __shared__ float row[kGatherW];
   const int r = blockIdx.x;
+  if (vec) {
+    // 16-byte accesses (vec: d % 8 == 0 and W, perm 16-byte aligned), 8
+    // elements per load, every one of a thread's loads issued at once
+    constexpr int kU = kGatherW / 8 / 1024;
+    uint4 v[kU];
+    const char* wr = static_cast<const char*>(W) + (size_t)r * d * (wt == GPTQ_F32 ? 4 : 2);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = 8 * (threadIdx.x + 1024 * u);
+      if (c < d) {
+        if (wt == GPTQ_F32) {
+          v[u] = *reinterpret_cast<const uint4*>(wr + 4 * (size_t)c);       // elements c .. c+3
+        } else {
+          v[u] = *reinterpret_cast<const uint4*>(wr + 2 * (size_t)c);       // elements c .. c+7
+        }
+      }
+    }
+    if (wt == GPTQ_F32) {
+      // the fp32 row needs twice the loads: the second half of each 8-element chunk
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = 8 * (threadIdx.x + 1024 * u);
+        if (c < d) {
+          const uint4 w2 = *reinterpret_cast<const uint4*>(wr + 4 * (size_t)(c + 4));
+          *reinterpret_cast<uint4*>(row + c) = v[u];
+          *reinterpret_cast<uint4*>(row + c + 4) = w2;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = 8 * (threadIdx.x + 1024 * u);
+        if (c < d) {
+          const uint32_t q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t h = (uint16_t)((e & 1) ? (q[e >> 1] >> 16) : (q[e >> 1] & 0xFFFFu));
+            f[e] = (wt == GPTQ_F16) ? (float)__builtin_bit_cast(_Float16, h)
+                                    : __builtin_bit_cast(float, (uint32_t)h << 16);
+          }
+          *reinterpret_cast<float4*>(row + c) = make_float4(f[0], f[1], f[2], f[3]);
+          *reinterpret_cast<float4*>(row + c + 4) = make_float4(f[4], f[5], f[6], f[7]);
+        }
+      }
+    }
+    __syncthreads();
+    for (int j = 4 * threadIdx.x; j < d; j += 4096) {
+      const int4 q = *reinterpret_cast<const int4*>(perm + j);
+      if (r == 0) {
+        g_idx[q.x] = j / G;
+        g_idx[q.y] = (j + 1) / G;
+        g_idx[q.z] = (j + 2) / G;
+        g_idx[q.w] = (j + 3) / G;
+      }
+      *reinterpret_cast<float4*>(Wp + (size_t)r * d + j) = make_float4(row[q.x], row[q.y], row[q.z], row[q.w]);
+    }
+    return;
+  }
   for (int c = threadIdx.x; c < d; c += 1024) row[c] = load_as_float(W, wt, (size_t)r * d + c);
   __syncthreads();
   for (int j = threadIdx.x; j < d; j += 1024) {
@@ -206,7 +265,9 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   double* gscale = reinterpret_cast<double*>(base + L.off_gscale);
 
   if (d <= kGatherW)
-    gather_w_row_kernel<<<d_out, 1024, 0, s>>>(W, w_dtype, d_out, d, perm, G, Wp, g_idx);
+    gather_w_row_kernel<<<d_out, 1024, 0, s>>>(W, w_dtype, d_out, d, perm, G, Wp, g_idx,
+                                               (d % 8 == 0) && (reinterpret_cast<uintptr_t>(W) % 16 == 0) &&
+                                                   (reinterpret_cast<uintptr_t>(perm) % 16 == 0));
   else
     gather_w_kernel<<<dim3((d + 255) / 256, std::min(d_out, 1024)), 256, 0, s>>>(W, w_dtype, d_out, d,
                                                                                 perm, G, Wp, g_idx);

@@ -229,6 +229,32 @@ def test_gptq_layer_parity(case):
         assert np.array_equal(pk, o.pack_int4(codes))
 
 
+def test_gptq_ragged_width_parity():
+    """d_in not a multiple of 8 (the Hessian call needs one, so H is given in
+    fp32 here): the order, the permuting gathers' element-wise paths and a
+    ragged last block, one group per row, desc_act."""
+    import post_weight_quantization_29_amd as P
+    d_out, d_in = 50, 333
+    say(f"[gptq ragged] {d_out}x{d_in}")
+    c = gi.random_case(d_out, d_in, 2000, seed=333, outlier_frac=0.02, outlier_factor=20.0)
+    W64 = gi.to_float64(c.W, "f32")
+    H32 = o.hessian([gi.to_float64(c.X, "f32")], d_in).astype(np.float32)
+    H64 = H32.astype(np.float64)
+    ref = o.gptq(W64, H64, bits=4, group_size=-1, block_size=128, damp_percent=0.01, desc_act=True)
+    cfg = P.make_config(bits=4, group_size=-1, block_size=128, damp_percent=0.01, desc_act=1)
+    res = P.quantize_layer_outputs(to_dev(c.W, "f32"), to_dev(H32, "f32"), cfg, pack=False)
+    torch.cuda.synchronize()
+    codes = res.codes.cpu().numpy()
+    par = compare_quant(ref, W64, H64, codes, res.scales.cpu().numpy(), res.zeros.cpu().numpy(),
+                        res.Q.cpu().numpy(), d_in, tie_tol=1e-3)
+    say(f"  {par}")
+    assert np.array_equal(res.perm.cpu().numpy(), ref.perm)
+    assert np.array_equal(res.g_idx.cpu().numpy(), ref.g_idx)
+    assert par.agree >= 0.999 and par.first_not_tie == 0
+    assert par.scale_rel <= 1e-3 and par.zero_mismatch == 0 and par.q_bad == 0
+    assert par.obj_rel <= 1e-3
+
+
 @pytest.mark.parametrize("case", [CASES[1], CASES[4]], ids=["100x384_t", "96x640_g256_t"])
 def test_gptq_layer_parity_without_keys(case):
     # desc_act = 0 needs no fp64 diagonal: damping then takes mean(diag H) from H
