@@ -329,9 +329,10 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     // has finished the earlier slices of stage k-1 (so stage k-2's slot is
     // free and receives stage k + kSlots16 - 2).  The last slice of a stage
     // then overlaps its MFMAs with the reads of the next stage's first slice
-    // and with the next copies.
+    // and with the next copies, issued one every second MFMA (in a burst
+    // they filled the address unit's queue and held the MFMA stream up).
     constexpr int kInFlight = kSlots16 - 3;        // later stages still in flight at a sync point
-    static_assert(kSlots16 >= 3 && NKS % 2 == 0, "ring layout");
+    static_assert(kSlots16 >= 3 && NKS % 2 == 0 && 2 * NI == 8, "ring layout: 8 copies over a slice's 16 MFMAs");
 #pragma unroll
     for (int a = 0; a <= kSlots16 - 3; ++a) {
       const i32x4_t r0 = stage_rsrc(ks0 + a);
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
                                      (uint32_t)(ks + 1) * kSliceBytes + h * 2048u);
           else
             op[nxt][f][h] = tr_at<T>((f < 4 ? nA + offA[f] : nB + offB[f - 4]) + h * 2048u);
-          if (last && n < 2 * NI) dma(rn, DSLOT, n);
+          if (last && (n & 1) == 0) dma(rn, DSLOT, n >> 1);   // a copy every second MFMA
           __builtin_amdgcn_sched_barrier(0);
         }
       }
