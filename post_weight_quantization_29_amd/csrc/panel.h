@@ -109,23 +109,35 @@ struct PanelArgs {
 // compile-time indices.  GT > 0: groups of GT columns inside the block (group
 // starts known at compile time); GT == 0: groups of G >= 128 columns, which
 // can only start at the block's first column.
-// The column loop of the 16 rows of row block rb.  LDS: sU4 (kQB x kQS/4 x
-// kQL float4), sInv (kQB doubles), sPerm (kQB ints).  PRE: the caller has put
-// into sPre[r][c] (pitch kQB + 4) the product the block's columns still owe
-// the previous block's update, (Err_prev * U[prev, block])[row r][column c],
-// computed like the trailing GEMM computes it; the running weights then start
-// from the work copy minus it, rounded to fp32 as the GEMM would store it.
+// U's diagonal block in LDS, strict upper part, as float4 slot groups: lane q
+// of row j reads U[b0+j][b0+16t+q] for slots t = 4g .. 4g+3 of group g.  Row j
+// only needs the slots t >= j/16, so group 0 (columns < 64) is kept for rows
+// j < 64 alone: group 1 of every row at [j][q], then group 0 of rows < 64 at
+// kQB*kQL + [j][q] (48 KB instead of 64).
+constexpr int kUPacked = (kQB + kQB / 2) * kQL;   // float4s
+static_assert(kQS == 8, "two float4 slot groups per lane and row");
+GPTQ_DEV int upk(int j, int g, int q) { return (g ? 0 : kQB * kQL) + j * kQL + q; }
+
+// The column loop of the 16 rows of row block rb.  LDS: sU (kUPacked float4),
+// sInv (kQB doubles), sPerm (kQB ints).  PRE: the caller has put into
+// sPre[r][c] (pitch kQB + 4) the product the block's columns still owe the
+// previous block's update, (Err_prev * U[prev, block])[row r][column c],
+// computed like the trailing GEMM computes it, followed by a barrier; the
+// running weights then start from the work copy minus it, rounded to fp32 as
+// the GEMM would store it.  sPre may share LDS with sU: it is read before sU
+// is written.
 template <int GT, bool PRE>
-GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4 (*sU4)[kQS / 4][kQL], double* sInv, int* sPerm,
+GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4* sU4, double* sInv, int* sPerm,
                          const float* sPre) {
   const int tid = threadIdx.x;
-  float* sU = reinterpret_cast<float*>(&sU4[0][0][0]);
+  float* sU = reinterpret_cast<float*>(sU4);
   // U's diagonal block, strict upper part (zero on and below the diagonal):
-  // 16 float4 loads in flight per thread
+  // 16 float4 loads in flight per thread, written to LDS once the running
+  // weights are set up
+  // 16-byte loads when every U row starts 16-byte aligned
+  const bool vec = (a.d % 4 == 0) && (reinterpret_cast<uintptr_t>(a.U) % 16 == 0);
+  float4 v[16];
   {
-    // 16-byte loads when every U row starts 16-byte aligned
-    const bool vec = (a.d % 4 == 0) && (reinterpret_cast<uintptr_t>(a.U) % 16 == 0);
-    float4 v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int e = u * 256 + tid;              // float4 index: row j, columns 4m .. 4m+3
@@ -143,24 +155,11 @@ GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4 (*sU4)[kQS / 4][kQL]
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = u * 256 + tid;
-      const int j = e >> 5, c = 4 * (e & 31);
-      const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int cc = c + k;
-        const int t = cc >> 4;
-        sU[((j * (kQS / 4) + (t >> 2)) * kQL + (cc & 15)) * 4 + (t & 3)] = (cc > j) ? vv[k] : 0.0f;
-      }
-    }
   }
   for (int j = tid; j < kQB; j += 256) {
     sInv[j] = (j < a.bw) ? 1.0 / (double)a.U[(size_t)(a.b0 + j) * a.d + a.b0 + j] : 0.0;
     sPerm[j] = (j < a.bw) ? a.perm[a.b0 + j] : 0;
   }
-  __syncthreads();
 
   const int q = tid & 15;
   const int row = rb * kQRows + (tid >> 4);
@@ -174,10 +173,24 @@ GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4 (*sU4)[kQS / 4][kQL]
   double w[kQS];
 #pragma unroll
   for (int t = 0; t < kQS; ++t) {
-    float v = (kQL * t + q < bw) ? wrow[kQL * t + q] : 0.0f;
-    if constexpr (PRE) v = v - sPre[(tid >> 4) * (kQB + 4) + kQL * t + q];
-    w[t] = (double)v;
+    float x = (kQL * t + q < bw) ? wrow[kQL * t + q] : 0.0f;
+    if constexpr (PRE) x = x - sPre[(tid >> 4) * (kQB + 4) + kQL * t + q];
+    w[t] = (double)x;
   }
+  if constexpr (PRE) __syncthreads();        // sPre is read: sU may overwrite it
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = u * 256 + tid;
+    const int j = e >> 5, c = 4 * (e & 31);
+    const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int cc = c + k;
+      const int t = cc >> 4;
+      if ((t >> 2) == 1 || j < kQB / 2) sU[upk(j, t >> 2, cc & 15) * 4 + (t & 3)] = (cc > j) ? vv[k] : 0.0f;
+    }
+  }
+  __syncthreads();
 
   // the grid and every integer decision are taken in fp64, like the rest of
   // the column loop
@@ -280,7 +293,7 @@ GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4 (*sU4)[kQS / 4][kQL]
     // entries at columns <= J are retired, and U is zero there)
 #pragma unroll
     for (int t = (I & ~3); t < kQS; t += 4) {
-      const float4 u4 = sU4[J][t >> 2][q];
+      const float4 u4 = sU4[upk(J, t >> 2, q)];        // group 0 only while J < 64
       if (t + 0 >= I) w[t + 0] = fma(-e, (double)u4.x, w[t + 0]);
       if (t + 1 >= I) w[t + 1] = fma(-e, (double)u4.y, w[t + 1]);
       if (t + 2 >= I) w[t + 2] = fma(-e, (double)u4.z, w[t + 2]);
@@ -308,7 +321,7 @@ GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4 (*sU4)[kQS / 4][kQL]
 
 template <int GT>
 __global__ __launch_bounds__(256) void panel_kernel(PanelArgs a) {
-  __shared__ float4 sU4[kQB][kQS / 4][kQL];   // sU4[j][t/4][q] = U[b0+j][b0+16t+q], t..t+3
+  __shared__ float4 sU4[kUPacked];            // U's diagonal block (see upk)
   __shared__ double sInv[kQB];
   __shared__ int sPerm[kQB];
   panel_rows<GT, false>(a, (int)blockIdx.x, sU4, sInv, sPerm, nullptr);

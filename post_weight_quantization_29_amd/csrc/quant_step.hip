@@ -29,47 +29,53 @@
 namespace gptq {
 
 constexpr int kPreP = kQB + 4;                             // pitch of the product rows (floats)
-constexpr size_t kStepU = (size_t)kQB * kQB * 4;           // U tile / sU4 (64 KB)
+constexpr int kPK = 64;                                    // k per staged chunk of the products
+// LDS: [0, kStepU) the packed U block of the column loop; before it, the
+// products' staging (a U chunk [kPK][kQB] and Err rows [kPK][16]) and then
+// the products themselves [16][kPreP], read before the U block is written
+constexpr size_t kStepU = (size_t)kUPacked * 16;           // 48 KB
+constexpr size_t kStepStageE = (size_t)kPK * kQB * 4;      // Err rows after the U chunk
 constexpr size_t kStepInv = kStepU;                        // sInv: kQB doubles
 constexpr size_t kStepPerm = kStepInv + kQB * 8;           // sPerm: kQB ints
-constexpr size_t kStepE = kStepPerm + kQB * 4;             // Err rows [kQB][16], later the products [16][kPreP]
-constexpr size_t kStepLds = kStepE + (size_t)kQRows * kPreP * 4;
-static_assert((size_t)kQB * kQRows * 4 <= (size_t)kQRows * kPreP * 4, "Err rows fit the product area");
+constexpr size_t kStepLds = kStepPerm + kQB * 4;
+static_assert(kStepStageE + (size_t)kPK * kQRows * 4 <= kStepU, "the products' staging fits the U area");
+static_assert((size_t)kQRows * kPreP * 4 <= kStepU, "the products fit the U area");
 static_assert(kStepLds >= 2 * (size_t)kGK * kGP * 4, "the GEMM tile's staging fits");
-static_assert(2 * kStepLds <= 160 * 1024, "two workgroups per CU");
+static_assert(3 * kStepLds <= 160 * 1024, "three workgroups per CU");
 
 // products P[r][c] = sum_k Eprev[k][row0 + r] * Uprev[k][c], r < 16, c < 128,
-// k < kprev (128 per block whose update is still owed), in chunks of 128 k
+// k < kprev (128 per block whose update is still owed), in chunks of kPK k
 // staged through LDS; the k order is the trailing GEMM tile's
 GPTQ_DEV void step_products(const StepArgs& f, int row0, char* lds) {
   const PanelArgs& a = f.pa;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* sE = reinterpret_cast<float*>(lds + kStepE);      // [k][16]
+  float* sE = reinterpret_cast<float*>(lds + kStepStageE);  // [k][16]
   float* sUb = reinterpret_cast<float*>(lds);              // [k][kQB]
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
   const int m = lane & 31, kh = lane >> 5;
-  for (int kc = 0; kc < f.kprev; kc += kQB) {
+  for (int kc = 0; kc < f.kprev; kc += kPK) {
     const float* E = f.Eprev + (size_t)kc * a.d_out;
     const float* Ub = f.Uprev + (size_t)kc * a.d;
     // Err rows: k = tid/16 + 16u, row row0 + tid%16 (16 consecutive floats per k)
     {
       const int i = tid & 15, r = row0 + i;
-      float e[8];
+      float e[kPK / 16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kPK / 16; ++u) {
         const int k = (tid >> 4) + 16 * u;
         e[u] = (r < a.d_out) ? E[(size_t)k * a.d_out + r] : 0.0f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sE[((tid >> 4) + 16 * u) * kQRows + i] = e[u];
+      for (int u = 0; u < kPK / 16; ++u) sE[((tid >> 4) + 16 * u) * kQRows + i] = e[u];
     }
-    // U tile: rows kc + k of the owed blocks, columns c < bw of this block (zero beyond)
+    // U chunk: rows kc + k of the owed blocks, columns c < bw of this block (zero beyond)
     {
-      float4 v[16];
+      constexpr int NU = kPK * kQB / 4 / 256;
+      float4 v[NU];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < NU; ++u) {
         const int e = u * 256 + tid, k = e >> 5, c = 4 * (e & 31);
         v[u] = (c + 3 < a.bw) ? *reinterpret_cast<const float4*>(Ub + (size_t)k * a.d + c)
                               : make_float4(c + 0 < a.bw ? Ub[(size_t)k * a.d + c + 0] : 0.0f,
@@ -77,7 +83,7 @@ GPTQ_DEV void step_products(const StepArgs& f, int row0, char* lds) {
                                             c + 2 < a.bw ? Ub[(size_t)k * a.d + c + 2] : 0.0f, 0.0f);
       }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < NU; ++u) {
         const int e = u * 256 + tid;
         reinterpret_cast<float4*>(sUb)[e] = v[u];
       }
@@ -85,32 +91,32 @@ GPTQ_DEV void step_products(const StepArgs& f, int row0, char* lds) {
     __syncthreads();
     // wave w: rows 0..31 (16..31 zero) x columns 32w .. 32w+31, k in pairs
 #pragma unroll 8
-    for (int k2 = 0; k2 < kQB; k2 += 2) {
+    for (int k2 = 0; k2 < kPK; k2 += 2) {
       const float av = (m < kQRows) ? sE[(k2 + kh) * kQRows + m] : 0.0f;
       const float bv = sUb[(k2 + kh) * kQB + 32 * wave + m];
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
     __syncthreads();                                       // sE and sUb are read
   }
-  float* sPre = reinterpret_cast<float*>(lds + kStepE);
+  float* sPre = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int rr = mfma32_row(r, lane);
     if (rr < kQRows) sPre[rr * kPreP + 32 * wave + mfma32_col(lane)] = acc[r];
   }
-  // the column loop's first barrier orders these stores before their reads
+  __syncthreads();                                         // the products are complete
 }
 
 template <int GT>
-__global__ __launch_bounds__(256, 2) void quant_step_kernel(StepArgs f) {
+__global__ __launch_bounds__(256, 3) void quant_step_kernel(StepArgs f) {
   __shared__ __attribute__((aligned(16))) char lds[kStepLds];
   const int npanel = (f.pa.d_out + kQRows - 1) / kQRows;
   const int wg = (int)blockIdx.x;
   if (wg < npanel) {
     step_products(f, wg * kQRows, lds);
-    panel_rows<GT, true>(f.pa, wg, reinterpret_cast<float4 (*)[kQS / 4][kQL]>(lds),
+    panel_rows<GT, true>(f.pa, wg, reinterpret_cast<float4*>(lds),
                          reinterpret_cast<double*>(lds + kStepInv), reinterpret_cast<int*>(lds + kStepPerm),
-                         reinterpret_cast<const float*>(lds + kStepE));
+                         reinterpret_cast<const float*>(lds));
     return;
   }
   // trailing tile: rows 128*(t / tn), columns 128*(t % tn) of the update's columns
