@@ -187,12 +187,17 @@ GPTQ_DEV void wait_vm0() { wait_vm<0>(); }
 // another, and each re-reads the panels it shares from memory (at 8192 x
 // 28672, 100x the activations' bytes per call).  Each workgroup therefore
 // publishes the stages it has done in its slot of its XCD's 64-slot row
-// (pace[x][c]) every four stages, and wave 0 waits while it is more than
-// kPaceLag stages ahead of the slowest workgroup of its XCD (finished ones
-// publish ~0u).  The wait is bounded (kPaceSpin polls); a workgroup whose
-// wait runs out stops pacing, so residency problems cost time, never a hang.
-// Only timing depends on it: every sum is the same.
+// (pace[x][c]) every kPaceEvery stage groups, and wave 0 then waits while it
+// is more than kPaceLag stages ahead of the slowest workgroup of its XCD
+// (finished ones publish ~0u).  A poll is rare because its load must be
+// waited for with every copy still in flight (the copies are issued by asm
+// the compiler cannot count), which drains the stage ring: polling every
+// group of five stages cost 14% of the call.  The wait is bounded
+// (kPaceSpin polls); a workgroup whose wait runs out stops pacing, so
+// residency problems cost time, never a hang.  Only timing depends on it:
+// every sum is the same.
 constexpr unsigned kPaceLag = 8;
+constexpr int kPaceEvery = 16;      // stage groups (of kSlots16 stages) between polls
 constexpr int kPaceSpin = 4096;
 constexpr int kPaceSlots = 64;
 
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     static_assert(kSlots16 == 5, "stage groups of five");
     int kk = ks0;                                  // stage kk uses slot (kk - ks0) % kSlots16
     for (; kk + 5 <= ks1; kk += 5) {
-      pace_at(done + (unsigned)(kk - ks0));
+      if (((kk - ks0) / kSlots16) % kPaceEvery == 0) pace_at(done + (unsigned)(kk - ks0));
       stage.template operator()<0>(kk);
       stage.template operator()<1>(kk + 1);
       stage.template operator()<2>(kk + 2);
