@@ -715,12 +715,9 @@ static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_d
   // 16-bit path: one resident workgroup per CU (256 CUs), persistent over items
   const unsigned pgrid = std::min<unsigned>(256u, items);
   const unsigned pg = (pgrid + kXCD - 1) / kXCD * kXCD;
-  // the fp64 diagonal only when it is asked for (the 16-bit kernels then do
-  // no diagonal work at all; H is the same either way)
-  // pacing pays where every workgroup streams all tokens of its tiles (one
-  // split: 262,144-token chains at 8192 x 28672, 4 % faster, 3.8x less
-  // traffic); with split token ranges the items are short and it does not
-  const bool pace_on = !f32 && p.splits == 1;
+  // pacing (rare polls) for every 16-bit plan: at 8192 x 28672 (one split)
+  // 197 -> 176 ms; with split token ranges 0-3 % (4096 .. 11008 columns)
+  const bool pace_on = !f32;
   if (pace_on) {
     zero_u32_kernel<<<1, 256, 0, s>>>(pace, kXCD * kPaceSlots);
     GPTQ_LAUNCH_CHECK();
