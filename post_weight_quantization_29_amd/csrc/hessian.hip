@@ -672,7 +672,7 @@ static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32, size_t max_ws = SIZ
   int smax = (int)std::max<int64_t>(1, std::min<int64_t>(64, p.nk / 16));
   // a scratch bound caps the split count (each split holds one partial per tile)
   const size_t per_split = (size_t)p.ntiles * p.tile * p.tile * sizeof(float) +
-                           (size_t)nt * p.tile * sizeof(double) + 2 * kAlign +
+                           (f32 ? (size_t)nt * p.tile * sizeof(double) : 0) + 2 * kAlign +
                            (size_t)kXCD * kPaceSlots * sizeof(unsigned);
   if (max_ws != SIZE_MAX) smax = std::max(1, std::min<int>(smax, (int)(max_ws / per_split)));
   for (int s = 1; s <= smax; ++s) {
@@ -684,7 +684,8 @@ static SyrkPlan syrk_plan(int64_t n_tokens, int d, bool f32, size_t max_ws = SIZ
   p.splits = (p.nk == 0) ? 1 : best_s;
   const size_t per_item = (size_t)p.tile * p.tile * sizeof(float);
   p.off_diag = align_up((size_t)p.splits * p.ntiles * per_item);
-  p.off_pace = align_up(p.off_diag + (size_t)p.splits * nt * p.tile * sizeof(double));
+  // fp64 diagonal partials: the fp32 kernel's (16-bit inputs sum x^2 in a pass of their own)
+  p.off_pace = align_up(p.off_diag + (f32 ? (size_t)p.splits * nt * p.tile * sizeof(double) : 0));
   p.off_sq = align_up(p.off_pace + (size_t)kXCD * kPaceSlots * sizeof(unsigned));
   p.sq_ws = f32 ? 0 : gptq_awq_sumsq_workspace_size(n_tokens, d);
   p.ws = align_up(p.off_sq + (f32 ? 0 : align_up((size_t)d * sizeof(double)) + p.sq_ws));
