@@ -165,7 +165,8 @@ int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_in, float d
  *          indexed by processing-order group; n_groups = ceil(d_in / G).
  *  g_idx   [d_in] int32 output: original column -> group.
  *  Q       [d_out x d_in] fp32 dequantized weights, original order; may be NULL.
- *  ws      scratch of gptq_quantize_workspace_size(d_out, d_in, cfg) bytes.
+ *  ws      scratch of gptq_quantize_workspace_size(d_out, d_in, cfg) bytes (cfg
+ *          NULL: a size that suffices for every configuration at this shape).
  *  d_out >= 1, d_in >= 1 (any width; packing needs d_in % 8 == 0). */
 size_t gptq_quantize_workspace_size(int32_t d_out, int32_t d_in, const gptq_config* cfg);
 int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_out, int32_t d_in,

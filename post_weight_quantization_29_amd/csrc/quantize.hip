@@ -232,7 +232,7 @@ static int check_config(const gptq_config* c, int d) {
 using namespace gptq;
 
 static int config_super_blocks(int d_out, int d, const gptq_config* cfg) {
-  if (!cfg) return 4;   // the largest layout
+  if (!cfg) return super_blocks(d_out, d, 1);   // the largest layout any configuration needs
   const int G = (cfg->group_size == -1) ? d : cfg->group_size;
   return super_blocks(d_out, d, G > 0 ? in_block_group(G) : 0);
 }

@@ -50,6 +50,13 @@ def test_workspace_queries(L):
     assert P.gptq_quantize_workspace_size(4096, 4096, cfg) >= 4096 * 4096 * 4
     assert P.gptq_layer_error_workspace_size(10, 16) > 0
     assert P.gptq_prepare_hinv_workspace_size(0) == 0
+    # a NULL configuration asks for a size that serves every configuration at
+    # the shape, including the super-block layout of work copies over 256 MB
+    f = L.gptq_quantize_workspace_size
+    for d_out, d_in in ((4096, 4096), (8192, 28672), (5120, 13824), (100, 333)):
+        any_cfg = f(d_out, d_in, None)
+        for G in (128, 64, 32, -1, 256):
+            assert any_cfg >= P.gptq_quantize_workspace_size(d_out, d_in, P.make_config(group_size=G)), (d_out, d_in, G)
 
 
 def test_argument_validation_before_any_launch(L):
