@@ -362,7 +362,7 @@ def test_quantize_is_deterministic():
     (256, 384, 32, 1, 3),      # groups inside the block, desc_act
     (64, 1024, 64, 0, 4),
     (4096, 4096, 128, 0, 4),   # the q_proj shape
-    (8192, 8320, 64, 1, 3),    # work copy over 256 MB: super-blocks of four blocks
+    (8192, 8320, 64, 1, 3),    # work copy over 256 MB: super-blocks of sixteen blocks, the last ragged
 ])
 def test_fused_block_steps_match_per_block(d_out, d, g, desc, bits):
     # the fused launches (next block's column loop beside the trailing update)
