@@ -10,6 +10,7 @@
 // partial tile in the MFMA register order, and a second kernel adds the
 // partials in a fixed order into H and mirrors off-diagonal tiles.
 #include "common.h"
+#include "split3.h"
 
 #include <mutex>
 
@@ -207,11 +208,30 @@ GPTQ_DEV unsigned wave_min_u32(unsigned v) {
   return v;
 }
 
-template <typename T, bool PACE>
+// Update mode (UPD): the same tile loop computes C[upper] -= P^T P for an fp32
+// panel P (K x n) given as bf16 planes h, m, l with P = h + m + l (each the
+// bf16 rounding of what the planes before it leave) and their negations.  X
+// is then plane h, the contraction runs over 6K virtual tokens, K per
+// segment, and segment (hh, hm, mh, hl, lh, mm) takes its A operand from the
+// negated plane and its B operand from the plane named: every product of two
+// pieces down to 2^-27 of |P_ki P_kj| is included, so each element gets about
+// the error of an fp32 product.  Tiles run as upper tiles (I <= J), the
+// accumulators start from C and end in C; the strictly lower 128-block of a
+// diagonal tile is left alone.  n is a multiple of 128, so a wave's 128 x 128
+// block is wholly inside C or wholly outside.
+struct Split3Args {
+  float* C;         // n x n, row pitch ldc
+  int ldc;
+  int kseg;         // K, a multiple of the 32-token stage
+  int64_t plane;    // elements from one plane to the next: h, m, l, -h, -m, -l
+};
+
+template <typename T, bool PACE, bool UPD>
 __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X, int64_t n_tokens,
                                                          int d, int nt, int ntiles, int splits,
                                                          int nk, float* __restrict__ partial,
-                                                         unsigned* __restrict__ pace) {
+                                                         unsigned* __restrict__ pace, Split3Args up) {
+  static_assert(!(UPD && PACE), "the update mode reads cached planes: no pacing");
   __shared__ __attribute__((aligned(16))) T sA[kSlots16][kStage16];
   __shared__ __attribute__((aligned(16))) T sB[kSlots16][kStage16];
   constexpr uint32_t kSlotBytes = kStage16 * 2;    // 16 KB
@@ -271,6 +291,11 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   I = __builtin_amdgcn_readfirstlane(I);
   J = __builtin_amdgcn_readfirstlane(J);
   const int w = s * ntiles + tri_index(I, J);     // partial slot
+  if (UPD) {
+    const int t = I;
+    I = J;
+    J = t;
+  }
   const int ks0 = __builtin_amdgcn_readfirstlane((int)((int64_t)nk * s / splits));
   const int ks1 = __builtin_amdgcn_readfirstlane((int)((int64_t)nk * (s + 1) / splits));
 
@@ -296,10 +321,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   }
   // buffer descriptor of stage kk (rows past the end, or kk outside this
   // split, read as zero)
-  auto stage_rsrc = [&](int kk) {
-    const int64_t t0 = (int64_t)kk * kK16;
-    const int64_t rows = (kk < ks1) ? min<int64_t>(kK16, n_tokens - t0) : 0;
-    const uint64_t base = reinterpret_cast<uint64_t>(X) + (uint64_t)t0 * row_bytes;
+  auto make_rsrc = [&](uint64_t base, int64_t rows) {
     i32x4_t r;
     r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base & 0xffffffffu));
     r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));   // stride 0
@@ -307,8 +329,26 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     r[3] = 0x00020000;
     return r;
   };
+  // A and B descriptors of stage kk (the same except in the update mode)
+  auto stage_rsrc = [&](int kk, i32x4_t& rA, i32x4_t& rB) {
+    const int64_t t0 = (int64_t)kk * kK16;
+    const int64_t rows = (kk < ks1) ? min<int64_t>(kK16, n_tokens - t0) : 0;
+    if constexpr (UPD) {
+      // segment g = 0..5 reads planes (-h,h) (-h,m) (-m,h) (-h,l) (-l,h) (-m,m)
+      const int per_seg = up.kseg / kK16;
+      const int g = kk / per_seg;
+      const int64_t row = (int64_t)(kk - g * per_seg) * kK16;
+      const int pa = 3 + ((0x120100 >> (4 * g)) & 0xF), pb = (0x102010 >> (4 * g)) & 0xF;
+      rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows);
+      rB = make_rsrc(reinterpret_cast<uint64_t>(X + pb * up.plane) + (uint64_t)row * row_bytes, rows);
+    } else {
+      rA = make_rsrc(reinterpret_cast<uint64_t>(X) + (uint64_t)t0 * row_bytes, rows);
+      rB = rA;
+    }
+  };
   // copy n (0..2*NI-1) of stage kk's DMA into slot `slot`
-  auto dma = [&](const i32x4_t& r, int slot, int n) {
+  auto dma = [&](const i32x4_t& rA, const i32x4_t& rB, int slot, int n) {
+    const i32x4_t& r = (n < NI) ? rA : rB;
     const int i = n % NI;
     const uint32_t dst = ((n < NI) ? ldsA : ldsB) + (uint32_t)slot * kSlotBytes + 4096u * i + 1024u * wave;
     const int voff = (n < NI) ? voffA[i] : voffB[i];
@@ -326,6 +366,22 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // update mode: this wave's 128 x 128 block of C (rows from tile I,
+  // columns from tile J), read before the first copy of the item
+  const int cm0 = I * kT16 + wm * 128, cn0 = J * kT16 + wn * 128;
+  const bool cwrite = UPD && !(I == J && wm == 1 && wn == 0) && cm0 < d && cn0 < d;
+  float* cw = UPD ? up.C + (size_t)(cm0 + 4 * (lane >> 5)) * up.ldc + cn0 + (lane & 31) : nullptr;
+  if constexpr (UPD) {
+    if (cwrite) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[i][j][r] = cw[(size_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * up.ldc + j * 32];
+    }
+  }
 
   if (ks0 < ks1) {
     // Ring of kSlots16 stage slots.  The sync point of stage k sits before
@@ -340,16 +396,18 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     static_assert(kSlots16 >= 3 && NKS % 2 == 0 && 2 * NI == 8, "ring layout: 8 copies over a slice's 16 MFMAs");
 #pragma unroll
     for (int a = 0; a <= kSlots16 - 3; ++a) {
-      const i32x4_t r0 = stage_rsrc(ks0 + a);
+      i32x4_t r0A, r0B;
+      stage_rsrc(ks0 + a, r0A, r0B);
 #pragma unroll
-      for (int n = 0; n < 2 * NI; ++n) dma(r0, a, n);
+      for (int n = 0; n < 2 * NI; ++n) dma(r0A, r0B, a, n);
     }
     wait_vm<kInFlight * 2 * NI>();
     lds_barrier();
     {
-      const i32x4_t r0 = stage_rsrc(ks0 + kSlots16 - 2);
+      i32x4_t r0A, r0B;
+      stage_rsrc(ks0 + kSlots16 - 2, r0A, r0B);
 #pragma unroll
-      for (int n = 0; n < 2 * NI; ++n) dma(r0, kSlots16 - 2, n);
+      for (int n = 0; n < 2 * NI; ++n) dma(r0A, r0B, kSlots16 - 2, n);
     }
     typename Op16<T>::v4 op[2][8][2];             // [buffer][a0..a3, b0..b3][lo, hi]
 #pragma unroll
@@ -364,7 +422,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
       constexpr int NSLOT = (SLOT + 1) % kSlots16, DSLOT = (SLOT + kSlots16 - 1) % kSlots16;
       const uint32_t bA = ldsA + (uint32_t)SLOT * kSlotBytes, bB = ldsB + (uint32_t)SLOT * kSlotBytes;
       const uint32_t nA = ldsA + (uint32_t)NSLOT * kSlotBytes, nB = ldsB + (uint32_t)NSLOT * kSlotBytes;
-      i32x4_t rn;
+      i32x4_t rnA, rnB;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int cur = ks & 1, nxt = cur ^ 1;
@@ -372,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
         if (last) {
           wait_vm<kInFlight * 2 * NI>();
           lds_barrier();
-          rn = stage_rsrc(kk + kSlots16 - 1);
+          stage_rsrc(kk + kSlots16 - 1, rnA, rnB);
         }
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
@@ -390,7 +448,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
                                      (uint32_t)(ks + 1) * kSliceBytes + h * 2048u);
           else
             op[nxt][f][h] = tr_at<T>((f < 4 ? nA + offA[f] : nB + offB[f - 4]) + h * 2048u);
-          if (last && (n & 1) == 0) dma(rn, DSLOT, n >> 1);   // a copy every second MFMA
+          if (last && (n & 1) == 0) dma(rnA, rnB, DSLOT, n >> 1);   // a copy every second MFMA
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -412,13 +470,25 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   }
   if (PACE) done += (unsigned)(ks1 - ks0);
 
-  float* out = partial + ((size_t)w * 4 + wave) * (16 * 16 * 64);
+  if constexpr (UPD) {
+    if (cwrite) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) out[((i * 4 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+          for (int r = 0; r < 16; ++r)
+            cw[(size_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * up.ldc + j * 32] = acc[i][j][r];
+    }
+  } else {
+    float* out = partial + ((size_t)w * 4 + wave) * (16 * 16 * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) out[((i * 4 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+  }
   }
   // finished: no one waits on this workgroup
   if (PACE && wave == 0 && lane == 0) __hip_atomic_store(prow + c, ~0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -724,13 +794,13 @@ static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_d
     GPTQ_LAUNCH_CHECK();
   }
   if (x_dtype == GPTQ_BF16) {
-    auto k = pace_on ? syrk16_kernel<__bf16, true> : syrk16_kernel<__bf16, false>;
+    auto k = pace_on ? syrk16_kernel<__bf16, true, false> : syrk16_kernel<__bf16, false, false>;
     k<<<pg, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
-                         (int)p.nk, partial, pace);
+                         (int)p.nk, partial, pace, Split3Args{});
   } else if (x_dtype == GPTQ_F16) {
-    auto k = pace_on ? syrk16_kernel<_Float16, true> : syrk16_kernel<_Float16, false>;
+    auto k = pace_on ? syrk16_kernel<_Float16, true, false> : syrk16_kernel<_Float16, false, false>;
     k<<<pg, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
-                         (int)p.nk, partial, pace);
+                         (int)p.nk, partial, pace, Split3Args{});
   } else {
     syrk32_kernel<<<items, 256, 0, s>>>(static_cast<const float*>(X), n_tokens, d_in, p.nt, p.ntiles,
                                         p.splits, p.nk, partial, pdiag);
@@ -781,6 +851,70 @@ static int scratch_for_current_device(void** out) {
     g_scratch_ptr[dev] = ptr;
   }
   *out = g_scratch_ptr[dev];
+  return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Split-bf16 update C[upper] -= P^T P (the factor's super-block updates)
+// ---------------------------------------------------------------------------
+// planes[p][k][c] (row pitch n), p = 0..5: h, m, l, -h, -m, -l with
+// h = bf16(P), m = bf16(P - h), l = bf16(P - h - m), rounded to nearest even;
+// both differences are exact in fp32, and |P - h - m - l| <= 2^-27 |P|
+// (each rounding keeps 8 significant bits).
+__global__ __launch_bounds__(256) void split3_planes_kernel(const float* __restrict__ P, int ldp, int K, int n,
+                                                            __bf16* __restrict__ planes) {
+  const int64_t total = (int64_t)K * n;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= total) return;
+  const int k = (int)(e / n), c = (int)(e - (int64_t)k * n);
+  const float4 v = *reinterpret_cast<const float4*>(P + (size_t)k * ldp + c);
+  const float a[4] = {v.x, v.y, v.z, v.w};
+  bf16x4_t h, m, l;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const __bf16 hu = (__bf16)a[u];
+    const float r1 = a[u] - (float)hu;
+    const __bf16 mu = (__bf16)r1;
+    const float r2 = r1 - (float)mu;
+    h[u] = hu;
+    m[u] = mu;
+    l[u] = (__bf16)r2;
+  }
+  *reinterpret_cast<bf16x4_t*>(planes + e) = h;
+  *reinterpret_cast<bf16x4_t*>(planes + total + e) = m;
+  *reinterpret_cast<bf16x4_t*>(planes + 2 * total + e) = l;
+  *reinterpret_cast<bf16x4_t*>(planes + 3 * total + e) = -h;
+  *reinterpret_cast<bf16x4_t*>(planes + 4 * total + e) = -m;
+  *reinterpret_cast<bf16x4_t*>(planes + 5 * total + e) = -l;
+}
+
+// The split form runs 256 resident 256 x 256 tiles per round at about 1 PFLOP/s
+// of bf16 products, six per fp32 product; the fp32 tiles reach ~110 TFLOP/s.
+// Below about 528 tiles (n ~ 8000) the rounds leave the chip partly idle and
+// the two take about the same time.
+bool split3_pays(int n) {
+  const int nt = (n + kT16 - 1) / kT16;
+  return nt * (nt + 1) / 2 >= 528;
+}
+
+size_t split3_planes_bytes(int K, int n) { return 6 * (size_t)K * (size_t)n * sizeof(__bf16); }
+
+int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void* planes, hipStream_t s) {
+  if (!P || !C || !planes || K <= 0 || K % kK16 != 0 || n <= 0 || n % 128 != 0 || ldp % 4 != 0 || ldp < n ||
+      ldc < n || (size_t)K * 6 / kK16 > (size_t)INT32_MAX)
+    return GPTQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(P) % 16 != 0 || reinterpret_cast<uintptr_t>(planes) % 16 != 0)
+    return GPTQ_ERR_INVALID_ARG;
+  __bf16* pl = static_cast<__bf16*>(planes);
+  const int64_t total = (int64_t)K * n;
+  split3_planes_kernel<<<(unsigned)((total / 4 + 255) / 256), 256, 0, s>>>(P, ldp, K, n, pl);
+  GPTQ_LAUNCH_CHECK();
+  const int nt = (n + kT16 - 1) / kT16, ntiles = nt * (nt + 1) / 2;
+  const unsigned items = (unsigned)(kXCD * ((ntiles + kXCD - 1) / kXCD));
+  const unsigned pg = (std::min<unsigned>(256u, items) + kXCD - 1) / kXCD * kXCD;
+  syrk16_kernel<__bf16, false, true><<<pg, 256, 0, s>>>(pl, (int64_t)6 * K, n, nt, ntiles, 1, 6 * K / kK16,
+                                                        nullptr, nullptr, Split3Args{C, ldc, K, total});
+  GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }
 

@@ -25,6 +25,7 @@
 //      X12 = -X11 * R12 * X22 (two grouped GEMMs per tree level)
 //   6. U[a][b] = X[n-1-b][n-1-a] for b >= a, 0 below.
 #include "gemm_f32.h"
+#include "split3.h"
 
 #include <vector>
 
@@ -638,7 +639,7 @@ __global__ __launch_bounds__(256) void flip_out_kernel(const float* __restrict__
 // ---------------------------------------------------------------- planning
 struct HinvLayout {
   int n, np, nblk, ldz;
-  size_t off_A, off_Z, off_sk, off_lam, off_flag, total;
+  size_t off_A, off_Z, off_sk, off_planes, off_lam, off_flag, total;
 };
 
 struct TreeNode { int a, mid, b; };
@@ -701,6 +702,10 @@ static HinvLayout hinv_layout(int n) {
   }
   L.off_sk = off;
   off = align_up(off + sk);
+  // bf16 planes of a super-block's rows for the split-bf16 trailing updates
+  const int gb = hinv_super_blocks(L.np);
+  L.off_planes = off;
+  if (gb > 1) off = align_up(off + split3_planes_bytes(gb * kNB, L.np - gb * kNB));
   L.off_lam = off;
   off = align_up(off + sizeof(double));
   L.off_flag = off;
@@ -730,6 +735,7 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
   float* A = reinterpret_cast<float*>(base + L.off_A);
   float* Z = reinterpret_cast<float*>(base + L.off_Z);
   float* SK = reinterpret_cast<float*>(base + L.off_sk);
+  void* planes = base + L.off_planes;
   double* lam = reinterpret_cast<double*>(base + L.off_lam);
   int* flag = reinterpret_cast<int*>(base + L.off_flag);
   const int n = L.n, np = L.np, nb = L.nblk;
@@ -790,6 +796,12 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
     const int free_cus = 256 - (1 + (rest - kNB) / kNB);
     ride = next_tiles <= 2 * free_cus;
     trail = TrailArgs{k0, Kk, ride ? std::max(0, ride_rows) : 0};
+    if (gb > 1 && s_end && !ride && split3_pays(rest)) {
+      // a super-block's whole update on bf16 MFMA through the split planes
+      const int st = split3_update(Arow, np, Kk, rest, Atrail, np, planes, s);
+      if (st != GPTQ_OK) return st;
+      continue;
+    }
     gemm_f32<true>(Arow, np, Arow, np, Atrail, np, ride ? kNB : urows, rest, Kk, -1.0f, 1.0f, 0, 0,
                    ride ? 0 : 1, s);
     GPTQ_LAUNCH_CHECK();

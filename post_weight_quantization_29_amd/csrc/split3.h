@@ -1,0 +1,26 @@
+// Symmetric rank-K update C[upper] -= P^T P of an fp32 panel on bf16 MFMA:
+// P is split into three bf16 planes (P = h + m + l) and the six plane
+// products that carry P's 24-bit significand are summed by the 16-bit SYRK
+// tile loop (csrc/hessian.hip), which gives each element about the rounding
+// error of an fp32 product at bf16 MFMA rates.
+#pragma once
+#include "common.h"
+
+namespace gptq {
+
+// true when an n-wide update has enough 256 x 256 tiles to fill the chip
+// (below that the fp32 tiles are as fast)
+bool split3_pays(int n);
+
+// bytes of the planes of a K x n panel (h, m, l and their negations)
+size_t split3_planes_bytes(int K, int n);
+
+// C[r][c] -= sum_k P[k][r] P[k][c] for r <= c (r, c < n; the strictly lower
+// 128-blocks of C are not touched; the lower halves of the diagonal 128-blocks
+// are written too).  P: K x n fp32, row pitch ldp; C: n x n fp32, row pitch
+// ldc; K a multiple of 32, n a multiple of 128, ldp a multiple of 4, P 16-byte
+// aligned; planes: split3_planes_bytes(K, n) bytes of device scratch, 16-byte
+// aligned.  Asynchronous on s.
+int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void* planes, hipStream_t s);
+
+}  // namespace gptq

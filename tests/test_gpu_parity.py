@@ -105,6 +105,43 @@ def test_prepare_hinv_parity(d, desc):
     assert np.abs(ident - np.eye(d)).max() <= 1e-2
 
 
+# A factor large enough that its super-block-end updates run in the split-bf16
+# form (rank-1024 updates of 9088 and 8064 trailing columns; the later ones
+# and the in-super-block updates stay in fp32 tiles), d ragged against the
+# 128-blocks.  H = 2 X^T X in fp32 from 12288 standard-normal tokens, shared
+# by both sides.
+def test_prepare_hinv_split_update():
+    d, n = 10000, 12288
+    say(f"[hinv] d={d} desc_act=1 (split-bf16 super-block updates)")
+    import post_weight_quantization_29_amd as P
+    rng = np.random.default_rng(10000)
+    X = rng.standard_normal((n, d), dtype=np.float32)
+    H32 = 2.0 * (X.T @ X)
+    del X
+    H32 = np.triu(H32) + np.triu(H32, 1).T          # exactly symmetric
+    H64 = H32.astype(np.float64)
+    ref = o.prepare(H64, 0.01, True)
+    Hd, _ = o.damp(H64[np.ix_(ref.perm, ref.perm)], 0.01)
+    del H64
+    Hg = to_dev(H32, "f32")
+    U = torch.empty((d, d), dtype=torch.float32, device="cuda")
+    perm = torch.empty((d,), dtype=torch.int32, device="cuda")
+    P.gptq_prepare_hinv(Hg, 0.01, 1, U, perm)
+    U = U.cpu().numpy().astype(np.float64)
+    assert np.array_equal(perm.cpu().numpy(), ref.perm)
+    assert np.all(np.tril(U, -1) == 0)
+    Ur = ref.U
+    dg = np.sqrt(np.diag(Ur))
+    el = float((np.abs(U - Ur) / np.outer(dg, dg)).max())
+    drel = float(np.max(np.abs(np.diag(U) - np.diag(Ur)) / np.diag(Ur)))
+    say(f"  U: max |dU|/sqrt(Uii Ujj) = {el:.3e}, diagonal max rel = {drel:.3e}")
+    assert el <= 1e-4 and drel <= 1e-4
+    # U^T U Hd = I on a sample of columns
+    cols = rng.choice(d, size=64, replace=False)
+    ident = U.T @ (U @ Hd[:, cols])
+    assert np.abs(ident - np.eye(d)[:, cols]).max() <= 1e-2
+
+
 # the desc_act order with heavy ties (diagonal values from a set of four, so
 # every rank is decided by the lower index), from H's own diagonal and from
 # fp64 keys, including sizes that leave a ragged last slice of the ranking
