@@ -208,30 +208,68 @@ GPTQ_DEV unsigned wave_min_u32(unsigned v) {
   return v;
 }
 
-// Update mode (UPD): the same tile loop computes C[upper] -= P^T P for an fp32
-// panel P (K x n) given as bf16 planes h, m, l with P = h + m + l (each the
-// bf16 rounding of what the planes before it leave) and their negations.  X
-// is then plane h, the contraction runs over 6K virtual tokens, K per
-// segment, and segment (hh, hm, mh, hl, lh, mm) takes its A operand from the
-// negated plane and its B operand from the plane named: every product of two
-// pieces down to 2^-27 of |P_ki P_kj| is included, so each element gets about
-// the error of an fp32 product.  Tiles run as upper tiles (I <= J), the
-// accumulators start from C and end in C; the strictly lower 128-block of a
-// diagonal tile is left alone.  n is a multiple of 128, so a wave's 128 x 128
-// block is wholly inside C or wholly outside.
+// Update modes.  MODE 1 (symmetric): the same tile loop computes
+// C[upper] -= P^T P for an fp32 panel P (K x n) given as bf16 planes h, m, l
+// with P = h + m + l (each the bf16 rounding of what the planes before it
+// leave) and their negations.  X is then plane h, the contraction runs over 6K
+// virtual tokens, K per segment, and segment (mm, lh, hl, mh, hm, hh) takes its
+// A operand from the negated plane and its B operand from the plane named:
+// every product of two pieces down to 2^-27 of |P_ki P_kj| is included, so
+// each element gets about the error of an fp32 product.  Tiles run as upper
+// tiles (I <= J), the accumulators start from zero and are added to C at the
+// end; the strictly lower 128-block of a diagonal tile is left alone.  n is a
+// multiple of 128, so a wave's 128 x 128 block is wholly inside C or outside.
+// MODE 2 (general): C (m x n) = beta C + alpha A^T B, alpha = +-1, beta 0 or
+// 1, for fp32 A (K x m) and B (K x n) given as the planes h, m, l of each
+// (A's from X, row pitch m = d; B's from B, row pitch n), over every tile of
+// C; C is read after the contraction and C + alpha acc (or alpha acc) is
+// stored, guarded element by element.
+// Plane of each of the six segments (nibble g of kSegA / kSegB: 0 = h,
+// 1 = m, 2 = l), smallest products first, so the accumulator grows from the
+// 2^-18-scale terms to the leading h h products and only those are rounded
+// at the scale of the result.
+constexpr int kSegA = 0x001021;   // m l h m h h
+constexpr int kSegB = 0x010201;   // m h l h m h
+
 struct Split3Args {
-  float* C;         // n x n, row pitch ldc
+  float* C;         // MODE 1: n x n; MODE 2: m x n; row pitch ldc
   int ldc;
   int kseg;         // K, a multiple of the 32-token stage
-  int64_t plane;    // elements from one plane to the next: h, m, l, -h, -m, -l
+  int64_t plane;    // elements from one plane of X to the next (MODE 1: h, m, l, -h, -m, -l)
+  const __bf16* B;  // MODE 2: B's planes h, m, l (row pitch n)
+  int64_t planeB;   // MODE 2: elements from one plane of B to the next
+  int n;            // MODE 2: columns of C and of B
+  int ntn;          // MODE 2: 256-wide tile columns
+  int neg;          // MODE 2: alpha = -1
+  int beta;         // MODE 2: 1 = C is read and accumulated into, 0 = C is overwritten
 };
 
-template <typename T, bool PACE, bool UPD>
+// MODE 2 tile order: strips of kSB tile rows, each walked column by column
+// (kSB tiles of a column, then the next column), cut into 8 contiguous chunks,
+// one per XCD; an XCD's 32 co-resident workgroups then share 4 A panels and
+// about 8 B panels.  Returns false for padding items.
+GPTQ_DEV bool rect_item(int w, int mt, int ntn, int ntiles, int& I, int& J) {
+  const int chunk = (ntiles + kXCD - 1) / kXCD;
+  const int x = w % kXCD, k = w / kXCD;
+  if (k >= chunk) return false;
+  const int L = x * chunk + k;
+  if (L >= ntiles) return false;
+  const int s = L / (kSB * ntn);
+  const int rem = L - s * kSB * ntn;
+  const int h = min(kSB, mt - s * kSB);
+  J = rem / h;
+  I = s * kSB + rem % h;
+  return true;
+}
+
+template <typename T, bool PACE, int MODE>
 __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X, int64_t n_tokens,
                                                          int d, int nt, int ntiles, int splits,
                                                          int nk, float* __restrict__ partial,
                                                          unsigned* __restrict__ pace, Split3Args up) {
-  static_assert(!(UPD && PACE), "the update mode reads cached planes: no pacing");
+  constexpr bool UPD = MODE != 0;
+  static_assert(!(UPD && PACE), "the update modes read cached planes: no pacing");
+  static_assert(MODE != 2 || sizeof(T) == 2, "planes are 16-bit");
   __shared__ __attribute__((aligned(16))) T sA[kSlots16][kStage16];
   __shared__ __attribute__((aligned(16))) T sB[kSlots16][kStage16];
   constexpr uint32_t kSlotBytes = kStage16 * 2;    // 16 KB
@@ -243,6 +281,8 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t row_bytes = (uint32_t)d * 2u;
+  const uint32_t rowB_bytes = (MODE == 2) ? (uint32_t)up.n * 2u : row_bytes;   // B's row pitch
+  const int dB = (MODE == 2) ? up.n : d;                                     // B's channels
   const uint32_t ldsA = (uint32_t)(uintptr_t)(LDS_AS const void*)&sA[0][0];
   const uint32_t ldsB = (uint32_t)(uintptr_t)(LDS_AS const void*)&sB[0][0];
 
@@ -280,8 +320,9 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     }
   };
   for (int kidx = c; kidx < per_xcd; kidx += nper) {
-  int s, I, J;
-  if (!xcd_item(kidx * kXCD + x, nt, ntiles, splits, s, I, J)) {
+  int s = 0, I, J;
+  if (MODE == 2 ? !rect_item(kidx * kXCD + x, nt, up.ntn, ntiles, I, J)
+                : !xcd_item(kidx * kXCD + x, nt, ntiles, splits, s, I, J)) {
     // a padding item: count its stages as done so the others do not wait on it
     const int sp = kidx / ((ntiles + kXCD - 1) / kXCD);
     if (PACE && sp < splits) done += (unsigned)((int64_t)nk * (sp + 1) / splits - (int64_t)nk * sp / splits);
@@ -291,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   I = __builtin_amdgcn_readfirstlane(I);
   J = __builtin_amdgcn_readfirstlane(J);
   const int w = s * ntiles + tri_index(I, J);     // partial slot
-  if (UPD) {
+  if (MODE == 1) {
     const int t = I;
     I = J;
     J = t;
@@ -316,16 +357,16 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       voffA[i] = (chA < d) ? (int)((uint32_t)(R + 8 * i) * row_bytes + chA * 2) : 0x7ffffff0;
-      voffB[i] = (chB < d) ? (int)((uint32_t)(R + 8 * i) * row_bytes + chB * 2) : 0x7ffffff0;
+      voffB[i] = (chB < dB) ? (int)((uint32_t)(R + 8 * i) * rowB_bytes + chB * 2) : 0x7ffffff0;
     }
   }
   // buffer descriptor of stage kk (rows past the end, or kk outside this
   // split, read as zero)
-  auto make_rsrc = [&](uint64_t base, int64_t rows) {
+  auto make_rsrc = [&](uint64_t base, int64_t rows, uint32_t rb) {
     i32x4_t r;
     r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base & 0xffffffffu));
     r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));   // stride 0
-    r[2] = __builtin_amdgcn_readfirstlane((int)(rows * row_bytes));
+    r[2] = __builtin_amdgcn_readfirstlane((int)(rows * rb));
     r[3] = 0x00020000;
     return r;
   };
@@ -333,16 +374,25 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   auto stage_rsrc = [&](int kk, i32x4_t& rA, i32x4_t& rB) {
     const int64_t t0 = (int64_t)kk * kK16;
     const int64_t rows = (kk < ks1) ? min<int64_t>(kK16, n_tokens - t0) : 0;
-    if constexpr (UPD) {
-      // segment g = 0..5 reads planes (-h,h) (-h,m) (-m,h) (-h,l) (-l,h) (-m,m)
+    if constexpr (MODE == 1) {
+      // segment g = 0..5 reads planes (-m,m) (-l,h) (-h,l) (-m,h) (-h,m) (-h,h)
       const int per_seg = up.kseg / kK16;
       const int g = kk / per_seg;
       const int64_t row = (int64_t)(kk - g * per_seg) * kK16;
-      const int pa = 3 + ((0x120100 >> (4 * g)) & 0xF), pb = (0x102010 >> (4 * g)) & 0xF;
-      rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows);
-      rB = make_rsrc(reinterpret_cast<uint64_t>(X + pb * up.plane) + (uint64_t)row * row_bytes, rows);
+      const int pa = 3 + ((kSegA >> (4 * g)) & 0xF), pb = (kSegB >> (4 * g)) & 0xF;
+      rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
+      rB = make_rsrc(reinterpret_cast<uint64_t>(X + pb * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
+    } else if constexpr (MODE == 2) {
+      // segment g = 0..5 reads planes (m,m) (l,h) (h,l) (m,h) (h,m) (h,h) of (A, B)
+      const int per_seg = up.kseg / kK16;
+      const int g = kk / per_seg;
+      const int64_t row = (int64_t)(kk - g * per_seg) * kK16;
+      const int pa = (kSegA >> (4 * g)) & 0xF, pb = (kSegB >> (4 * g)) & 0xF;
+      rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
+      rB = make_rsrc(reinterpret_cast<uint64_t>(up.B + pb * up.planeB) + (uint64_t)row * rowB_bytes, rows,
+                     rowB_bytes);
     } else {
-      rA = make_rsrc(reinterpret_cast<uint64_t>(X) + (uint64_t)t0 * row_bytes, rows);
+      rA = make_rsrc(reinterpret_cast<uint64_t>(X) + (uint64_t)t0 * row_bytes, rows, row_bytes);
       rB = rA;
     }
   };
@@ -366,22 +416,19 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  // update mode: this wave's 128 x 128 block of C (rows from tile I,
-  // columns from tile J), read before the first copy of the item
+  // update modes: this wave's 128 x 128 block of C (rows from tile I,
+  // columns from tile J).  The accumulators start from zero and C is read
+  // and added once after the contraction (as in the fp32 tiles): the 6K
+  // additions are then rounded at the scale of the update, not of C.
   const int cm0 = I * kT16 + wm * 128, cn0 = J * kT16 + wn * 128;
-  const bool cwrite = UPD && !(I == J && wm == 1 && wn == 0) && cm0 < d && cn0 < d;
+  const bool cwrite = (MODE == 1) ? (!(I == J && wm == 1 && wn == 0) && cm0 < d && cn0 < d)
+                                  : (MODE == 2 && cm0 < d && cn0 < dB);
   float* cw = UPD ? up.C + (size_t)(cm0 + 4 * (lane >> 5)) * up.ldc + cn0 + (lane & 31) : nullptr;
-  if constexpr (UPD) {
-    if (cwrite) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc[i][j][r] = cw[(size_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * up.ldc + j * 32];
-    }
-  }
+  // MODE 2: element (i, j, r) of the block is row cm0 + crow(i, r), column
+  // cn0 + j*32 + lane%32
+  auto c_in = [&](int i, int j, int r) {
+    return cm0 + 4 * (lane >> 5) + i * 32 + 8 * (r >> 2) + (r & 3) < d && cn0 + (lane & 31) + j * 32 < dB;
+  };
 
   if (ks0 < ks1) {
     // Ring of kSlots16 stage slots.  The sync point of stage k sits before
@@ -471,14 +518,59 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   if (PACE) done += (unsigned)(ks1 - ks0);
 
   if constexpr (UPD) {
+    // C + alpha acc, 32 rows at a time.  Every load of a group is issued
+    // before its stores (a load after a store through the same pointer
+    // would wait for it), through a buffer resource at the wave's block: one
+    // lane offset, the row offsets wave-uniform (scalar), so 128 loads in
+    // flight need no address registers.
     if (cwrite) {
+      const float sg = (MODE == 2 && up.neg) ? -1.0f : 1.0f;
+      const bool rd = (MODE == 1) || up.beta;
+      const int ldc = up.ldc;
+      const __amdgpu_buffer_rsrc_t cr =
+          __builtin_amdgcn_make_buffer_rsrc(up.C + (size_t)cm0 * ldc + cn0, (short)0, 0x7ffffff0, 0x00020000);
+      const int vo = (4 * (lane >> 5) * ldc + (lane & 31)) * 4;
+      // blocks wholly inside C take no per-element guard (MODE 1: always); the
+      // guarded form (edge blocks of a ragged C) is a separate code path
+      auto epi = [&]<bool G, bool RD>() {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int ih = 0; ih < 4; ih += 1) {
+          float old[1][4][16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+          for (int i2 = 0; i2 < 1; ++i2)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            cw[(size_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * up.ldc + j * 32] = acc[i][j][r];
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int i = ih + i2;
+                const int so = ((i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32) * 4;
+                old[i2][j][r] = 0.0f;
+                if (RD && (!G || c_in(i, j, r)))
+                  old[i2][j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cr, vo, so, 0));
+              }
+#pragma unroll
+          for (int i2 = 0; i2 < 1; ++i2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int i = ih + i2;
+                const int so = ((i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32) * 4;
+                if (!G || c_in(i, j, r))
+                  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, old[i2][j][r] + sg * acc[i][j][r]),
+                                                        cr, vo, so, 0);
+              }
+        }
+      };
+      const bool whole = MODE == 1 || (cm0 + 128 <= d && cn0 + 128 <= dB);
+      if (whole && rd)
+        epi.template operator()<false, true>();
+      else if (MODE == 2 && whole)
+        epi.template operator()<false, false>();
+      else if (MODE == 2 && rd)
+        epi.template operator()<true, true>();
+      else if (MODE == 2)
+        epi.template operator()<true, false>();
     }
   } else {
     float* out = partial + ((size_t)w * 4 + wave) * (16 * 16 * 64);
@@ -794,11 +886,11 @@ static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_d
     GPTQ_LAUNCH_CHECK();
   }
   if (x_dtype == GPTQ_BF16) {
-    auto k = pace_on ? syrk16_kernel<__bf16, true, false> : syrk16_kernel<__bf16, false, false>;
+    auto k = pace_on ? syrk16_kernel<__bf16, true, 0> : syrk16_kernel<__bf16, false, 0>;
     k<<<pg, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
                          (int)p.nk, partial, pace, Split3Args{});
   } else if (x_dtype == GPTQ_F16) {
-    auto k = pace_on ? syrk16_kernel<_Float16, true, false> : syrk16_kernel<_Float16, false, false>;
+    auto k = pace_on ? syrk16_kernel<_Float16, true, 0> : syrk16_kernel<_Float16, false, 0>;
     k<<<pg, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
                          (int)p.nk, partial, pace, Split3Args{});
   } else {
@@ -857,12 +949,12 @@ static int scratch_for_current_device(void** out) {
 // ---------------------------------------------------------------------------
 // Split-bf16 update C[upper] -= P^T P (the factor's super-block updates)
 // ---------------------------------------------------------------------------
-// planes[p][k][c] (row pitch n), p = 0..5: h, m, l, -h, -m, -l with
-// h = bf16(P), m = bf16(P - h), l = bf16(P - h - m), rounded to nearest even;
-// both differences are exact in fp32, and |P - h - m - l| <= 2^-27 |P|
+// planes[p][k][c] (row pitch n), p = 0..nplanes-1: h, m, l (, -h, -m, -l)
+// with h = bf16(P), m = bf16(P - h), l = bf16(P - h - m), rounded to nearest
+// even; both differences are exact in fp32, and |P - h - m - l| <= 2^-27 |P|
 // (each rounding keeps 8 significant bits).
 __global__ __launch_bounds__(256) void split3_planes_kernel(const float* __restrict__ P, int ldp, int K, int n,
-                                                            __bf16* __restrict__ planes) {
+                                                            __bf16* __restrict__ planes, int nplanes) {
   const int64_t total = (int64_t)K * n;
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= total) return;
@@ -883,6 +975,7 @@ __global__ __launch_bounds__(256) void split3_planes_kernel(const float* __restr
   *reinterpret_cast<bf16x4_t*>(planes + e) = h;
   *reinterpret_cast<bf16x4_t*>(planes + total + e) = m;
   *reinterpret_cast<bf16x4_t*>(planes + 2 * total + e) = l;
+  if (nplanes < 6) return;
   *reinterpret_cast<bf16x4_t*>(planes + 3 * total + e) = -h;
   *reinterpret_cast<bf16x4_t*>(planes + 4 * total + e) = -m;
   *reinterpret_cast<bf16x4_t*>(planes + 5 * total + e) = -l;
@@ -907,13 +1000,58 @@ int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void
     return GPTQ_ERR_INVALID_ARG;
   __bf16* pl = static_cast<__bf16*>(planes);
   const int64_t total = (int64_t)K * n;
-  split3_planes_kernel<<<(unsigned)((total / 4 + 255) / 256), 256, 0, s>>>(P, ldp, K, n, pl);
+  split3_planes_kernel<<<(unsigned)((total / 4 + 255) / 256), 256, 0, s>>>(P, ldp, K, n, pl, 6);
   GPTQ_LAUNCH_CHECK();
   const int nt = (n + kT16 - 1) / kT16, ntiles = nt * (nt + 1) / 2;
   const unsigned items = (unsigned)(kXCD * ((ntiles + kXCD - 1) / kXCD));
   const unsigned pg = (std::min<unsigned>(256u, items) + kXCD - 1) / kXCD * kXCD;
-  syrk16_kernel<__bf16, false, true><<<pg, 256, 0, s>>>(pl, (int64_t)6 * K, n, nt, ntiles, 1, 6 * K / kK16,
+  syrk16_kernel<__bf16, false, 1><<<pg, 256, 0, s>>>(pl, (int64_t)6 * K, n, nt, ntiles, 1, 6 * K / kK16,
                                                         nullptr, nullptr, Split3Args{C, ldc, K, total});
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+// The general form at K = 2048 runs a 256 x 256 tile in about 0.35 ms; with
+// fewer tiles than one round of the 256 CUs the fp32 tiles are as fast.
+bool split3_gemm_applies(const float* A, int lda, const float* B, int ldb, int K, int m, int n) {
+  if (!A || !B || K <= 0 || K % kK16 != 0 || m <= 0 || n <= 0 || m % 8 != 0 || n % 8 != 0) return false;
+  if (lda % 4 != 0 || ldb % 4 != 0 || lda < m || ldb < n) return false;
+  if (reinterpret_cast<uintptr_t>(A) % 16 != 0 || reinterpret_cast<uintptr_t>(B) % 16 != 0) return false;
+  if ((size_t)K * 6 / kK16 > (size_t)INT32_MAX) return false;
+  const int64_t tiles = (int64_t)((m + kT16 - 1) / kT16) * ((n + kT16 - 1) / kT16);
+  return tiles >= 256;
+}
+
+size_t split3_gemm_planes_bytes(int K, int m, int n) { return 3 * (size_t)K * ((size_t)m + (size_t)n) * sizeof(__bf16); }
+
+int split3_gemm(const float* A, int lda, const float* B, int ldb, int K, int m, int n, float* C, int ldc,
+                bool neg, bool beta, void* planes, hipStream_t s) {
+  if (!split3_gemm_applies(A, lda, B, ldb, K, m, n) || !C || ldc < n || !planes ||
+      reinterpret_cast<uintptr_t>(planes) % 16 != 0)
+    return GPTQ_ERR_INVALID_ARG;
+  __bf16* pa = static_cast<__bf16*>(planes);
+  const int64_t ta = (int64_t)K * m, tb = (int64_t)K * n;
+  __bf16* pb = pa + 3 * ta;   // 3 K m elements: 16-byte aligned since m % 8 == 0
+  split3_planes_kernel<<<(unsigned)((ta / 4 + 255) / 256), 256, 0, s>>>(A, lda, K, m, pa, 3);
+  GPTQ_LAUNCH_CHECK();
+  split3_planes_kernel<<<(unsigned)((tb / 4 + 255) / 256), 256, 0, s>>>(B, ldb, K, n, pb, 3);
+  GPTQ_LAUNCH_CHECK();
+  const int mt = (m + kT16 - 1) / kT16, ntn = (n + kT16 - 1) / kT16, ntiles = mt * ntn;
+  const unsigned items = (unsigned)(kXCD * ((ntiles + kXCD - 1) / kXCD));
+  const unsigned pg = (std::min<unsigned>(256u, items) + kXCD - 1) / kXCD * kXCD;
+  Split3Args a{};
+  a.C = C;
+  a.ldc = ldc;
+  a.kseg = K;
+  a.plane = ta;
+  a.B = pb;
+  a.planeB = tb;
+  a.n = n;
+  a.ntn = ntn;
+  a.neg = neg ? 1 : 0;
+  a.beta = beta ? 1 : 0;
+  syrk16_kernel<__bf16, false, 2><<<pg, 256, 0, s>>>(pa, (int64_t)6 * K, m, mt, ntiles, 1, 6 * K / kK16, nullptr,
+                                                     nullptr, a);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }

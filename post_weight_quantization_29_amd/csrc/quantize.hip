@@ -17,6 +17,7 @@
 //                   and kept in ErrT.
 //   trailing GEMM:  W[:, b1:] -= Err * U[b0:b1, b1:] (fp32 MFMA).
 #include "gemm_f32.h"
+#include "split3.h"
 #include "panel.h"
 
 #include <utility>
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256) void pack_dense_kernel(const uint8_t* __restri
 
 // ---------------------------------------------------------------- planning
 struct QuantLayout {
-  size_t off_wp, off_err, off_gscale, total;
+  size_t off_wp, off_err, off_gscale, off_planes, total;
 };
 
 // Blocks per super-block (the lazy updates of the columns after a super-block
@@ -202,6 +203,10 @@ static QuantLayout quant_layout(int d_out, int d, int gb) {
   off = align_up(off + 2 * (size_t)gb * kQB * d_out * sizeof(float));
   L.off_gscale = off;   // fp64 scale of each row's group in progress (groups wider than the block)
   off = align_up(off + (size_t)d_out * sizeof(double));
+  // bf16 planes of a super-block's Err rows and U rows for the split-bf16
+  // update of the columns after the next super-block
+  L.off_planes = off;
+  if (gb > 1) off = align_up(off + split3_gemm_planes_bytes(gb * kQB, d_out, d));
   L.total = off;
   return L;
 }
@@ -265,6 +270,7 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   float* Wp = reinterpret_cast<float*>(base + L.off_wp);
   float* ErrT = reinterpret_cast<float*>(base + L.off_err);
   double* gscale = reinterpret_cast<double*>(base + L.off_gscale);
+  void* planes = base + L.off_planes;
 
   if (d <= kGatherW)
     gather_w_row_kernel<<<d_out, 1024, 0, s>>>(W, w_dtype, d_out, d, perm, G, Wp, g_idx,
@@ -337,9 +343,15 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
       GPTQ_LAUNCH_CHECK();
       if (tail > 0) {
         const int c = d - tail;
-        gemm_f32<true>(st.Eprev, d_out, U + (size_t)k0 * d + c, d, Wp + c, d, d_out, tail, st.kprev,
-                       -1.0f, 1.0f, 0, 0, 0, s);
-        GPTQ_LAUNCH_CHECK();
+        const float* Uc = U + (size_t)k0 * d + c;
+        if (split3_gemm_applies(st.Eprev, d_out, Uc, d, st.kprev, d_out, tail)) {
+          // on bf16 MFMA through split fp32 planes (about an fp32 product's error)
+          const int e = split3_gemm(st.Eprev, d_out, Uc, d, st.kprev, d_out, tail, Wp + c, d, true, true, planes, s);
+          if (e != GPTQ_OK) return e;
+        } else {
+          gemm_f32<true>(st.Eprev, d_out, Uc, d, Wp + c, d, d_out, tail, st.kprev, -1.0f, 1.0f, 0, 0, 0, s);
+          GPTQ_LAUNCH_CHECK();
+        }
       }
     }
     return GPTQ_OK;
@@ -368,9 +380,23 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
     const bool s_end = (b + 1) % gb == 0;
     const int k0 = s_end ? (b / gb) * gb * kQB : b0;
     const int c1 = s_end ? d : super_end(b);
-    gemm_f32<true>(s_end ? err_of(b - b % gb) : err_of(b), d_out, U + (size_t)k0 * d + b1, d, Wp + b1, d,
-                   d_out, c1 - b1, b1 - k0, -1.0f, 1.0f, 0, 0, 0, s);
+    const float* E = s_end ? err_of(b - b % gb) : err_of(b);
+    // at a super-block's end the columns after the next super-block take the
+    // split-bf16 product when it applies, as in the fused steps
+    int c_s = c1;
+    if (s_end && gb > 1) {
+      const int tail = std::max(0, d - std::max(super_end(b + 1), b1 + std::min(kQB, d - b1)));
+      const int c = d - tail;
+      if (tail > 0 && split3_gemm_applies(E, d_out, U + (size_t)k0 * d + c, d, b1 - k0, d_out, tail)) c_s = c;
+    }
+    gemm_f32<true>(E, d_out, U + (size_t)k0 * d + b1, d, Wp + b1, d, d_out, c_s - b1, b1 - k0, -1.0f, 1.0f, 0, 0,
+                   0, s);
     GPTQ_LAUNCH_CHECK();
+    if (c_s < c1) {
+      const int e = split3_gemm(E, d_out, U + (size_t)k0 * d + c_s, d, b1 - k0, d_out, c1 - c_s, Wp + c_s, d, true,
+                                true, planes, s);
+      if (e != GPTQ_OK) return e;
+    }
   }
   return GPTQ_OK;
 }
