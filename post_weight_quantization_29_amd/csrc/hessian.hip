@@ -242,24 +242,28 @@ struct Split3Args {
   int ntn;          // MODE 2: 256-wide tile columns
   int neg;          // MODE 2: alpha = -1
   int beta;         // MODE 2: 1 = C is read and accumulated into, 0 = C is overwritten
+  int kmode;        // MODE 2 contraction of tile (I, J): 0 all K; 1 k >= 256 I; 2 k < min(K, 256 (J + 1))
 };
 
-// MODE 2 tile order: strips of kSB tile rows, each walked column by column
-// (kSB tiles of a column, then the next column), cut into 8 contiguous chunks,
-// one per XCD; an XCD's 32 co-resident workgroups then share 4 A panels and
-// about 8 B panels.  Returns false for padding items.
-GPTQ_DEV bool rect_item(int w, int mt, int ntn, int ntiles, int& I, int& J) {
-  const int chunk = (ntiles + kXCD - 1) / kXCD;
-  const int x = w % kXCD, k = w / kXCD;
-  if (k >= chunk) return false;
-  const int L = x * chunk + k;
-  if (L >= ntiles) return false;
-  const int s = L / (kSB * ntn);
-  const int rem = L - s * kSB * ntn;
-  const int h = min(kSB, mt - s * kSB);
-  J = rem / h;
-  I = s * kSB + rem % h;
-  return true;
+// MODE 2 tile order: strips of kSB tile rows cut into column-blocks (the kSB
+// tiles of one tile column of a strip), dealt round-robin to the 8 XCDs:
+// item k of XCD x is tile k % kSB of column-block (k / kSB) * 8 + x, so a
+// round of an XCD's 32 co-resident workgroups shares 4 A panels and 8 B
+// panels, and with triangular operands (the tile's contraction grows with
+// its row or column) every XCD gets the same mix of long and short tiles.
+// Items past C's last tile row return false.
+GPTQ_DEV bool rect_item(int x, int k, int mt, int ntn, int& I, int& J) {
+  const int q = (k / kSB) * kXCD + x;
+  const int sb = q / ntn;
+  I = sb * kSB + k % kSB;
+  J = q - sb * ntn;
+  return I < mt;
+}
+
+// items per XCD of the MODE 2 order
+GPTQ_DEV int rect_items_per_xcd(int mt, int ntn) {
+  const int nsb = (mt + kSB - 1) / kSB;
+  return ((nsb * ntn + kXCD - 1) / kXCD) * kSB;
 }
 
 template <typename T, bool PACE, int MODE>
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   // XCD x's list, so the workgroups of an XCD move through the list in rounds
   // and those sharing channel panels read the same tokens at the same time.
   const int x = blockIdx.x % kXCD, c = blockIdx.x / kXCD, nper = gridDim.x / kXCD;
-  const int per_xcd = ((ntiles + kXCD - 1) / kXCD) * splits;
+  const int per_xcd = (MODE == 2) ? rect_items_per_xcd(nt, up.ntn) : ((ntiles + kXCD - 1) / kXCD) * splits;
   unsigned* prow = PACE ? pace + x * kPaceSlots : nullptr;
   bool pacing = PACE && (wave == 0) && (nper <= kPaceSlots);
   unsigned done = 0;                             // stages done (skipped items included)
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   };
   for (int kidx = c; kidx < per_xcd; kidx += nper) {
   int s = 0, I, J;
-  if (MODE == 2 ? !rect_item(kidx * kXCD + x, nt, up.ntn, ntiles, I, J)
+  if (MODE == 2 ? !rect_item(x, kidx, nt, up.ntn, I, J)
                 : !xcd_item(kidx * kXCD + x, nt, ntiles, splits, s, I, J)) {
     // a padding item: count its stages as done so the others do not wait on it
     const int sp = kidx / ((ntiles + kXCD - 1) / kXCD);
@@ -332,13 +336,23 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   I = __builtin_amdgcn_readfirstlane(I);
   J = __builtin_amdgcn_readfirstlane(J);
   const int w = s * ntiles + tri_index(I, J);     // partial slot
+  if (MODE == 2 && up.kmode == 2) J = up.ntn - 1 - J;   // longest contractions first
   if (MODE == 1) {
     const int t = I;
     I = J;
     J = t;
   }
-  const int ks0 = __builtin_amdgcn_readfirstlane((int)((int64_t)nk * s / splits));
-  const int ks1 = __builtin_amdgcn_readfirstlane((int)((int64_t)nk * (s + 1) / splits));
+  // MODE 2: the tile's contraction [klo, khi) (triangular operands), 6 segments of pseg stages
+  int klo = 0, pseg = 0;
+  if constexpr (MODE == 2) {
+    int khi = up.kseg;
+    if (up.kmode == 1) klo = I * kT16;
+    if (up.kmode == 2) khi = min(up.kseg, (J + 1) * kT16);
+    pseg = __builtin_amdgcn_readfirstlane((khi - klo) / kK16);
+    klo = __builtin_amdgcn_readfirstlane(klo);
+  }
+  const int ks0 = (MODE == 2) ? 0 : __builtin_amdgcn_readfirstlane((int)((int64_t)nk * s / splits));
+  const int ks1 = (MODE == 2) ? 6 * pseg : __builtin_amdgcn_readfirstlane((int)((int64_t)nk * (s + 1) / splits));
 
   // copies of the previous item (and its stores) are complete and every wave
   // is done with its LDS
@@ -383,10 +397,10 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
       rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
       rB = make_rsrc(reinterpret_cast<uint64_t>(X + pb * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
     } else if constexpr (MODE == 2) {
-      // segment g = 0..5 reads planes (m,m) (l,h) (h,l) (m,h) (h,m) (h,h) of (A, B)
-      const int per_seg = up.kseg / kK16;
-      const int g = kk / per_seg;
-      const int64_t row = (int64_t)(kk - g * per_seg) * kK16;
+      // segment g = 0..5 reads planes (m,m) (l,h) (h,l) (m,h) (h,m) (h,h) of (A, B);
+      // stages past the tile's last one read nothing (rows = 0)
+      const int g = min(kk / pseg, 5);
+      const int64_t row = klo + (int64_t)(kk - g * pseg) * kK16;
       const int pa = (kSegA >> (4 * g)) & 0xF, pb = (kSegB >> (4 * g)) & 0xF;
       rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
       rB = make_rsrc(reinterpret_cast<uint64_t>(up.B + pb * up.planeB) + (uint64_t)row * rowB_bytes, rows,
@@ -954,13 +968,19 @@ static int scratch_for_current_device(void** out) {
 // even; both differences are exact in fp32, and |P - h - m - l| <= 2^-27 |P|
 // (each rounding keeps 8 significant bits).
 __global__ __launch_bounds__(256) void split3_planes_kernel(const float* __restrict__ P, int ldp, int K, int n,
-                                                            __bf16* __restrict__ planes, int nplanes) {
+                                                            __bf16* __restrict__ planes, int nplanes, bool upper) {
   const int64_t total = (int64_t)K * n;
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= total) return;
   const int k = (int)(e / n), c = (int)(e - (int64_t)k * n);
   const float4 v = *reinterpret_cast<const float4*>(P + (size_t)k * ldp + c);
-  const float a[4] = {v.x, v.y, v.z, v.w};
+  float a[4] = {v.x, v.y, v.z, v.w};
+  if (upper) {
+    // P upper triangular: entries below its diagonal are taken as zero
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k > c + u) a[u] = 0.0f;
+  }
   bf16x4_t h, m, l;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -1000,7 +1020,7 @@ int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void
     return GPTQ_ERR_INVALID_ARG;
   __bf16* pl = static_cast<__bf16*>(planes);
   const int64_t total = (int64_t)K * n;
-  split3_planes_kernel<<<(unsigned)((total / 4 + 255) / 256), 256, 0, s>>>(P, ldp, K, n, pl, 6);
+  split3_planes_kernel<<<(unsigned)((total / 4 + 255) / 256), 256, 0, s>>>(P, ldp, K, n, pl, 6, false);
   GPTQ_LAUNCH_CHECK();
   const int nt = (n + kT16 - 1) / kT16, ntiles = nt * (nt + 1) / 2;
   const unsigned items = (unsigned)(kXCD * ((ntiles + kXCD - 1) / kXCD));
@@ -1011,30 +1031,80 @@ int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void
   return GPTQ_OK;
 }
 
+// planes[p][k][i] (row pitch m), p = 0..2: h, m, l of A[i][k] for A m x K
+// row-major (pitch lda), transposed through a 64 x 64 LDS tile; with `upper`
+// the entries of A below its diagonal (k < i) are taken as zero.
+__global__ __launch_bounds__(256) void split3_planes_t_kernel(const float* __restrict__ A, int lda, int K, int m,
+                                                              __bf16* __restrict__ planes, bool upper) {
+  __shared__ float t[64][65];
+  const int k0 = blockIdx.x * 64, i0 = blockIdx.y * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 256 * q, r = e >> 4, c4 = (e & 15) * 4;
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (i0 + r < m && k0 + c4 < K) v = *reinterpret_cast<const float4*>(A + (size_t)(i0 + r) * lda + k0 + c4);
+    t[r][c4] = v.x;
+    t[r][c4 + 1] = v.y;
+    t[r][c4 + 2] = v.z;
+    t[r][c4 + 3] = v.w;
+  }
+  __syncthreads();
+  const int64_t total = (int64_t)K * m;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 256 * q, rr = e >> 4, cc = (e & 15) * 4;
+    const int k = k0 + rr, i = i0 + cc;
+    if (k >= K || i >= m) continue;
+    bf16x4_t h, mm, l;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float a = t[cc + u][rr];
+      if (upper && k < i + u) a = 0.0f;
+      const __bf16 hu = (__bf16)a;
+      const float r1 = a - (float)hu;
+      const __bf16 mu = (__bf16)r1;
+      h[u] = hu;
+      mm[u] = mu;
+      l[u] = (__bf16)(r1 - (float)mu);
+    }
+    const int64_t o = (int64_t)k * m + i;
+    *reinterpret_cast<bf16x4_t*>(planes + o) = h;
+    *reinterpret_cast<bf16x4_t*>(planes + total + o) = mm;
+    *reinterpret_cast<bf16x4_t*>(planes + 2 * total + o) = l;
+  }
+}
+
 // The general form at K = 2048 runs a 256 x 256 tile in about 0.35 ms; with
 // fewer tiles than one round of the 256 CUs the fp32 tiles are as fast.
-bool split3_gemm_applies(const float* A, int lda, const float* B, int ldb, int K, int m, int n) {
-  if (!A || !B || K <= 0 || K % kK16 != 0 || m <= 0 || n <= 0 || m % 8 != 0 || n % 8 != 0) return false;
-  if (lda % 4 != 0 || ldb % 4 != 0 || lda < m || ldb < n) return false;
-  if (reinterpret_cast<uintptr_t>(A) % 16 != 0 || reinterpret_cast<uintptr_t>(B) % 16 != 0) return false;
+bool split3_gemm_shape_ok(int K, int m, int n) {
+  if (K <= 0 || K % kK16 != 0 || m <= 0 || n <= 0 || m % 8 != 0 || n % 8 != 0) return false;
   if ((size_t)K * 6 / kK16 > (size_t)INT32_MAX) return false;
   const int64_t tiles = (int64_t)((m + kT16 - 1) / kT16) * ((n + kT16 - 1) / kT16);
   return tiles >= 256;
 }
 
+bool split3_gemm_applies(const float* A, int lda, bool a_rows, const float* B, int ldb, int K, int m, int n) {
+  if (!A || !B || !split3_gemm_shape_ok(K, m, n)) return false;
+  if (lda % 4 != 0 || ldb % 4 != 0 || lda < (a_rows ? K : m) || ldb < n) return false;
+  return reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(B) % 16 == 0;
+}
+
 size_t split3_gemm_planes_bytes(int K, int m, int n) { return 3 * (size_t)K * ((size_t)m + (size_t)n) * sizeof(__bf16); }
 
-int split3_gemm(const float* A, int lda, const float* B, int ldb, int K, int m, int n, float* C, int ldc,
-                bool neg, bool beta, void* planes, hipStream_t s) {
-  if (!split3_gemm_applies(A, lda, B, ldb, K, m, n) || !C || ldc < n || !planes ||
-      reinterpret_cast<uintptr_t>(planes) % 16 != 0)
+int split3_gemm(const float* A, int lda, bool a_rows, const float* B, int ldb, int K, int m, int n, float* C,
+                int ldc, bool neg, bool beta, int tri, void* planes, hipStream_t s) {
+  if (!split3_gemm_applies(A, lda, a_rows, B, ldb, K, m, n) || !C || ldc < n || !planes ||
+      reinterpret_cast<uintptr_t>(planes) % 16 != 0 || tri < 0 || tri > 2 || (tri == 1 && !a_rows))
     return GPTQ_ERR_INVALID_ARG;
   __bf16* pa = static_cast<__bf16*>(planes);
   const int64_t ta = (int64_t)K * m, tb = (int64_t)K * n;
   __bf16* pb = pa + 3 * ta;   // 3 K m elements: 16-byte aligned since m % 8 == 0
-  split3_planes_kernel<<<(unsigned)((ta / 4 + 255) / 256), 256, 0, s>>>(A, lda, K, m, pa, 3);
+  if (a_rows)
+    split3_planes_t_kernel<<<dim3((K + 63) / 64, (m + 63) / 64), 256, 0, s>>>(A, lda, K, m, pa, tri == 1);
+  else
+    split3_planes_kernel<<<(unsigned)((ta / 4 + 255) / 256), 256, 0, s>>>(A, lda, K, m, pa, 3, false);
   GPTQ_LAUNCH_CHECK();
-  split3_planes_kernel<<<(unsigned)((tb / 4 + 255) / 256), 256, 0, s>>>(B, ldb, K, n, pb, 3);
+  split3_planes_kernel<<<(unsigned)((tb / 4 + 255) / 256), 256, 0, s>>>(B, ldb, K, n, pb, 3, tri == 2);
   GPTQ_LAUNCH_CHECK();
   const int mt = (m + kT16 - 1) / kT16, ntn = (n + kT16 - 1) / kT16, ntiles = mt * ntn;
   const unsigned items = (unsigned)(kXCD * ((ntiles + kXCD - 1) / kXCD));
@@ -1050,6 +1120,7 @@ int split3_gemm(const float* A, int lda, const float* B, int ldb, int K, int m, 
   a.ntn = ntn;
   a.neg = neg ? 1 : 0;
   a.beta = beta ? 1 : 0;
+  a.kmode = tri;
   syrk16_kernel<__bf16, false, 2><<<pg, 256, 0, s>>>(pa, (int64_t)6 * K, m, mt, ntiles, 1, 6 * K / kK16, nullptr,
                                                      nullptr, a);
   GPTQ_LAUNCH_CHECK();

@@ -675,6 +675,10 @@ static int hinv_super_blocks(int np) {
   return ((size_t)np * np * sizeof(float) > (size_t(256) << 20)) ? 8 : 1;
 }
 
+// a tree node [a, mid) + [mid, b) takes its two products in the split-bf16
+// form when both have enough tiles (Z = X11 R12 and X12 = -Z X22 are M x N)
+static bool tree_split3(int M, int N) { return split3_gemm_shape_ok(M, M, N) && split3_gemm_shape_ok(N, M, N); }
+
 static HinvLayout hinv_layout(int n) {
   HinvLayout L;
   L.n = n;
@@ -702,10 +706,22 @@ static HinvLayout hinv_layout(int n) {
   }
   L.off_sk = off;
   off = align_up(off + sk);
-  // bf16 planes of a super-block's rows for the split-bf16 trailing updates
+  // bf16 planes of a super-block's rows for the split-bf16 trailing updates,
+  // and of the operands of the tree nodes whose products take the split form
+  // (the factor and the tree run one after the other: one region serves both)
   const int gb = hinv_super_blocks(L.np);
+  size_t planes = (gb > 1) ? split3_planes_bytes(gb * kNB, L.np - gb * kNB) : 0;
+  {
+    std::vector<std::vector<TreeNode>> levels;
+    build_levels(0, L.nblk, 0, levels);
+    for (const auto& nodes : levels)
+      for (const TreeNode& t : nodes) {
+        const int M = (t.mid - t.a) * kNB, N = (t.b - t.mid) * kNB;
+        if (tree_split3(M, N)) planes = std::max(planes, split3_gemm_planes_bytes(std::max(M, N), M, N));
+      }
+  }
   L.off_planes = off;
-  if (gb > 1) off = align_up(off + split3_planes_bytes(gb * kNB, L.np - gb * kNB));
+  off = align_up(off + planes);
   L.off_lam = off;
   off = align_up(off + sizeof(double));
   L.off_flag = off;
@@ -813,7 +829,29 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
   std::vector<std::vector<TreeNode>> levels;
   build_levels(0, nb, 0, levels);
   for (int lv = (int)levels.size() - 1; lv >= 0; --lv) {
-    const std::vector<TreeNode>& nodes = levels[lv];
+    // nodes large enough run their two products in the split-bf16 form, one
+    // node at a time: Z = X11 R12 (X11 upper triangular: tile row I contracts
+    // from 256 I), then X12 = -Z X22 (X22 upper triangular: tile column J
+    // contracts up to 256 (J + 1)); the entries below the two diagonals are
+    // read as zero.  The rest go to the grouped fp32 launches.
+    std::vector<TreeNode> nodes;
+    for (const TreeNode& t : levels[lv]) {
+      const int r0 = t.a * kNB, r1 = t.mid * kNB, r2 = t.b * kNB;
+      const int M = r1 - r0, N = r2 - r1;
+      float* Zn = Z + (size_t)r0 * L.ldz;
+      const float* X11 = A + (size_t)r0 * np + r0;
+      const float* R12 = A + (size_t)r0 * np + r1;
+      const float* X22 = A + (size_t)r1 * np + r1;
+      if (!tree_split3(M, N) || !split3_gemm_applies(X11, np, true, R12, np, M, M, N) ||
+          !split3_gemm_applies(Zn, L.ldz, true, X22, np, N, M, N)) {
+        nodes.push_back(t);
+        continue;
+      }
+      int st = split3_gemm(X11, np, true, R12, np, M, M, N, Zn, L.ldz, false, false, 1, planes, s);
+      if (st != GPTQ_OK) return st;
+      st = split3_gemm(Zn, L.ldz, true, X22, np, N, M, N, A + (size_t)r0 * np + r1, np, true, false, 2, planes, s);
+      if (st != GPTQ_OK) return st;
+    }
     for (size_t c0 = 0; c0 < nodes.size(); c0 += kGemmMaxGroup) {
       const int cnt = (int)std::min<size_t>(kGemmMaxGroup, nodes.size() - c0);
       GemmGroup g1, g2;

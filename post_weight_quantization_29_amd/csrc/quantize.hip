@@ -344,9 +344,9 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
       if (tail > 0) {
         const int c = d - tail;
         const float* Uc = U + (size_t)k0 * d + c;
-        if (split3_gemm_applies(st.Eprev, d_out, Uc, d, st.kprev, d_out, tail)) {
+        if (split3_gemm_applies(st.Eprev, d_out, false, Uc, d, st.kprev, d_out, tail)) {
           // on bf16 MFMA through split fp32 planes (about an fp32 product's error)
-          const int e = split3_gemm(st.Eprev, d_out, Uc, d, st.kprev, d_out, tail, Wp + c, d, true, true, planes, s);
+          const int e = split3_gemm(st.Eprev, d_out, false, Uc, d, st.kprev, d_out, tail, Wp + c, d, true, true, 0, planes, s);
           if (e != GPTQ_OK) return e;
         } else {
           gemm_f32<true>(st.Eprev, d_out, Uc, d, Wp + c, d, d_out, tail, st.kprev, -1.0f, 1.0f, 0, 0, 0, s);
@@ -387,14 +387,14 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
     if (s_end && gb > 1) {
       const int tail = std::max(0, d - std::max(super_end(b + 1), b1 + std::min(kQB, d - b1)));
       const int c = d - tail;
-      if (tail > 0 && split3_gemm_applies(E, d_out, U + (size_t)k0 * d + c, d, b1 - k0, d_out, tail)) c_s = c;
+      if (tail > 0 && split3_gemm_applies(E, d_out, false, U + (size_t)k0 * d + c, d, b1 - k0, d_out, tail)) c_s = c;
     }
     gemm_f32<true>(E, d_out, U + (size_t)k0 * d + b1, d, Wp + b1, d, d_out, c_s - b1, b1 - k0, -1.0f, 1.0f, 0, 0,
                    0, s);
     GPTQ_LAUNCH_CHECK();
     if (c_s < c1) {
-      const int e = split3_gemm(E, d_out, U + (size_t)k0 * d + c_s, d, b1 - k0, d_out, c1 - c_s, Wp + c_s, d, true,
-                                true, planes, s);
+      const int e = split3_gemm(E, d_out, false, U + (size_t)k0 * d + c_s, d, b1 - k0, d_out, c1 - c_s, Wp + c_s, d,
+                                true, true, 0, planes, s);
       if (e != GPTQ_OK) return e;
     }
   }

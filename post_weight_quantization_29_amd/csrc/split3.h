@@ -24,16 +24,21 @@ size_t split3_planes_bytes(int K, int n);
 int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void* planes, hipStream_t s);
 
 // General product on the same tile loop: C = beta C + alpha A^T B with
-// alpha = -1 (neg) or +1 and beta = 1 or 0, for A: K x m fp32 (row pitch lda)
-// and B: K x n fp32 (row pitch ldb), both k-major; C: m x n fp32, row pitch
-// ldc.  The planes h, m, l of A and of B are formed first (3 K (m + n) bf16
-// in planes, 16-byte aligned).  Applies when m, n are multiples of 8, K of
-// 32, lda and ldb of 4, A and B 16-byte aligned, and C has at least 256
-// tiles of 256 x 256 (split3_gemm_applies); callers use the fp32 tiles
-// otherwise.  Asynchronous on s.
-bool split3_gemm_applies(const float* A, int lda, const float* B, int ldb, int K, int m, int n);
+// alpha = -1 (neg) or +1 and beta = 1 or 0, for A: K x m fp32 k-major (row
+// pitch lda), or, with a_rows, m x K row-major (transposed while it is
+// split), and B: K x n fp32 k-major (row pitch ldb); C: m x n fp32, row pitch
+// ldc.  tri = 1: A is upper triangular (a_rows; A[i][k] = 0 for k < i, tile
+// row I contracts k >= 256 I); tri = 2: B is upper triangular (B[k][j] = 0
+// for k > j, tile column J contracts k < 256 (J + 1)); entries below those
+// diagonals are not read as stored.  The planes h, m, l of A and of B are
+// formed first (3 K (m + n) bf16 in planes, 16-byte aligned).  Applies when
+// m, n are multiples of 8, K of 32, lda and ldb of 4, A and B 16-byte
+// aligned, and C has at least 256 tiles of 256 x 256; callers use the fp32
+// tiles otherwise.  Asynchronous on s.
+bool split3_gemm_shape_ok(int K, int m, int n);
+bool split3_gemm_applies(const float* A, int lda, bool a_rows, const float* B, int ldb, int K, int m, int n);
 size_t split3_gemm_planes_bytes(int K, int m, int n);
-int split3_gemm(const float* A, int lda, const float* B, int ldb, int K, int m, int n, float* C, int ldc,
-                bool neg, bool beta, void* planes, hipStream_t s);
+int split3_gemm(const float* A, int lda, bool a_rows, const float* B, int ldb, int K, int m, int n, float* C,
+                int ldc, bool neg, bool beta, int tri, void* planes, hipStream_t s);
 
 }  // namespace gptq
