@@ -385,22 +385,31 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     return r;
   };
   // A and B descriptors of stage kk (the same except in the update mode)
+  // update modes: stage kk is stage seg_i of segment seg_g; the calls below
+  // come in stage order from ks0 = 0, so the pair is advanced instead of
+  // divided out of kk
+  const int seg_len = (MODE == 1) ? up.kseg / kK16 : pseg;
+  int seg_g = 0, seg_i = 0;
   auto stage_rsrc = [&](int kk, i32x4_t& rA, i32x4_t& rB) {
     const int64_t t0 = (int64_t)kk * kK16;
     const int64_t rows = (kk < ks1) ? min<int64_t>(kK16, n_tokens - t0) : 0;
+    int g = 0;
+    int64_t row = 0;
+    if constexpr (UPD) {
+      g = min(seg_g, 5);                 // stages past the tile's last one read nothing (rows = 0)
+      row = klo + (int64_t)seg_i * kK16;
+      if (++seg_i == seg_len) {
+        seg_i = 0;
+        ++seg_g;
+      }
+    }
     if constexpr (MODE == 1) {
       // segment g = 0..5 reads planes (-m,m) (-l,h) (-h,l) (-m,h) (-h,m) (-h,h)
-      const int per_seg = up.kseg / kK16;
-      const int g = kk / per_seg;
-      const int64_t row = (int64_t)(kk - g * per_seg) * kK16;
       const int pa = 3 + ((kSegA >> (4 * g)) & 0xF), pb = (kSegB >> (4 * g)) & 0xF;
       rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
       rB = make_rsrc(reinterpret_cast<uint64_t>(X + pb * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
     } else if constexpr (MODE == 2) {
-      // segment g = 0..5 reads planes (m,m) (l,h) (h,l) (m,h) (h,m) (h,h) of (A, B);
-      // stages past the tile's last one read nothing (rows = 0)
-      const int g = min(kk / pseg, 5);
-      const int64_t row = klo + (int64_t)(kk - g * pseg) * kK16;
+      // segment g = 0..5 reads planes (m,m) (l,h) (h,l) (m,h) (h,m) (h,h) of (A, B)
       const int pa = (kSegA >> (4 * g)) & 0xF, pb = (kSegB >> (4 * g)) & 0xF;
       rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
       rB = make_rsrc(reinterpret_cast<uint64_t>(up.B + pb * up.planeB) + (uint64_t)row * rowB_bytes, rows,
@@ -585,6 +594,64 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
         epi.template operator()<true, true>();
       else if (MODE == 2)
         epi.template operator()<true, false>();
+    }
+  } else if (up.C) {
+    // One token split (up.C = H, row pitch d): no partial tile and no
+    // reduction pass; the tile adds 2 acc into H itself (fl(H + 2 acc), the
+    // same rounding as the reduction's) and, off the diagonal, into the
+    // mirrored block.  Each 32-row group's loads are issued before its stores.
+    if (cm0 < d && cn0 < d) {
+      float* H = up.C;
+      const __amdgpu_buffer_rsrc_t hr =
+          __builtin_amdgcn_make_buffer_rsrc(H + (size_t)cm0 * d + cn0, (short)0, 0x7ffffff0, 0x00020000);
+      const __amdgpu_buffer_rsrc_t mr =
+          __builtin_amdgcn_make_buffer_rsrc(H + (size_t)cn0 * d + cm0, (short)0, 0x7ffffff0, 0x00020000);
+      const int vo = (4 * (lane >> 5) * d + (lane & 31)) * 4;   // (row, col) of the block
+      const int vm = ((lane & 31) * d + 4 * (lane >> 5)) * 4;   // (col, row): the mirror
+      if (cm0 + 128 <= d && cn0 + 128 <= d) {
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          if (pass == 1 && I == J) break;
+          const __amdgpu_buffer_rsrc_t br = pass ? mr : hr;
+          const int vl = pass ? vm : vo;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float old[4][16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int rr = i * 32 + 8 * (r >> 2) + (r & 3), cc = j * 32;
+                const int so = (pass ? cc * d + rr : rr * d + cc) * 4;
+                old[j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, vl, so, 0));
+              }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int rr = i * 32 + 8 * (r >> 2) + (r & 3), cc = j * 32;
+                const int so = (pass ? cc * d + rr : rr * d + cc) * 4;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, old[j][r] + 2.0f * acc[i][j][r]),
+                                                      br, vl, so, 0);
+              }
+          }
+        }
+      } else {
+        // a block at the edge of H (d not a multiple of 128)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = cm0 + 4 * (lane >> 5) + i * 32 + 8 * (r >> 2) + (r & 3);
+              const int col = cn0 + (lane & 31) + j * 32;
+              if (row < d && col < d) {
+                H[(size_t)row * d + col] += 2.0f * acc[i][j][r];
+                if (I != J) H[(size_t)col * d + row] += 2.0f * acc[i][j][r];
+              }
+            }
+      }
     }
   } else {
     float* out = partial + ((size_t)w * 4 + wave) * (16 * 16 * 64);
@@ -899,14 +966,18 @@ static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_d
     zero_u32_kernel<<<1, 256, 0, s>>>(pace, kXCD * kPaceSlots);
     GPTQ_LAUNCH_CHECK();
   }
+  // one token split: the 16-bit tiles add into H themselves (no reduction)
+  const bool direct = !f32 && p.splits == 1;
+  Split3Args da{};
+  if (direct) da.C = H;
   if (x_dtype == GPTQ_BF16) {
     auto k = pace_on ? syrk16_kernel<__bf16, true, 0> : syrk16_kernel<__bf16, false, 0>;
     k<<<pg, 256, 0, s>>>(static_cast<const __bf16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
-                         (int)p.nk, partial, pace, Split3Args{});
+                         (int)p.nk, partial, pace, da);
   } else if (x_dtype == GPTQ_F16) {
     auto k = pace_on ? syrk16_kernel<_Float16, true, 0> : syrk16_kernel<_Float16, false, 0>;
     k<<<pg, 256, 0, s>>>(static_cast<const _Float16*>(X), n_tokens, d_in, p.nt, p.ntiles, p.splits,
-                         (int)p.nk, partial, pace, Split3Args{});
+                         (int)p.nk, partial, pace, da);
   } else {
     syrk32_kernel<<<items, 256, 0, s>>>(static_cast<const float*>(X), n_tokens, d_in, p.nt, p.ntiles,
                                         p.splits, p.nk, partial, pdiag);
@@ -914,7 +985,7 @@ static int hessian_launch(float* H, double* hdiag, const void* X, gptq_dtype x_d
   GPTQ_LAUNCH_CHECK();
   if (f32)
     syrk_reduce_kernel<2, 256><<<p.ntiles * 4, 256, 0, s>>>(partial, H, d_in, p.ntiles, p.splits);
-  else
+  else if (!direct)
     // 512 threads: the 66 KB LDS tile allows two workgroups per CU, so the
     // loads in flight come from more threads per workgroup
     syrk_reduce_kernel<4, 512><<<p.ntiles * 4, 512, 0, s>>>(partial, H, d_in, p.ntiles, p.splits);
