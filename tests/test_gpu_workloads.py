@@ -272,3 +272,44 @@ def test_large_layer_wide_groups(G, desc):
     assert par.agree >= 0.999 and par.first_not_tie == 0
     assert par.scale_rel <= 1e-3 and par.zero_mismatch == 0 and par.q_bad == 0
     assert par.obj_rel <= 1e-3
+
+
+def test_ragged_rows_split_tail():
+    """8200 x 8320 (d_out not a multiple of 128): a work copy over 256 MB, so
+    the column loop runs sixteen-block super-blocks and their tails (4224 and
+    2176 columns after the first two super-blocks) take the split-bf16
+    product, whose last tile row holds only 8 rows (the guarded edge path).
+    The fused and the per-block schedules agree bit for bit, and sampled rows
+    (the 8 rows of the ragged tile row among them) meet the whole-layer bar
+    against the float64 oracle given the same fp32 H."""
+    import post_weight_quantization_29_amd as P
+    d_out, d = 8200, 8320
+    say(f"[ragged split tail] {d_out}x{d} G128")
+    rng = np.random.default_rng(8200)
+    X = rng.standard_normal((12288, d), dtype=np.float32)
+    H32 = 2.0 * (X.T @ X)
+    del X
+    W = (rng.standard_normal((d_out, d)) * 0.02).astype(np.float16)
+    Wg, Hg = torch.from_numpy(W).cuda(), torch.from_numpy(H32).cuda()
+    cfg = P.make_config(bits=4, group_size=128)
+    a = P.quantize_layer_outputs(Wg, Hg, cfg, with_q=True)
+    torch.cuda.synchronize()
+    b = P.quantize_layer_outputs(Wg, Hg, P.make_config(bits=4, group_size=128, per_block_steps=1), with_q=True)
+    torch.cuda.synchronize()
+    for x, y in ((a.codes, b.codes), (a.scales, b.scales), (a.zeros, b.zeros), (a.Q, b.Q)):
+        assert bool(torch.equal(x, y))
+    del b
+    H64 = H32.astype(np.float64)
+    W64 = W.astype(np.float64)
+    rows = _sample(d_out, 120, 37, must=(0,) + tuple(range(8192, 8200)))
+    ref = o.gptq(W64[rows], H64, bits=4, group_size=128, damp_percent=0.01)
+    tr = torch.as_tensor(rows, device="cuda")
+    codes = a.codes.index_select(0, tr).cpu().numpy()
+    par = compare_quant(ref, W64[rows], H64, codes, a.scales.index_select(0, tr).cpu().numpy(),
+                        a.zeros.index_select(0, tr).cpu().numpy(), a.Q.index_select(0, tr).cpu().numpy(), 128)
+    say(f"  {par}")
+    assert par.agree >= 0.999 and par.first_not_tie == 0
+    assert par.scale_rel <= 1e-3 and par.zero_mismatch == 0 and par.q_bad == 0
+    assert par.obj_rel <= 1e-3
+    del a, Wg, Hg
+    torch.cuda.empty_cache()
