@@ -208,42 +208,57 @@ GPTQ_DEV unsigned wave_min_u32(unsigned v) {
   return v;
 }
 
-// Update modes.  MODE 1 (symmetric): the same tile loop computes
-// C[upper] -= P^T P for an fp32 panel P (K x n) given as bf16 planes h, m, l
-// with P = h + m + l (each the bf16 rounding of what the planes before it
-// leave) and their negations.  X is then plane h, the contraction runs over 6K
-// virtual tokens, K per segment, and segment (mm, lh, hl, mh, hm, hh) takes its
-// A operand from the negated plane and its B operand from the plane named:
-// every product of two pieces down to 2^-27 of |P_ki P_kj| is included, so
-// each element gets about the error of an fp32 product.  Tiles run as upper
-// tiles (I <= J), the accumulators start from zero and are added to C at the
-// end; the strictly lower 128-block of a diagonal tile is left alone.  n is a
-// multiple of 128, so a wave's 128 x 128 block is wholly inside C or outside.
+// Update modes: fp32 products on the 16-bit tile loop.  An fp32 operand x is
+// scaled by a power of two per output row or column, 2^(14 - e) with e the
+// exponent of that row's or column's largest |x| (exact; the largest then
+// lies in [2^14, 2^15), inside fp16's range), and split into two fp16 pieces
+// h = fp16(x'), l = fp16(x' - h) (the difference is exact in fp32 and
+// |x' - h - l| <= 2^-22 |x'|).  A product of two operands is the sum of the
+// three piece products lh, hl, hh (the dropped ll and the split residuals
+// are <= 3 2^-22 of the product, below what the fp32 accumulation of the
+// contraction already carries), so each fp32 product costs three fp16
+// products on v_mfma_f32_32x32x16_f16.  The contraction runs over 3K virtual
+// tokens, one segment of K per piece product, smallest first, so the
+// accumulator grows from the 2^-11-scale products to the hh ones and only
+// those are rounded at the scale of the result; the accumulators start from
+// zero and C takes C + alpha 2^(eA_i + eB_j - 28) acc once at the end (the
+// power of two exact), through buffer resources.
+// MODE 1 (symmetric): C[upper] -= P^T P for an fp32 panel P (K x n, planes
+// h, l of X, row pitch n); tiles run as upper tiles (I <= J) and the strictly
+// lower 128-block of a diagonal tile is left alone.  n is a multiple of 128,
+// so a wave's 128 x 128 block is wholly inside C or outside.
 // MODE 2 (general): C (m x n) = beta C + alpha A^T B, alpha = +-1, beta 0 or
-// 1, for fp32 A (K x m) and B (K x n) given as the planes h, m, l of each
-// (A's from X, row pitch m = d; B's from B, row pitch n), over every tile of
-// C; C is read after the contraction and C + alpha acc (or alpha acc) is
-// stored, guarded element by element.
-// Plane of each of the six segments (nibble g of kSegA / kSegB: 0 = h,
-// 1 = m, 2 = l), smallest products first, so the accumulator grows from the
-// 2^-18-scale terms to the leading h h products and only those are rounded
-// at the scale of the result.
-constexpr int kSegA = 0x001021;   // m l h m h h
-constexpr int kSegB = 0x010201;   // m h l h m h
+// 1, for fp32 A (K x m) and B (K x n) given as their planes h, l (A's from X,
+// row pitch m = d; B's from B, row pitch n), over every tile of C, stores
+// guarded element by element.
+// Piece of each of the three segments (nibble g of kSegA / kSegB: 0 = h,
+// 1 = l): l h, h l, h h.
+constexpr int kSegs = 3;
+constexpr int kSegA = 0x001;
+constexpr int kSegB = 0x010;
 
 struct Split3Args {
   float* C;         // MODE 1: n x n; MODE 2: m x n; row pitch ldc
   int ldc;
   int kseg;         // K, a multiple of the 32-token stage
-  int64_t plane;    // elements from one plane of X to the next (MODE 1: h, m, l, -h, -m, -l)
-  const __bf16* B;  // MODE 2: B's planes h, m, l (row pitch n)
+  int64_t plane;    // elements from one plane of X to the next (h, l)
+  const _Float16* B;  // MODE 2: B's planes h, l (row pitch n)
   int64_t planeB;   // MODE 2: elements from one plane of B to the next
+  const unsigned* sA;  // largest |x| (float bits) of each row of C's operand A (MODE 1: of P's columns)
+  const unsigned* sB;  // the same for the columns of C (MODE 1: sA again)
   int n;            // MODE 2: columns of C and of B
   int ntn;          // MODE 2: 256-wide tile columns
-  int neg;          // MODE 2: alpha = -1
+  int neg;          // MODE 2: alpha = -1 (MODE 1: always)
   int beta;         // MODE 2: 1 = C is read and accumulated into, 0 = C is overwritten
   int kmode;        // MODE 2 contraction of tile (I, J): 0 all K; 1 k >= 256 I; 2 k < min(K, 256 (J + 1))
 };
+
+// exponent e of a row's or column's largest |x| (given as float bits): its
+// pieces are taken of x 2^(14 - e); an all-zero row or column takes e = 0
+GPTQ_DEV int piece_exp(unsigned maxbits) {
+  const float m = __builtin_bit_cast(float, maxbits);
+  return (m > 0.0f) ? ilogbf(m) : 0;
+}
 
 // MODE 2 tile order: strips of kSB tile rows cut into column-blocks (the kSB
 // tiles of one tile column of a strip), dealt round-robin to the 8 XCDs:
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     klo = __builtin_amdgcn_readfirstlane(klo);
   }
   const int ks0 = (MODE == 2) ? 0 : __builtin_amdgcn_readfirstlane((int)((int64_t)nk * s / splits));
-  const int ks1 = (MODE == 2) ? 6 * pseg : __builtin_amdgcn_readfirstlane((int)((int64_t)nk * (s + 1) / splits));
+  const int ks1 = (MODE == 2) ? kSegs * pseg : __builtin_amdgcn_readfirstlane((int)((int64_t)nk * (s + 1) / splits));
 
   // copies of the previous item (and its stores) are complete and every wave
   // is done with its LDS
@@ -396,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
     int g = 0;
     int64_t row = 0;
     if constexpr (UPD) {
-      g = min(seg_g, 5);                 // stages past the tile's last one read nothing (rows = 0)
+      g = min(seg_g, kSegs - 1);         // stages past the tile's last one read nothing (rows = 0)
       row = klo + (int64_t)seg_i * kK16;
       if (++seg_i == seg_len) {
         seg_i = 0;
@@ -404,12 +419,12 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
       }
     }
     if constexpr (MODE == 1) {
-      // segment g = 0..5 reads planes (-m,m) (-l,h) (-h,l) (-m,h) (-h,m) (-h,h)
-      const int pa = 3 + ((kSegA >> (4 * g)) & 0xF), pb = (kSegB >> (4 * g)) & 0xF;
+      // segment g = 0..2 reads pieces (l,h) (h,l) (h,h) of (P, P)
+      const int pa = (kSegA >> (4 * g)) & 0xF, pb = (kSegB >> (4 * g)) & 0xF;
       rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
       rB = make_rsrc(reinterpret_cast<uint64_t>(X + pb * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
     } else if constexpr (MODE == 2) {
-      // segment g = 0..5 reads planes (m,m) (l,h) (h,l) (m,h) (h,m) (h,h) of (A, B)
+      // segment g = 0..2 reads pieces (l,h) (h,l) (h,h) of (A, B)
       const int pa = (kSegA >> (4 * g)) & 0xF, pb = (kSegB >> (4 * g)) & 0xF;
       rA = make_rsrc(reinterpret_cast<uint64_t>(X + pa * up.plane) + (uint64_t)row * row_bytes, rows, row_bytes);
       rB = make_rsrc(reinterpret_cast<uint64_t>(up.B + pb * up.planeB) + (uint64_t)row * rowB_bytes, rows,
@@ -541,13 +556,26 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   if (PACE) done += (unsigned)(ks1 - ks0);
 
   if constexpr (UPD) {
-    // C + alpha acc, 32 rows at a time.  Every load of a group is issued
-    // before its stores (a load after a store through the same pointer
-    // would wait for it), through a buffer resource at the wave's block: one
-    // lane offset, the row offsets wave-uniform (scalar), so 128 loads in
-    // flight need no address registers.
+    // The tile's row and column exponents go to LDS: the stage ring is free
+    // once every wave is past its last stage and the copies issued ahead
+    // (empty ones past the tile's end still write their zeros) have landed.
+    int* eRow = reinterpret_cast<int*>(&sA[0][0]);
+    int* eCol = eRow + kT16;
+    wait_vm0();
+    lds_barrier();
+    {
+      const int r = I * kT16 + tid, c = J * kT16 + tid;
+      eRow[tid] = (r < d) ? piece_exp(up.sA[r]) : 0;
+      eCol[tid] = (c < dB) ? piece_exp(up.sB[c]) : 0;
+    }
+    __syncthreads();
+    // C + alpha 2^(eRow + eCol - 28) acc, 32 rows at a time.  Every load of a
+    // group is issued before its stores (a load after a store through the
+    // same pointer would wait for it), through a buffer resource at the
+    // wave's block: one lane offset, the row offsets wave-uniform (scalar),
+    // so 64 loads in flight need no address registers.
     if (cwrite) {
-      const float sg = (MODE == 2 && up.neg) ? -1.0f : 1.0f;
+      const float sg = (MODE == 1 || up.neg) ? -1.0f : 1.0f;
       const bool rd = (MODE == 1) || up.beta;
       const int ldc = up.ldc;
       const __amdgpu_buffer_rsrc_t cr =
@@ -579,9 +607,12 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
               for (int r = 0; r < 16; ++r) {
                 const int i = ih + i2;
                 const int so = ((i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32) * 4;
-                if (!G || c_in(i, j, r))
-                  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, old[i2][j][r] + sg * acc[i][j][r]),
-                                                        cr, vo, so, 0);
+                if (!G || c_in(i, j, r)) {
+                  const int ex = eRow[wm * 128 + 4 * (lane >> 5) + i * 32 + 8 * (r >> 2) + (r & 3)] +
+                                 eCol[wn * 128 + (lane & 31) + j * 32] - 28;
+                  __builtin_amdgcn_raw_buffer_store_b32(
+                      __builtin_bit_cast(uint32_t, old[i2][j][r] + sg * ldexpf(acc[i][j][r], ex)), cr, vo, so, 0);
+                }
               }
         }
       };
@@ -1032,81 +1063,93 @@ static int scratch_for_current_device(void** out) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-bf16 update C[upper] -= P^T P (the factor's super-block updates)
+// Split products (the factor's super-block updates and the tree's large
+// nodes, the column loop's super-block tails): scaled fp16 pieces of fp32
+// operands on the update modes of the tile loop
 // ---------------------------------------------------------------------------
-// planes[p][k][c] (row pitch n), p = 0..nplanes-1: h, m, l (, -h, -m, -l)
-// with h = bf16(P), m = bf16(P - h), l = bf16(P - h - m), rounded to nearest
-// even; both differences are exact in fp32, and |P - h - m - l| <= 2^-27 |P|
-// (each rounding keeps 8 significant bits).
+// Largest |x| of each column c < n of a K x n panel (row pitch ld) as float
+// bits, by atomicMax on the bits of non-negative floats (order-free); with
+// `upper` only k <= c counts (an upper-triangular operand).  out starts at 0.
+// A thread takes four adjacent columns (16-byte loads, n and ld multiples of
+// 4) over 64 rows, eight rows' loads in flight.
+__global__ __launch_bounds__(256) void col_absmax_kernel(const float* __restrict__ P, int ld, int K, int n, bool upper,
+                                                         unsigned* __restrict__ out) {
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= n) return;
+  const int k0 = blockIdx.y * 64, k1 = min(K, upper ? min(k0 + 64, c + 4) : k0 + 64);
+  float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = k0; k < k1; k += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = (k + u < k1) ? *reinterpret_cast<const float4*>(P + (size_t)(k + u) * ld + c) : make_float4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float a[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (!upper || k + u <= c + q) m[q] = fmaxf(m[q], fabsf(a[q]));
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (m[q] > 0.0f) atomicMax(out + c + q, __builtin_bit_cast(unsigned, m[q]));
+}
+
+// Largest |A[i][k]| of each row i < m of a row-major m x K matrix (pitch
+// lda), one workgroup per row; with `upper` only k >= i counts.
+__global__ __launch_bounds__(256) void row_absmax_kernel(const float* __restrict__ A, int lda, int K, bool upper,
+                                                         unsigned* __restrict__ out) {
+  __shared__ float red[4];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  float m = 0.0f;
+  for (int k = (upper ? i : 0) + tid; k < K; k += 256) m = fmaxf(m, fabsf(A[(size_t)i * lda + k]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) out[i] = __builtin_bit_cast(unsigned, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+}
+
+// the two fp16 pieces of x scaled by 2^(14 - e)
+GPTQ_DEV void split2(float x, int e, _Float16& h, _Float16& l) {
+  const float xs = ldexpf(x, 14 - e);
+  h = (_Float16)xs;
+  l = (_Float16)(xs - (float)h);
+}
+
+// planes[p][k][c] (row pitch n), p = 0, 1: h, l of P[k][c] scaled by its
+// column's exponent (smax[c]); with `upper` entries below P's diagonal
+// (k > c) are taken as zero.
 __global__ __launch_bounds__(256) void split3_planes_kernel(const float* __restrict__ P, int ldp, int K, int n,
-                                                            __bf16* __restrict__ planes, int nplanes, bool upper) {
+                                                            const unsigned* __restrict__ smax, bool upper,
+                                                            _Float16* __restrict__ planes) {
   const int64_t total = (int64_t)K * n;
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= total) return;
   const int k = (int)(e / n), c = (int)(e - (int64_t)k * n);
   const float4 v = *reinterpret_cast<const float4*>(P + (size_t)k * ldp + c);
-  float a[4] = {v.x, v.y, v.z, v.w};
-  if (upper) {
-    // P upper triangular: entries below its diagonal are taken as zero
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (k > c + u) a[u] = 0.0f;
-  }
-  bf16x4_t h, m, l;
+  const float a[4] = {v.x, v.y, v.z, v.w};
+  f16x4_t h, l;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const __bf16 hu = (__bf16)a[u];
-    const float r1 = a[u] - (float)hu;
-    const __bf16 mu = (__bf16)r1;
-    const float r2 = r1 - (float)mu;
+    const float x = (upper && k > c + u) ? 0.0f : a[u];
+    _Float16 hu, lu;
+    split2(x, piece_exp(smax[c + u]), hu, lu);
     h[u] = hu;
-    m[u] = mu;
-    l[u] = (__bf16)r2;
+    l[u] = lu;
   }
-  *reinterpret_cast<bf16x4_t*>(planes + e) = h;
-  *reinterpret_cast<bf16x4_t*>(planes + total + e) = m;
-  *reinterpret_cast<bf16x4_t*>(planes + 2 * total + e) = l;
-  if (nplanes < 6) return;
-  *reinterpret_cast<bf16x4_t*>(planes + 3 * total + e) = -h;
-  *reinterpret_cast<bf16x4_t*>(planes + 4 * total + e) = -m;
-  *reinterpret_cast<bf16x4_t*>(planes + 5 * total + e) = -l;
+  *reinterpret_cast<f16x4_t*>(planes + e) = h;
+  *reinterpret_cast<f16x4_t*>(planes + total + e) = l;
 }
 
-// The split form runs 256 resident 256 x 256 tiles per round at about 1 PFLOP/s
-// of bf16 products, six per fp32 product; the fp32 tiles reach ~110 TFLOP/s.
-// Below about 528 tiles (n ~ 8000) the rounds leave the chip partly idle and
-// the two take about the same time.
-bool split3_pays(int n) {
-  const int nt = (n + kT16 - 1) / kT16;
-  return nt * (nt + 1) / 2 >= 528;
-}
-
-size_t split3_planes_bytes(int K, int n) { return 6 * (size_t)K * (size_t)n * sizeof(__bf16); }
-
-int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void* planes, hipStream_t s) {
-  if (!P || !C || !planes || K <= 0 || K % kK16 != 0 || n <= 0 || n % 128 != 0 || ldp % 4 != 0 || ldp < n ||
-      ldc < n || (size_t)K * 6 / kK16 > (size_t)INT32_MAX)
-    return GPTQ_ERR_INVALID_ARG;
-  if (reinterpret_cast<uintptr_t>(P) % 16 != 0 || reinterpret_cast<uintptr_t>(planes) % 16 != 0)
-    return GPTQ_ERR_INVALID_ARG;
-  __bf16* pl = static_cast<__bf16*>(planes);
-  const int64_t total = (int64_t)K * n;
-  split3_planes_kernel<<<(unsigned)((total / 4 + 255) / 256), 256, 0, s>>>(P, ldp, K, n, pl, 6, false);
-  GPTQ_LAUNCH_CHECK();
-  const int nt = (n + kT16 - 1) / kT16, ntiles = nt * (nt + 1) / 2;
-  const unsigned items = (unsigned)(kXCD * ((ntiles + kXCD - 1) / kXCD));
-  const unsigned pg = (std::min<unsigned>(256u, items) + kXCD - 1) / kXCD * kXCD;
-  syrk16_kernel<__bf16, false, 1><<<pg, 256, 0, s>>>(pl, (int64_t)6 * K, n, nt, ntiles, 1, 6 * K / kK16,
-                                                        nullptr, nullptr, Split3Args{C, ldc, K, total});
-  GPTQ_LAUNCH_CHECK();
-  return GPTQ_OK;
-}
-
-// planes[p][k][i] (row pitch m), p = 0..2: h, m, l of A[i][k] for A m x K
-// row-major (pitch lda), transposed through a 64 x 64 LDS tile; with `upper`
-// the entries of A below its diagonal (k < i) are taken as zero.
+// planes[p][k][i] (row pitch m), p = 0, 1: h, l of A[i][k] for A m x K
+// row-major (pitch lda), scaled by its row's exponent (smax[i]), transposed
+// through a 64 x 64 LDS tile; with `upper` the entries below A's diagonal
+// (k < i) are taken as zero.
 __global__ __launch_bounds__(256) void split3_planes_t_kernel(const float* __restrict__ A, int lda, int K, int m,
-                                                              __bf16* __restrict__ planes, bool upper) {
+                                                              const unsigned* __restrict__ smax, bool upper,
+                                                              _Float16* __restrict__ planes) {
   __shared__ float t[64][65];
   const int k0 = blockIdx.x * 64, i0 = blockIdx.y * 64, tid = threadIdx.x;
 #pragma unroll
@@ -1126,30 +1169,69 @@ __global__ __launch_bounds__(256) void split3_planes_t_kernel(const float* __res
     const int e = tid + 256 * q, rr = e >> 4, cc = (e & 15) * 4;
     const int k = k0 + rr, i = i0 + cc;
     if (k >= K || i >= m) continue;
-    bf16x4_t h, mm, l;
+    f16x4_t h, l;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      float a = t[cc + u][rr];
-      if (upper && k < i + u) a = 0.0f;
-      const __bf16 hu = (__bf16)a;
-      const float r1 = a - (float)hu;
-      const __bf16 mu = (__bf16)r1;
+      const float x = (upper && k < i + u) ? 0.0f : t[cc + u][rr];
+      _Float16 hu, lu;
+      split2(x, piece_exp(smax[i + u]), hu, lu);
       h[u] = hu;
-      mm[u] = mu;
-      l[u] = (__bf16)(r1 - (float)mu);
+      l[u] = lu;
     }
     const int64_t o = (int64_t)k * m + i;
-    *reinterpret_cast<bf16x4_t*>(planes + o) = h;
-    *reinterpret_cast<bf16x4_t*>(planes + total + o) = mm;
-    *reinterpret_cast<bf16x4_t*>(planes + 2 * total + o) = l;
+    *reinterpret_cast<f16x4_t*>(planes + o) = h;
+    *reinterpret_cast<f16x4_t*>(planes + total + o) = l;
   }
 }
 
-// The general form at K = 2048 runs a 256 x 256 tile in about 0.35 ms; with
-// fewer tiles than one round of the 256 CUs the fp32 tiles are as fast.
+// The split form runs 256 resident 256 x 256 tiles per round at about 1 PFLOP/s
+// of fp16 products, three per fp32 product; the fp32 tiles reach ~110 TFLOP/s.
+// Below about 528 tiles (n ~ 8000) the rounds leave the chip partly idle.
+bool split3_pays(int n) {
+  const int nt = (n + kT16 - 1) / kT16;
+  return nt * (nt + 1) / 2 >= 528;
+}
+
+// planes (h, l: 2 K n fp16), then the columns' largest |x| (n u32)
+size_t split3_planes_bytes(int K, int n) { return align_up(4 * (size_t)K * n) + align_up(4 * (size_t)n); }
+
+int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void* planes, hipStream_t s) {
+  if (!P || !C || !planes || K <= 0 || K % kK16 != 0 || n <= 0 || n % 128 != 0 || ldp % 4 != 0 || ldp < n ||
+      ldc < n || (size_t)K * kSegs / kK16 > (size_t)INT32_MAX)
+    return GPTQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(P) % 16 != 0 || reinterpret_cast<uintptr_t>(planes) % 16 != 0)
+    return GPTQ_ERR_INVALID_ARG;
+  _Float16* pl = static_cast<_Float16*>(planes);
+  const int64_t total = (int64_t)K * n;
+  unsigned* smax = reinterpret_cast<unsigned*>(static_cast<char*>(planes) + align_up(4 * (size_t)total));
+  zero_u32_kernel<<<1, 256, 0, s>>>(smax, n);
+  GPTQ_LAUNCH_CHECK();
+  col_absmax_kernel<<<dim3((n + 1023) / 1024, (K + 63) / 64), 256, 0, s>>>(P, ldp, K, n, false, smax);
+  GPTQ_LAUNCH_CHECK();
+  split3_planes_kernel<<<(unsigned)((total / 4 + 255) / 256), 256, 0, s>>>(P, ldp, K, n, smax, false, pl);
+  GPTQ_LAUNCH_CHECK();
+  const int nt = (n + kT16 - 1) / kT16, ntiles = nt * (nt + 1) / 2;
+  const unsigned items = (unsigned)(kXCD * ((ntiles + kXCD - 1) / kXCD));
+  const unsigned pg = (std::min<unsigned>(256u, items) + kXCD - 1) / kXCD * kXCD;
+  Split3Args a{};
+  a.C = C;
+  a.ldc = ldc;
+  a.kseg = K;
+  a.plane = total;
+  a.sA = smax;
+  a.sB = smax;
+  syrk16_kernel<_Float16, false, 1><<<pg, 256, 0, s>>>(pl, (int64_t)kSegs * K, n, nt, ntiles, 1, kSegs * K / kK16,
+                                                       nullptr, nullptr, a);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+// The general form at K = 2048 runs a 256 x 256 tile in well under a
+// millisecond; with fewer tiles than one round of the 256 CUs the fp32 tiles
+// are as fast.
 bool split3_gemm_shape_ok(int K, int m, int n) {
   if (K <= 0 || K % kK16 != 0 || m <= 0 || n <= 0 || m % 8 != 0 || n % 8 != 0) return false;
-  if ((size_t)K * 6 / kK16 > (size_t)INT32_MAX) return false;
+  if ((size_t)K * kSegs / kK16 > (size_t)INT32_MAX) return false;
   const int64_t tiles = (int64_t)((m + kT16 - 1) / kT16) * ((n + kT16 - 1) / kT16);
   return tiles >= 256;
 }
@@ -1160,22 +1242,37 @@ bool split3_gemm_applies(const float* A, int lda, bool a_rows, const float* B, i
   return reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(B) % 16 == 0;
 }
 
-size_t split3_gemm_planes_bytes(int K, int m, int n) { return 3 * (size_t)K * ((size_t)m + (size_t)n) * sizeof(__bf16); }
+// planes of A and B (h, l: 2 K (m + n) fp16), then the largest |x| of A's
+// rows of C and of B's columns (m + n u32)
+size_t split3_gemm_planes_bytes(int K, int m, int n) {
+  return align_up(4 * (size_t)K * ((size_t)m + (size_t)n)) + align_up(4 * ((size_t)m + (size_t)n));
+}
 
 int split3_gemm(const float* A, int lda, bool a_rows, const float* B, int ldb, int K, int m, int n, float* C,
                 int ldc, bool neg, bool beta, int tri, void* planes, hipStream_t s) {
   if (!split3_gemm_applies(A, lda, a_rows, B, ldb, K, m, n) || !C || ldc < n || !planes ||
       reinterpret_cast<uintptr_t>(planes) % 16 != 0 || tri < 0 || tri > 2 || (tri == 1 && !a_rows))
     return GPTQ_ERR_INVALID_ARG;
-  __bf16* pa = static_cast<__bf16*>(planes);
+  _Float16* pa = static_cast<_Float16*>(planes);
   const int64_t ta = (int64_t)K * m, tb = (int64_t)K * n;
-  __bf16* pb = pa + 3 * ta;   // 3 K m elements: 16-byte aligned since m % 8 == 0
-  if (a_rows)
-    split3_planes_t_kernel<<<dim3((K + 63) / 64, (m + 63) / 64), 256, 0, s>>>(A, lda, K, m, pa, tri == 1);
-  else
-    split3_planes_kernel<<<(unsigned)((ta / 4 + 255) / 256), 256, 0, s>>>(A, lda, K, m, pa, 3, false);
+  _Float16* pb = pa + 2 * ta;   // 2 K m elements: 16-byte aligned since m % 8 == 0
+  unsigned* sA = reinterpret_cast<unsigned*>(static_cast<char*>(planes) + align_up(4 * (size_t)(ta + tb)));
+  unsigned* sB = sA + m;
+  zero_u32_kernel<<<1, 256, 0, s>>>(sA, m + n);
   GPTQ_LAUNCH_CHECK();
-  split3_planes_kernel<<<(unsigned)((tb / 4 + 255) / 256), 256, 0, s>>>(B, ldb, K, n, pb, 3, tri == 2);
+  if (a_rows)
+    row_absmax_kernel<<<m, 256, 0, s>>>(A, lda, K, tri == 1, sA);
+  else
+    col_absmax_kernel<<<dim3((m + 1023) / 1024, (K + 63) / 64), 256, 0, s>>>(A, lda, K, m, false, sA);
+  GPTQ_LAUNCH_CHECK();
+  col_absmax_kernel<<<dim3((n + 1023) / 1024, (K + 63) / 64), 256, 0, s>>>(B, ldb, K, n, tri == 2, sB);
+  GPTQ_LAUNCH_CHECK();
+  if (a_rows)
+    split3_planes_t_kernel<<<dim3((K + 63) / 64, (m + 63) / 64), 256, 0, s>>>(A, lda, K, m, sA, tri == 1, pa);
+  else
+    split3_planes_kernel<<<(unsigned)((ta / 4 + 255) / 256), 256, 0, s>>>(A, lda, K, m, sA, false, pa);
+  GPTQ_LAUNCH_CHECK();
+  split3_planes_kernel<<<(unsigned)((tb / 4 + 255) / 256), 256, 0, s>>>(B, ldb, K, n, sB, tri == 2, pb);
   GPTQ_LAUNCH_CHECK();
   const int mt = (m + kT16 - 1) / kT16, ntn = (n + kT16 - 1) / kT16, ntiles = mt * ntn;
   const unsigned items = (unsigned)(kXCD * ((ntiles + kXCD - 1) / kXCD));
@@ -1187,13 +1284,15 @@ int split3_gemm(const float* A, int lda, bool a_rows, const float* B, int ldb, i
   a.plane = ta;
   a.B = pb;
   a.planeB = tb;
+  a.sA = sA;
+  a.sB = sB;
   a.n = n;
   a.ntn = ntn;
   a.neg = neg ? 1 : 0;
   a.beta = beta ? 1 : 0;
   a.kmode = tri;
-  syrk16_kernel<__bf16, false, 2><<<pg, 256, 0, s>>>(pa, (int64_t)6 * K, m, mt, ntiles, 1, 6 * K / kK16, nullptr,
-                                                     nullptr, a);
+  syrk16_kernel<_Float16, false, 2><<<pg, 256, 0, s>>>(pa, (int64_t)kSegs * K, m, mt, ntiles, 1, kSegs * K / kK16,
+                                                       nullptr, nullptr, a);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }

@@ -675,7 +675,7 @@ static int hinv_super_blocks(int np) {
   return ((size_t)np * np * sizeof(float) > (size_t(256) << 20)) ? 8 : 1;
 }
 
-// a tree node [a, mid) + [mid, b) takes its two products in the split-bf16
+// a tree node [a, mid) + [mid, b) takes its two products in the split fp16
 // form when both have enough tiles (Z = X11 R12 and X12 = -Z X22 are M x N)
 static bool tree_split3(int M, int N) { return split3_gemm_shape_ok(M, M, N) && split3_gemm_shape_ok(N, M, N); }
 
@@ -706,7 +706,7 @@ static HinvLayout hinv_layout(int n) {
   }
   L.off_sk = off;
   off = align_up(off + sk);
-  // bf16 planes of a super-block's rows for the split-bf16 trailing updates,
+  // fp16 pieces of a super-block's rows for the split trailing updates,
   // and of the operands of the tree nodes whose products take the split form
   // (the factor and the tree run one after the other: one region serves both)
   const int gb = hinv_super_blocks(L.np);
@@ -813,7 +813,7 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
     ride = next_tiles <= 2 * free_cus;
     trail = TrailArgs{k0, Kk, ride ? std::max(0, ride_rows) : 0};
     if (gb > 1 && s_end && !ride && split3_pays(rest)) {
-      // a super-block's whole update on bf16 MFMA through the split planes
+      // a super-block's whole update on fp16 MFMA through the split pieces
       const int st = split3_update(Arow, np, Kk, rest, Atrail, np, planes, s);
       if (st != GPTQ_OK) return st;
       continue;
@@ -829,7 +829,7 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
   std::vector<std::vector<TreeNode>> levels;
   build_levels(0, nb, 0, levels);
   for (int lv = (int)levels.size() - 1; lv >= 0; --lv) {
-    // nodes large enough run their two products in the split-bf16 form, one
+    // nodes large enough run their two products in the split fp16 form, one
     // node at a time: Z = X11 R12 (X11 upper triangular: tile row I contracts
     // from 256 I), then X12 = -Z X22 (X22 upper triangular: tile column J
     // contracts up to 256 (J + 1)); the entries below the two diagonals are

@@ -203,7 +203,7 @@ static QuantLayout quant_layout(int d_out, int d, int gb) {
   off = align_up(off + 2 * (size_t)gb * kQB * d_out * sizeof(float));
   L.off_gscale = off;   // fp64 scale of each row's group in progress (groups wider than the block)
   off = align_up(off + (size_t)d_out * sizeof(double));
-  // bf16 planes of a super-block's Err rows and U rows for the split-bf16
+  // fp16 pieces of a super-block's Err rows and U rows for the split
   // update of the columns after the next super-block
   L.off_planes = off;
   if (gb > 1) off = align_up(off + split3_gemm_planes_bytes(gb * kQB, d_out, d));
@@ -345,7 +345,7 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
         const int c = d - tail;
         const float* Uc = U + (size_t)k0 * d + c;
         if (split3_gemm_applies(st.Eprev, d_out, false, Uc, d, st.kprev, d_out, tail)) {
-          // on bf16 MFMA through split fp32 planes (about an fp32 product's error)
+          // on fp16 MFMA through split fp32 operands (about an fp32 product's error)
           const int e = split3_gemm(st.Eprev, d_out, false, Uc, d, st.kprev, d_out, tail, Wp + c, d, true, true, 0, planes, s);
           if (e != GPTQ_OK) return e;
         } else {
@@ -382,7 +382,7 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
     const int c1 = s_end ? d : super_end(b);
     const float* E = s_end ? err_of(b - b % gb) : err_of(b);
     // at a super-block's end the columns after the next super-block take the
-    // split-bf16 product when it applies, as in the fused steps
+    // split fp16 product when it applies, as in the fused steps
     int c_s = c1;
     if (s_end && gb > 1) {
       const int tail = std::max(0, d - std::max(super_end(b + 1), b1 + std::min(kQB, d - b1)));

@@ -1,8 +1,11 @@
-// Symmetric rank-K update C[upper] -= P^T P of an fp32 panel on bf16 MFMA:
-// P is split into three bf16 planes (P = h + m + l) and the six plane
-// products that carry P's 24-bit significand are summed by the 16-bit SYRK
-// tile loop (csrc/hessian.hip), which gives each element about the rounding
-// error of an fp32 product at bf16 MFMA rates.
+// Products of fp32 operands on the 16-bit MFMA tile loop (csrc/hessian.hip):
+// each operand is scaled by a power of two per output row or column (exact)
+// and split into two fp16 pieces h + l, and the three piece products lh, hl,
+// hh carry the product to within 3 2^-22 of it, below what the contraction's
+// fp32 accumulation carries; so each fp32 product costs three fp16 MFMA
+// products.  Symmetric rank-K updates (the factor's super-block updates) and
+// general products (the tree inverse's large nodes, the column loop's
+// super-block tails).
 #pragma once
 #include "common.h"
 
@@ -12,7 +15,7 @@ namespace gptq {
 // (below that the fp32 tiles are as fast)
 bool split3_pays(int n);
 
-// bytes of the planes of a K x n panel (h, m, l and their negations)
+// bytes of the planes of a K x n panel (h, l) and of its columns' scales
 size_t split3_planes_bytes(int K, int n);
 
 // C[r][c] -= sum_k P[k][r] P[k][c] for r <= c (r, c < n; the strictly lower
@@ -30,8 +33,9 @@ int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void
 // ldc.  tri = 1: A is upper triangular (a_rows; A[i][k] = 0 for k < i, tile
 // row I contracts k >= 256 I); tri = 2: B is upper triangular (B[k][j] = 0
 // for k > j, tile column J contracts k < 256 (J + 1)); entries below those
-// diagonals are not read as stored.  The planes h, m, l of A and of B are
-// formed first (3 K (m + n) bf16 in planes, 16-byte aligned).  Applies when
+// diagonals are not read as stored.  The pieces h, l of A and of B are
+// formed first (2 K (m + n) fp16 and m + n scales in planes, 16-byte
+// aligned: split3_gemm_planes_bytes(K, m, n)).  Applies when
 // m, n are multiples of 8, K of 32, lda and ldb of 4, A and B 16-byte
 // aligned, and C has at least 256 tiles of 256 x 256; callers use the fp32
 // tiles otherwise.  Asynchronous on s.
