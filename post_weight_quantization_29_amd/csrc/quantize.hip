@@ -293,6 +293,18 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   auto err_of = [&](int b) { return ErrT + ((size_t)((b / gb) & 1) * gb + b % gb) * kQB * d_out; };
   // first column after block b's super-block
   auto super_end = [&](int b) { return std::min(d, (b / gb + 1) * gb * kQB); };
+  // At the end of super-block S (block b its last, gb > 1) the columns after
+  // the next block take S's update (K = 128 gb) as one split fp16 product
+  // when it applies; else the columns after the next super-block alone; else
+  // none (d).  Both schedules take the same choice, so their bits agree.
+  auto split_start = [&](int b) {
+    const int b1 = (b + 1) * kQB, k0 = (b / gb) * gb * kQB;
+    const float* E = err_of(b - b % gb);
+    const int c_next = b1 + std::min(kQB, d - b1);
+    for (const int c : {c_next, std::max(super_end(b + 1), c_next)})
+      if (c < d && split3_gemm_applies(E, d_out, false, U + (size_t)k0 * d + c, d, b1 - k0, d_out, d - c)) return c;
+    return d;
+  };
 
   // Fused block steps (groups inside the block, operands the 16-byte loads
   // take): block 0's column loop, then one launch per later block holding its
@@ -331,13 +343,15 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
       st.Urest = U + (size_t)k0 * d + b1 + bw1;
       st.rest = std::max(0, (s_end ? d : super_end(b)) - (b1 + bw1));
       // At a super-block's end (gb > 1) the update of the columns after the
-      // next super-block is a plain GEMM of K = 128 gb: it runs as a launch of
-      // its own, four tiles per CU instead of the fused kernel's two.
+      // next block (K = 128 gb) runs as a launch of its own: the split fp16
+      // product from split_start(b) on, the fp32 tiles (four per CU instead of
+      // the fused kernel's two) for the columns after the next super-block
+      // when the split does not apply.
       int tail = 0;
       if (s_end && gb > 1) {
-        const int c_split = super_end(b + 1);
-        tail = std::max(0, d - std::max(c_split, b1 + bw1));
-        st.rest -= tail;
+        const int c_s = split_start(b);
+        tail = (c_s < d) ? d - c_s : std::max(0, d - std::max(super_end(b + 1), b1 + bw1));
+        st.rest = std::max(0, st.rest - tail);
       }
       launch_quant_step(st, gt, s);
       GPTQ_LAUNCH_CHECK();
@@ -381,14 +395,9 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
     const int k0 = s_end ? (b / gb) * gb * kQB : b0;
     const int c1 = s_end ? d : super_end(b);
     const float* E = s_end ? err_of(b - b % gb) : err_of(b);
-    // at a super-block's end the columns after the next super-block take the
-    // split fp16 product when it applies, as in the fused steps
-    int c_s = c1;
-    if (s_end && gb > 1) {
-      const int tail = std::max(0, d - std::max(super_end(b + 1), b1 + std::min(kQB, d - b1)));
-      const int c = d - tail;
-      if (tail > 0 && split3_gemm_applies(E, d_out, false, U + (size_t)k0 * d + c, d, b1 - k0, d_out, tail)) c_s = c;
-    }
+    // at a super-block's end the columns from split_start(b) on take the
+    // split fp16 product, as in the fused steps
+    const int c_s = (s_end && gb > 1) ? split_start(b) : c1;
     gemm_f32<true>(E, d_out, U + (size_t)k0 * d + b1, d, Wp + b1, d, d_out, c_s - b1, b1 - k0, -1.0f, 1.0f, 0, 0,
                    0, s);
     GPTQ_LAUNCH_CHECK();
