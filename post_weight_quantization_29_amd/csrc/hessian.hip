@@ -1186,10 +1186,11 @@ __global__ __launch_bounds__(256) void split3_planes_t_kernel(const float* __res
 
 // The split form runs 256 resident 256 x 256 tiles per round at about 1 PFLOP/s
 // of fp16 products, three per fp32 product; the fp32 tiles reach ~110 TFLOP/s.
-// Below about 528 tiles (n ~ 8000) the rounds leave the chip partly idle.
+// From one round of tiles on (n ~ 5600) it is the faster of the two
+// (measured at d = 13824: 528 -> 256 tiles, prepare 16.7 -> 16.1 ms).
 bool split3_pays(int n) {
   const int nt = (n + kT16 - 1) / kT16;
-  return nt * (nt + 1) / 2 >= 528;
+  return nt * (nt + 1) / 2 >= 256;
 }
 
 // planes (h, l: 2 K n fp16), then the columns' largest |x| (n u32)
@@ -1226,14 +1227,13 @@ int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void
   return GPTQ_OK;
 }
 
-// The general form at K = 2048 runs a 256 x 256 tile in well under a
-// millisecond; with fewer tiles than one round of the 256 CUs the fp32 tiles
-// are as fast.
+// The general form pays from half a round of 256 x 256 tiles on (the tree's
+// nodes of 3456 x 3456 at d = 13824 among them).
 bool split3_gemm_shape_ok(int K, int m, int n) {
   if (K <= 0 || K % kK16 != 0 || m <= 0 || n <= 0 || m % 8 != 0 || n % 8 != 0) return false;
   if ((size_t)K * kSegs / kK16 > (size_t)INT32_MAX) return false;
   const int64_t tiles = (int64_t)((m + kT16 - 1) / kT16) * ((n + kT16 - 1) / kT16);
-  return tiles >= 256;
+  return tiles >= 128;
 }
 
 bool split3_gemm_applies(const float* A, int lda, bool a_rows, const float* B, int ldb, int K, int m, int n) {

@@ -37,7 +37,7 @@ int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void
 // formed first (2 K (m + n) fp16 and m + n scales in planes, 16-byte
 // aligned: split3_gemm_planes_bytes(K, m, n)).  Applies when
 // m, n are multiples of 8, K of 32, lda and ldb of 4, A and B 16-byte
-// aligned, and C has at least 256 tiles of 256 x 256; callers use the fp32
+// aligned, and C has at least 128 tiles of 256 x 256; callers use the fp32
 // tiles otherwise.  Asynchronous on s.
 bool split3_gemm_shape_ok(int K, int m, int n);
 bool split3_gemm_applies(const float* A, int lda, bool a_rows, const float* B, int ldb, int K, int m, int n);
