@@ -251,6 +251,7 @@ struct Split3Args {
   int neg;          // MODE 2: alpha = -1 (MODE 1: always)
   int beta;         // MODE 2: 1 = C is read and accumulated into, 0 = C is overwritten
   int kmode;        // MODE 2 contraction of tile (I, J): 0 all K; 1 k >= 256 I; 2 k < min(K, 256 (J + 1))
+  unsigned* queue;  // MODE 2, kmode != 0: per-XCD item counters (x * 32), zero at launch
 };
 
 // exponent e of a row's or column's largest |x| (given as float bits): its
@@ -316,7 +317,15 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   // XCD x's list, so the workgroups of an XCD move through the list in rounds
   // and those sharing channel panels read the same tokens at the same time.
   const int x = blockIdx.x % kXCD, c = blockIdx.x / kXCD, nper = gridDim.x / kXCD;
-  const int per_xcd = (MODE == 2) ? rect_items_per_xcd(nt, up.ntn) : ((ntiles + kXCD - 1) / kXCD) * splits;
+  // MODE 2 with triangular bounds: the items of an XCD's list are taken one
+  // by one from the XCD's counter, longest contraction first (its strips run
+  // along the dimension the contraction length depends on), so its
+  // workgroups stay evenly loaded whatever the lengths (a fixed deal of
+  // items to workgroups left the busiest with 1.1-1.4x the mean)
+  const bool dyn = (MODE == 2) && up.queue != nullptr;
+  const bool tcol = (MODE == 2) && up.kmode == 2;   // strips of tile columns
+  const int per_xcd = (MODE == 2) ? (tcol ? rect_items_per_xcd(up.ntn, nt) : rect_items_per_xcd(nt, up.ntn))
+                                  : ((ntiles + kXCD - 1) / kXCD) * splits;
   unsigned* prow = PACE ? pace + x * kPaceSlots : nullptr;
   bool pacing = PACE && (wave == 0) && (nper <= kPaceSlots);
   unsigned done = 0;                             // stages done (skipped items included)
@@ -338,9 +347,20 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
       __builtin_amdgcn_s_sleep(2);
     }
   };
-  for (int kidx = c; kidx < per_xcd; kidx += nper) {
+  for (int kidx = c;; kidx += nper) {
+  if (dyn) {
+    // every wave is done with the ring (and the previous item's exponent
+    // tables); thread 0 takes the next item and hands it over through LDS
+    wait_vm0();
+    lds_barrier();
+    unsigned* slot = reinterpret_cast<unsigned*>(&sA[0][0]);
+    if (tid == 0) *slot = atomicAdd(up.queue + x * 32, 1u);
+    __syncthreads();
+    kidx = __builtin_amdgcn_readfirstlane((int)*slot);
+  }
+  if (kidx >= per_xcd) break;
   int s = 0, I, J;
-  if (MODE == 2 ? !rect_item(x, kidx, nt, up.ntn, I, J)
+  if (MODE == 2 ? !(tcol ? rect_item(x, kidx, up.ntn, nt, J, I) : rect_item(x, kidx, nt, up.ntn, I, J))
                 : !xcd_item(kidx * kXCD + x, nt, ntiles, splits, s, I, J)) {
     // a padding item: count its stages as done so the others do not wait on it
     const int sp = kidx / ((ntiles + kXCD - 1) / kXCD);
@@ -1245,7 +1265,8 @@ bool split3_gemm_applies(const float* A, int lda, bool a_rows, const float* B, i
 // planes of A and B (h, l: 2 K (m + n) fp16), then the largest |x| of A's
 // rows of C and of B's columns (m + n u32)
 size_t split3_gemm_planes_bytes(int K, int m, int n) {
-  return align_up(4 * (size_t)K * ((size_t)m + (size_t)n)) + align_up(4 * ((size_t)m + (size_t)n));
+  return align_up(4 * (size_t)K * ((size_t)m + (size_t)n)) + align_up(4 * ((size_t)m + (size_t)n)) +
+         (size_t)kXCD * 32 * sizeof(unsigned);
 }
 
 int split3_gemm(const float* A, int lda, bool a_rows, const float* B, int ldb, int K, int m, int n, float* C,
@@ -1291,6 +1312,11 @@ int split3_gemm(const float* A, int lda, bool a_rows, const float* B, int ldb, i
   a.neg = neg ? 1 : 0;
   a.beta = beta ? 1 : 0;
   a.kmode = tri;
+  if (tri != 0) {
+    a.queue = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(sA) + align_up(4 * ((size_t)m + (size_t)n)));
+    zero_u32_kernel<<<1, 256, 0, s>>>(a.queue, kXCD * 32);
+    GPTQ_LAUNCH_CHECK();
+  }
   syrk16_kernel<_Float16, false, 2><<<pg, 256, 0, s>>>(pa, (int64_t)kSegs * K, m, mt, ntiles, 1, kSegs * K / kK16,
                                                        nullptr, nullptr, a);
   GPTQ_LAUNCH_CHECK();
