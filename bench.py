@@ -664,6 +664,10 @@ def main():
                           "frac_excl_hessian": round((t_roof - roofs["hessian"] * 1e3)
                                                      / (ms_step - mean["hessian"] - mean["zero_h"]), 4)},
         "stages": stages,
+        "timing_note": ("stages_ms: HIP events around each stage of the timed steps on one stream, each stage "
+                        "right after the one before, so prepare_hinv and quantize run at the clock the chip keeps "
+                        "after the Hessian's full MFMA load (alone they run up to 15-20 % faster); per_config: "
+                        "median of 3 after a warm-up, each prepare_hinv right after its Hessian calls"),
         "roofline": {"bound": "mfma", "achieved": achieved_tf, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
