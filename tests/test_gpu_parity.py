@@ -105,14 +105,14 @@ def test_prepare_hinv_parity(d, desc):
     assert np.abs(ident - np.eye(d)).max() <= 1e-2
 
 
-# A factor large enough that its super-block-end updates run in the split-bf16
-# form (rank-1024 updates of 9088 and 8064 trailing columns; the later ones
-# and the in-super-block updates stay in fp32 tiles), d ragged against the
-# 128-blocks.  H = 2 X^T X in fp32 from 12288 standard-normal tokens, shared
-# by both sides.
+# A factor large enough that its super-block-end updates (rank-1024 updates of
+# 9088, 8064 and 7040 trailing columns) and the tree inverse's top node run
+# as split fp16 products (the updates inside super-blocks and the smaller
+# nodes stay in fp32 tiles), d ragged against the 128-blocks.  H = 2 X^T X
+# in fp32 from 12288 standard-normal tokens, shared by both sides.
 def test_prepare_hinv_split_update():
     d, n = 10000, 12288
-    say(f"[hinv] d={d} desc_act=1 (split-bf16 super-block updates)")
+    say(f"[hinv] d={d} desc_act=1 (split fp16 super-block updates and tree)")
     import post_weight_quantization_29_amd as P
     rng = np.random.default_rng(10000)
     X = rng.standard_normal((n, d), dtype=np.float32)
@@ -140,6 +140,41 @@ def test_prepare_hinv_split_update():
     cols = rng.choice(d, size=64, replace=False)
     ident = U.T @ (U @ Hd[:, cols])
     assert np.abs(ident - np.eye(d)[:, cols]).max() <= 1e-2
+
+
+# The split products scale each operand row or column by a power of two
+# before cutting it into fp16 pieces; here the channels span six orders of
+# magnitude (H = D H0 D, D log-uniform in [1e-3, 1e3], so H's entries span
+# twelve), which the factor follows exactly in exact arithmetic (U = U0 D^-1
+# up to the order), and the element bound relative to sqrt(U_ii U_jj) is
+# the same as for the unscaled factor.
+def test_prepare_hinv_split_update_wide_scales():
+    d, n = 10000, 12288
+    say(f"[hinv] d={d} desc_act=1, channel scales 1e-3 .. 1e3 (split products)")
+    import post_weight_quantization_29_amd as P
+    rng = np.random.default_rng(10001)
+    X = rng.standard_normal((n, d), dtype=np.float32)
+    H32 = 2.0 * (X.T @ X)
+    del X
+    D = np.exp(rng.uniform(np.log(1e-3), np.log(1e3), d)).astype(np.float32)
+    H32 = (D[:, None] * H32 * D[None, :]).astype(np.float32)
+    H32 = np.triu(H32) + np.triu(H32, 1).T          # exactly symmetric
+    H64 = H32.astype(np.float64)
+    ref = o.prepare(H64, 0.01, True)
+    del H64
+    Hg = to_dev(H32, "f32")
+    U = torch.empty((d, d), dtype=torch.float32, device="cuda")
+    perm = torch.empty((d,), dtype=torch.int32, device="cuda")
+    P.gptq_prepare_hinv(Hg, 0.01, 1, U, perm)
+    U = U.cpu().numpy().astype(np.float64)
+    assert np.array_equal(perm.cpu().numpy(), ref.perm)
+    assert np.all(np.tril(U, -1) == 0)
+    Ur = ref.U
+    dg = np.sqrt(np.diag(Ur))
+    el = float((np.abs(U - Ur) / np.outer(dg, dg)).max())
+    drel = float(np.max(np.abs(np.diag(U) - np.diag(Ur)) / np.diag(Ur)))
+    say(f"  U: max |dU|/sqrt(Uii Ujj) = {el:.3e}, diagonal max rel = {drel:.3e}")
+    assert el <= 1e-4 and drel <= 1e-4
 
 
 # the desc_act order with heavy ties (diagonal values from a set of four, so
