@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256, 3) void gemm_f32_kernel(GemmGroup grp, float a
 // over the chip); thread t of slice s handles elements s*1024 + t + 256u,
 // u = 0..3, of the tile's 16384 in partial order (reads fully coalesced).
 constexpr int kRedSlices = 16;
-static __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmGroup grp, const float* __restrict__ partial,
+[[maybe_unused]] static __global__ __launch_bounds__(256) void gemm_splitk_reduce(GemmGroup grp, const float* __restrict__ partial,
                                                           int parts, float alpha, float beta) {
   const int wg = blockIdx.x / kRedSlices, slice = blockIdx.x % kRedSlices;
   int pi = 0;

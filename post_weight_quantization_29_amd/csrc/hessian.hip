@@ -481,7 +481,6 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const T* __restrict__ X,
   const int cm0 = I * kT16 + wm * 128, cn0 = J * kT16 + wn * 128;
   const bool cwrite = (MODE == 1) ? (!(I == J && wm == 1 && wn == 0) && cm0 < d && cn0 < d)
                                   : (MODE == 2 && cm0 < d && cn0 < dB);
-  float* cw = UPD ? up.C + (size_t)(cm0 + 4 * (lane >> 5)) * up.ldc + cn0 + (lane & 31) : nullptr;
   // MODE 2: element (i, j, r) of the block is row cm0 + crow(i, r), column
   // cn0 + j*32 + lane%32
   auto c_in = [&](int i, int j, int r) {

@@ -256,7 +256,7 @@ GPTQ_DEV void panel_rows(const PanelArgs& a, int rb, float4* sU4, double* sInv, 
       grid_params(mn, mx, (double)a.maxq, scale, zero);
     }
     rscale = 1.0 / scale;
-    const int gi = (GT > 0) ? (a.b0 + J) / GT : a.b0 / a.G;
+    const int gi = (GT > 0) ? (a.b0 + J) / (GT > 0 ? GT : 1) : a.b0 / a.G;
     if (rv && q == 0) {
       a.scales[(size_t)row * a.ng + gi] = (float)scale;
       a.zeros[(size_t)row * a.ng + gi] = (int)zero;
