@@ -293,15 +293,16 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
   auto err_of = [&](int b) { return ErrT + ((size_t)((b / gb) & 1) * gb + b % gb) * kQB * d_out; };
   // first column after block b's super-block
   auto super_end = [&](int b) { return std::min(d, (b / gb + 1) * gb * kQB); };
-  // At the end of super-block S (block b its last, gb > 1) the columns after
-  // the next block take S's update (K = 128 gb) as one split fp16 product
-  // when it applies; else the columns after the next super-block alone; else
-  // none (d).  Both schedules take the same choice, so their bits agree.
+  // At the end of super-block S (block b its last, gb > 1) every later column
+  // takes S's update (K = 128 gb) as one split fp16 product when it applies
+  // (the next block's column loop then owes nothing); else the columns after
+  // the next block; else those after the next super-block; else none (d).
+  // Both schedules take the same choice, so their bits agree.
   auto split_start = [&](int b) {
     const int b1 = (b + 1) * kQB, k0 = (b / gb) * gb * kQB;
     const float* E = err_of(b - b % gb);
     const int c_next = b1 + std::min(kQB, d - b1);
-    for (const int c : {c_next, std::max(super_end(b + 1), c_next)})
+    for (const int c : {b1, c_next, std::max(super_end(b + 1), c_next)})
       if (c < d && split3_gemm_applies(E, d_out, false, U + (size_t)k0 * d + c, d, b1 - k0, d_out, d - c)) return c;
     return d;
   };
@@ -350,8 +351,18 @@ extern "C" int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int32_t d_
       int tail = 0;
       if (s_end && gb > 1) {
         const int c_s = split_start(b);
-        tail = (c_s < d) ? d - c_s : std::max(0, d - std::max(super_end(b + 1), b1 + bw1));
-        st.rest = std::max(0, st.rest - tail);
+        if (c_s == b1) {
+          // the whole update, the next block's columns included, first; the
+          // next block's column loop then starts from the work copy as it is
+          const int e = split3_gemm(st.Eprev, d_out, false, st.Uprev, d, st.kprev, d_out, d - b1, Wp + b1, d, true,
+                                    true, 0, planes, s);
+          if (e != GPTQ_OK) return e;
+          st.kprev = 0;
+          st.rest = 0;
+        } else {
+          tail = (c_s < d) ? d - c_s : std::max(0, d - std::max(super_end(b + 1), b1 + bw1));
+          st.rest = std::max(0, st.rest - tail);
+        }
       }
       launch_quant_step(st, gt, s);
       GPTQ_LAUNCH_CHECK();
