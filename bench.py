@@ -366,13 +366,14 @@ def cpu_baseline(W, wl, args):
 
 # ---------------------------------------------------------------- widened rows
 
-def w4a16_measure(P, torch, packed, scales, zeros, group_size, reps=24):
+def w4a16_measure(P, torch, packed, scales, zeros, group_size, g_idx=None, reps=24):
     """Decode-shaped product on packed layers (one activation row, bf16 in, fp32
     out): the quantized layer of this step (held in three copies used in turn
     when it is small, so each call streams its weights from HBM rather than the
-    256 MB last-level cache), and a prefill shape (2048 activation rows, the
-    MFMA path) against the bf16 MFMA peak.  HIP events on the launch stream,
-    mean over reps after a warm-up."""
+    256 MB last-level cache), read with contiguous groups and, when the layer
+    has one, with its act-order g_idx (a group per column); and a prefill shape
+    (2048 activation rows, the MFMA path) against the bf16 MFMA peak.  HIP
+    events on the launch stream, mean over reps after a warm-up."""
     out = []
     dev = packed.device
     g = torch.Generator(device=dev)
@@ -388,17 +389,22 @@ def w4a16_measure(P, torch, packed, scales, zeros, group_size, reps=24):
     for c in copies:
         P.gptq_w4a16_gemm(X, c[0], c[1], c[2], Y, group_size=group_size)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(reps):
-        c = copies[i % len(copies)]
-        P.gptq_w4a16_gemm(X, c[0], c[1], c[2], Y, group_size=group_size)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
-    nbytes = nbytes_layer + X.numel() * 2 + Y.numel() * 4
-    out.append({"shape": f"{d_out}x{d_in}", "m": 1, "us": round(us, 2), "bytes": nbytes,
-                "GB_per_s": round(nbytes / us / 1e3, 1),
-                "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)})
+    for gi_ in ([None] if g_idx is None else [None, g_idx]):
+        if gi_ is not None:
+            for c in copies:
+                P.gptq_w4a16_gemm(X, c[0], c[1], c[2], Y, g_idx=gi_, group_size=group_size)
+        e0.record(stream)
+        for i in range(reps):
+            c = copies[i % len(copies)]
+            P.gptq_w4a16_gemm(X, c[0], c[1], c[2], Y, g_idx=gi_, group_size=group_size)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        # algorithmic bytes: codes, scales and zeros, X, Y (and g_idx with it)
+        nbytes = nbytes_layer + X.numel() * 2 + Y.numel() * 4 + (0 if gi_ is None else gi_.numel() * 4)
+        out.append({"shape": f"{d_out}x{d_in}", "m": 1, "groups": "contiguous" if gi_ is None else "g_idx",
+                    "us": round(us, 2), "bytes": nbytes, "GB_per_s": round(nbytes / us / 1e3, 1),
+                    "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)})
     mp = 2048
     Xp = torch.randn((mp, d_in), device=dev, generator=g).to(torch.bfloat16)
     Yp = torch.empty((mp, d_out), dtype=torch.float32, device=dev)
@@ -682,7 +688,8 @@ def main():
                                    "tokens_per_call": gi.CHUNK_TOKENS, "ms": round(t_hs, 4),
                                    "TFLOP_per_s": round(h_flops / (t_hs / 1e3) / 1e12, 1)}
         log("[bench] streamed Hessian done")
-        out["w4a16_decode"] = w4a16_measure(P, torch, packed, scales, zeros, q.group_size)
+        out["w4a16_decode"] = w4a16_measure(P, torch, packed, scales, zeros, q.group_size,
+                                            g_idx=g_idx if q.desc_act else None)
         log("[bench] w4a16 done")
     del Xg, H, U, ws_h, ws_f, ws_q, codes, packed
     torch.cuda.empty_cache()

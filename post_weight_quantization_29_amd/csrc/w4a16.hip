@@ -184,19 +184,25 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
   }
 }
 
-// One or two activation rows over long rows (natural groups): the four waves
-// of a workgroup (four output rows) walk the same columns, so each step's
-// activation chunk (256 words = 2048 columns per activation row) is loaded
-// once per workgroup into LDS (double buffered, one barrier per step) instead
-// of once per wave; the weights are formed and dotted exactly as above.
-template <typename T, typename TY>
+// One or two activation rows over long rows: the four waves of a workgroup
+// (four output rows) walk the same columns, so each step's activation chunk
+// (256 words = 2048 columns per activation row) is loaded once per workgroup
+// into LDS (double buffered, one barrier per step) instead of once per wave;
+// the weights are formed and dotted exactly as above.  With a group per
+// column (g_idx, the act-order layout, NATURAL false) each wave first copies
+// its row's (scale, zero) pairs into LDS (dynamic, ng pairs per wave), so a
+// code's group costs one LDS read instead of two scattered global ones, and
+// g_idx is read 16 bytes at a time (four columns).
+template <typename T, typename TY, bool NATURAL>
 __global__ __launch_bounds__(256) void w4a16_shared_x_kernel(const uint16_t* __restrict__ X, int m, int d_in,
                                                              const uint32_t* __restrict__ packed,
                                                              const float* __restrict__ scales,
-                                                             const int32_t* __restrict__ zeros, int G,
+                                                             const int32_t* __restrict__ zeros,
+                                                             const int32_t* __restrict__ g_idx, int G,
                                                              int ng, int d_out, TY* __restrict__ Y) {
   typedef typename Act<T>::v2 v2;
   __shared__ uint4 sX[2][2][256];
+  extern __shared__ float2 sGrp[];             // [4][ng] (scale, zero) when !NATURAL
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = blockIdx.x * 4 + wave;
   const int r = min(r0, d_out - 1);            // rows past the end: computed, not stored
@@ -206,6 +212,12 @@ __global__ __launch_bounds__(256) void w4a16_shared_x_kernel(const uint16_t* __r
   const uint32_t* prow = packed + (size_t)r * nw;
   const float* srow = scales + (size_t)r * ng;
   const int32_t* zrow = zeros + (size_t)r * ng;
+  // the wave's (scale, zero) table; its writes are ordered before every read
+  // by the first step's barrier
+  float2* sg = sGrp + (NATURAL ? 0 : wave * ng);
+  if constexpr (!NATURAL) {
+    for (int g = lane; g < ng; g += 64) sg[g] = make_float2(srow[g], (float)zrow[g]);
+  }
   float acc[2] = {0.0f, 0.0f};
   int buf = 0;
   for (int q0 = 0; q0 < nw; q0 += 256) {
@@ -225,18 +237,39 @@ __global__ __launch_bounds__(256) void w4a16_shared_x_kernel(const uint16_t* __r
     if (q < nw) {
       const uint32_t pw[4] = {p4.x, p4.y, p4.z, p4.w};
       v2 w[4][4];
-      float sc = 0.0f, zf = 0.0f;
+      if constexpr (NATURAL) {
+        float sc = 0.0f, zf = 0.0f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c0 = (q + u) * 8;
-        if (u == 0 || !gshared) {
-          int g = (int)((float)c0 * invG);      // exact quotient after one correction
-          if (g * G > c0) --g;
-          if ((g + 1) * G <= c0) ++g;
-          sc = srow[g];
-          zf = (float)zrow[g];
+        for (int u = 0; u < 4; ++u) {
+          const int c0 = (q + u) * 8;
+          if (u == 0 || !gshared) {
+            int g = (int)((float)c0 * invG);    // exact quotient after one correction
+            if (g * G > c0) --g;
+            if ((g + 1) * G <= c0) ++g;
+            sc = srow[g];
+            zf = (float)zrow[g];
+          }
+          dequant_word<T, true>(pw[u], c0, sc, zf, srow, zrow, nullptr, ng, w[u]);
         }
-        dequant_word<T, true>(pw[u], c0, sc, zf, srow, zrow, nullptr, ng, w[u]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // the same weights as dequant_word's per-code form, the group's
+          // (scale, zero) from the wave's table
+          const int c0 = (q + u) * 8;
+          const int4 ga = *reinterpret_cast<const int4*>(g_idx + c0);
+          const int4 gb = *reinterpret_cast<const int4*>(g_idx + c0 + 4);
+          const int gk[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+          float c[8], v[8];
+          word_codes(pw[u], c);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float2 sz = sg[min(max(gk[k], 0), ng - 1)];
+            v[k] = sz.x * (c[k] - sz.y);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[u][j] = Act<T>::pack(v[2 * j], v[2 * j + 1]);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -413,6 +446,9 @@ __global__ __launch_bounds__(256) void w4a16_mfma_kernel(const uint16_t* __restr
 constexpr int64_t kMfmaMinRows = 64;
 // columns from which one or two activation rows are shared through LDS
 constexpr int kSharedXMinCols = 8192;
+// groups per row up to which a group per column (g_idx) takes the LDS
+// (scale, zero) tables of w4a16_shared_x_kernel (4 x 1536 pairs = 48 KB)
+constexpr int kSharedGroupsMax = 1536;
 
 template <typename T, typename TY, int RPW>
 static void launch_w4a16_rpw(const uint16_t* x, int64_t m, int d_in, const uint32_t* packed, const float* scales,
@@ -450,11 +486,18 @@ static void launch_w4a16(const void* X, int64_t m, int d_in, const uint32_t* pac
     // long rows with natural groups: one activation load per workgroup
     // (measured at 8192 x 28672: one row 46.8 -> 44.4 us, two rows 76 -> 58 us;
     // at 4096 columns the extra barrier does not pay)
-    const bool shared_x = !g_idx && d_in >= kSharedXMinCols && (d_in % 32) == 0 &&
-                          ((reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(x)) & 15) == 0;
-    if (shared_x) {
-      w4a16_shared_x_kernel<T, TY><<<(unsigned)((d_out + 3) / 4), 256, 0, s>>>(x, (int)m, d_in, packed, scales,
-                                                                               zeros, G, ng, d_out, y);
+    // (act order at 8192 x 28672: one row 410 -> 129 us with the LDS tables)
+    const bool long_rows = d_in >= kSharedXMinCols && (d_in % 32) == 0 &&
+                           ((reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(x)) & 15) == 0;
+    const unsigned grid = (unsigned)((d_out + 3) / 4);
+    if (long_rows && !g_idx) {
+      w4a16_shared_x_kernel<T, TY, true><<<grid, 256, 0, s>>>(x, (int)m, d_in, packed, scales, zeros, nullptr, G,
+                                                              ng, d_out, y);
+      return;
+    }
+    if (long_rows && (reinterpret_cast<uintptr_t>(g_idx) & 15) == 0 && ng <= kSharedGroupsMax) {
+      w4a16_shared_x_kernel<T, TY, false><<<grid, 256, (size_t)4 * ng * sizeof(float2), s>>>(
+          x, (int)m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y);
       return;
     }
     launch_w4a16_rpw<T, TY, 1>(x, m, d_in, packed, scales, zeros, g_idx, G, ng, d_out, y, s);

@@ -64,6 +64,11 @@ CASES = [
     # (d_out not a multiple of 4: the last workgroup's extra rows are not stored)
     (1, 130, 9216, 128, 0, "bf16", "f32"),
     (2, 70, 8192, 64, 0, "f16", "bf16"),
+    # the same with a group per column (act order, g_idx): the rows' (scale,
+    # zero) tables in LDS; more groups than the tables hold: the per-wave form
+    (1, 130, 8192, 32, 1, "bf16", "f32"),
+    (2, 70, 9216, 64, 1, "f16", "bf16"),
+    (1, 40, 12800, 8, 1, "bf16", "f32"),
     # 32 or more activation rows: the tiled MFMA product
     (200, 300, 1024, 64, 1, "f16", "f32"),
     (128, 4096, 4096, 128, 0, "bf16", "bf16"),
@@ -131,6 +136,31 @@ def test_w4a16_70b_gate_proj_shape_batch16_sampled_rows():
     bound = np.abs(X64) @ np.abs(o.dequantize16(packed[rows], scales[rows], zeros[rows], g_idx, d_in,
                                                "bf16")).T
     _check(Y.float().cpu().numpy()[:, rows].astype(np.float64), Yref, bound, "bf16")
+
+
+@pytest.mark.parametrize("m, xd", [(1, "bf16"), (2, "f16"), (64, "bf16")])
+def test_w4a16_zero_points_at_and_beyond_1024(m, xd):
+    """Natural groups whose zero points lie far outside the 4-bit grid (an
+    all-positive or all-negative group's zero point is not clamped), mixed
+    with ordinary ones: one or two activation rows over long rows (the
+    activations shared through LDS) and the tiled MFMA product.  The weights
+    scale * (code - zero) then reach ~1500 scale steps, and Y meets the same
+    bar as on ordinary grids."""
+    import post_weight_quantization_29_amd as P
+    d_out, d_in, G = 70, 9216, 128
+    packed, scales, zeros, g_idx = _layer(d_out, d_in, G, 0, seed=4242 + m)
+    rng = np.random.default_rng(4243 + m)
+    special = np.array([-1500, -1025, -1024, -1023, -7, 0, 15, 1023, 1024, 1025, 1500], dtype=np.int32)
+    zeros = rng.choice(special, size=zeros.shape).astype(np.int32)
+    X = gi.cast_storage(rng.standard_normal((m, d_in)).astype(np.float32), xd)
+    X64 = gi.to_float64(X, xd)
+    Yref = o.w4a16_matmul(X64, packed, scales, zeros, g_idx, dtype=xd)
+    bound = np.abs(X64) @ np.abs(o.dequantize16(packed, scales, zeros, g_idx, d_in, xd)).T
+    Y = torch.empty((m, d_out), dtype=torch.float32, device="cuda")
+    P.gptq_w4a16_gemm(to_dev(X, xd), torch.from_numpy(packed.view(np.int32)).cuda(),
+                      torch.from_numpy(scales).cuda(), torch.from_numpy(zeros).cuda(), Y, group_size=G)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy().astype(np.float64), Yref, bound, "f32")
 
 
 def test_w4a16_end_to_end_small_layer():
