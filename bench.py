@@ -538,8 +538,8 @@ def block_measure(P, torch, Xg, n_tokens=32768, seq_len=2048):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: --gpus must be 1 (the path would "
-                                   "shard X by tokens and W by rows; see the design notes)",
+        print(json.dumps({"error": "the GPTQ path here runs on one GPU: --gpus must be 1 (across "
+                                   "GPUs it would shard X by tokens for H and W by output rows)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

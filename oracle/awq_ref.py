@@ -20,7 +20,7 @@ Sources (short names as in gptq_ref):
   [P4] "AWQ与GPTQ谁更强？ms-swift量化模块深度评测": AwqConfig(bits=4,
        group_size=128, zero_point=True), i.e. 4-bit asymmetric groups of 128.
 
-Readings of open points (each also listed in the design notes):
+Readings of open points:
   * Statistic: a_j = sum_t x_tj^2 over the calibration tokens (the RMS squared
     times N; the ranking and the argmin below do not depend on the 1/N).
   * Salient set: the k channels with the largest a_j, ties to the lower index,

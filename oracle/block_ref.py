@@ -15,7 +15,7 @@ Sources (short names as in gptq_ref):
   [P5] the GPTQ practice page, section 2.1: the Hessian of a layer comes from
        that layer's calibration inputs, H = 2 X^T X.
 
-Readings of open points (each also listed in the design notes):
+Readings of open points:
   * The block is Llama's decoder layer (the pages quantize Llama/Qwen-style
     models): RMSNorm (eps 1e-6, weight gamma), q/k/v projections, rotary
     position embedding (rotate-half pairs (i, i + hd/2), theta_i =

@@ -20,7 +20,7 @@ Sources (five web pages on GPTQ/AWQ; short names used below):
        128 consecutive columns sharing one scale and zero point, desc_act,
        damp_percent).
 
-Readings of open points (each also listed in the design notes):
+Readings of open points:
   * H = 2 X^T X over all calibration tokens, no 1/N (codes are invariant to a
     positive scaling of H).
   * damp: lambda = damp_percent * mean(diag H), H_d = H + lambda I.
