@@ -619,18 +619,56 @@ __global__ __launch_bounds__(256) void dinv_scatter_kernel(const float* __restri
 // ---------------------------------------------------------------- 6. anti-transpose
 __global__ __launch_bounds__(256) void flip_out_kernel(const float* __restrict__ X, int np, int n,
                                                        float* __restrict__ U) {
-  __shared__ float tile[32][33];
-  const int a0 = blockIdx.y * 32, b0 = blockIdx.x * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
-  // U[a][b] = X[n-1-b][n-1-a]; read rows r = n-1-b (b in tile), cols c = n-1-a
-  for (int yy = ty; yy < 32; yy += 8) {
+  // U[a][b] = X[n-1-b][n-1-a] for b >= a, 0 below the diagonal; 64 x 64 tiles
+  // of U, staged through LDS.  Tiles wholly inside U with n a multiple of 4 move
+  // 16 bytes per access (the source columns of four consecutive a are four
+  // consecutive, reversed floats); edge tiles go element by element.
+  __shared__ float tile[64][65];
+  const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  const bool full = (a0 + 64 <= n) && (b0 + 64 <= n) && (n % 4 == 0);
+  if (full && b0 + 63 < a0) {
+    // wholly below the diagonal
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = k * 256 + tid, ya = e >> 4, x4 = 4 * (e & 15);
+      *reinterpret_cast<float4*>(U + (size_t)(a0 + ya) * n + b0 + x4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  if (full) {
+    // tile[yb][xa] = X[n-1-(b0+yb)][n-1-(a0+xa)]: a float4 at source column
+    // n-1-(a0+x4+3) holds xa = x4+3, x4+2, x4+1, x4
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = k * 256 + tid, yb = e >> 4, x4 = 4 * (e & 15);
+      const int b = b0 + yb;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (b >= a0 + x4)   // some a of the four has b >= a
+        v = *reinterpret_cast<const float4*>(X + (size_t)(n - 1 - b) * np + (n - 4 - a0 - x4));
+      tile[yb][x4 + 3] = (b >= a0 + x4 + 3) ? v.x : 0.0f;
+      tile[yb][x4 + 2] = (b >= a0 + x4 + 2) ? v.y : 0.0f;
+      tile[yb][x4 + 1] = (b >= a0 + x4 + 1) ? v.z : 0.0f;
+      tile[yb][x4 + 0] = v.w;   // b >= a0 + x4 here, or v is zero
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = k * 256 + tid, ya = e >> 4, x4 = 4 * (e & 15);
+      *reinterpret_cast<float4*>(U + (size_t)(a0 + ya) * n + b0 + x4) =
+          make_float4(tile[x4][ya], tile[x4 + 1][ya], tile[x4 + 2][ya], tile[x4 + 3][ya]);
+    }
+    return;
+  }
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 64 x 4
+  for (int yy = ty; yy < 64; yy += 4) {
     const int b = b0 + yy, a = a0 + tx;
     float v = 0.0f;
     if (a < n && b < n && b >= a) v = X[(size_t)(n - 1 - b) * np + (n - 1 - a)];
     tile[yy][tx] = v;
   }
   __syncthreads();
-  for (int yy = ty; yy < 32; yy += 8) {
+  for (int yy = ty; yy < 64; yy += 4) {
     const int a = a0 + yy, b = b0 + tx;
     if (a < n && b < n) U[(size_t)a * n + b] = tile[tx][yy];
   }
@@ -893,7 +931,7 @@ extern "C" int gptq_prepare_hinv(const float* H, const double* hdiag, int32_t d_
   }
 
   // 6. U
-  flip_out_kernel<<<dim3((n + 31) / 32, (n + 31) / 32), 256, 0, s>>>(A, np, n, U);
+  flip_out_kernel<<<dim3((n + 63) / 64, (n + 63) / 64), 256, 0, s>>>(A, np, n, U);
   GPTQ_LAUNCH_CHECK();
 
   int hflag = 0;
