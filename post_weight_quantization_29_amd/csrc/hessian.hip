@@ -1090,29 +1090,44 @@ static int scratch_for_current_device(void** out) {
 // bits, by atomicMax on the bits of non-negative floats (order-free); with
 // `upper` only k <= c counts (an upper-triangular operand).  out starts at 0.
 // A thread takes four adjacent columns (16-byte loads, n and ld multiples of
-// 4) over 64 rows, eight rows' loads in flight.
+// 4) over 16 rows, eight rows' loads in flight.
 __global__ __launch_bounds__(256) void col_absmax_kernel(const float* __restrict__ P, int ld, int K, int n, bool upper,
                                                          unsigned* __restrict__ out) {
-  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (c >= n) return;
-  const int k0 = blockIdx.y * 64, k1 = min(K, upper ? min(k0 + 64, c + 4) : k0 + 64);
+  // a workgroup takes 256 columns by 64 rows: four row groups of 16 rows, one
+  // wave each (a lane: four columns), their maxima combined in LDS before the
+  // one atomic per column (the maximum is exact in any order)
+  __shared__ float red[4][256];
+  const int tx = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int c = blockIdx.x * 256 + tx * 4;
+  const int k0 = blockIdx.y * 64 + rg * 16;
   float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k = k0; k < k1; k += 8) {
-    float4 v[8];
+  if (c < n) {
+    const int k1 = min(K, upper ? min(k0 + 16, c + 4) : k0 + 16);
+    for (int k = k0; k < k1; k += 8) {
+      float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = (k + u < k1) ? *reinterpret_cast<const float4*>(P + (size_t)(k + u) * ld + c) : make_float4(0, 0, 0, 0);
+      for (int u = 0; u < 8; ++u)
+        v[u] = (k + u < k1) ? *reinterpret_cast<const float4*>(P + (size_t)(k + u) * ld + c) : make_float4(0, 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float a[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      for (int u = 0; u < 8; ++u) {
+        const float a[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (!upper || k + u <= c + q) m[q] = fmaxf(m[q], fabsf(a[q]));
+        for (int q = 0; q < 4; ++q)
+          if (!upper || k + u <= c + q) m[q] = fmaxf(m[q], fabsf(a[q]));
+      }
     }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (m[q] > 0.0f) atomicMax(out + c + q, __builtin_bit_cast(unsigned, m[q]));
+  for (int q = 0; q < 4; ++q) red[rg][tx * 4 + q] = m[q];
+  __syncthreads();
+  if (rg == 0 && c < n) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = tx * 4 + q;
+      const float mm = fmaxf(fmaxf(red[0][j], red[1][j]), fmaxf(red[2][j], red[3][j]));
+      if (mm > 0.0f) atomicMax(out + c + q, __builtin_bit_cast(unsigned, mm));
+    }
+  }
 }
 
 // Largest |A[i][k]| of each row i < m of a row-major m x K matrix (pitch
@@ -1226,7 +1241,7 @@ int split3_update(const float* P, int ldp, int K, int n, float* C, int ldc, void
   unsigned* smax = reinterpret_cast<unsigned*>(static_cast<char*>(planes) + align_up(4 * (size_t)total));
   zero_u32_kernel<<<1, 256, 0, s>>>(smax, n);
   GPTQ_LAUNCH_CHECK();
-  col_absmax_kernel<<<dim3((n + 1023) / 1024, (K + 63) / 64), 256, 0, s>>>(P, ldp, K, n, false, smax);
+  col_absmax_kernel<<<dim3((n + 255) / 256, (K + 63) / 64), 256, 0, s>>>(P, ldp, K, n, false, smax);
   GPTQ_LAUNCH_CHECK();
   split3_planes_kernel<<<(unsigned)((total / 4 + 255) / 256), 256, 0, s>>>(P, ldp, K, n, smax, false, pl);
   GPTQ_LAUNCH_CHECK();
@@ -1283,9 +1298,9 @@ int split3_gemm(const float* A, int lda, bool a_rows, const float* B, int ldb, i
   if (a_rows)
     row_absmax_kernel<<<m, 256, 0, s>>>(A, lda, K, tri == 1, sA);
   else
-    col_absmax_kernel<<<dim3((m + 1023) / 1024, (K + 63) / 64), 256, 0, s>>>(A, lda, K, m, false, sA);
+    col_absmax_kernel<<<dim3((m + 255) / 256, (K + 63) / 64), 256, 0, s>>>(A, lda, K, m, false, sA);
   GPTQ_LAUNCH_CHECK();
-  col_absmax_kernel<<<dim3((n + 1023) / 1024, (K + 63) / 64), 256, 0, s>>>(B, ldb, K, n, tri == 2, sB);
+  col_absmax_kernel<<<dim3((n + 255) / 256, (K + 63) / 64), 256, 0, s>>>(B, ldb, K, n, tri == 2, sB);
   GPTQ_LAUNCH_CHECK();
   if (a_rows)
     split3_planes_t_kernel<<<dim3((K + 63) / 64, (m + 63) / 64), 256, 0, s>>>(A, lda, K, m, sA, tri == 1, pa);
